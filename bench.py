@@ -1,0 +1,156 @@
+#!/usr/bin/env python3
+"""Benchmark of the 3D type 1 + type 2 NUFFT on one MI355X.
+
+One step = the whole hot path over one batch of points: bin-sort (setpts) + type 1
+(spread, FFT, deconvolve) on a type 1 plan, then setpts + type 2 (pre-correct/pad, FFT,
+interpolate) on a type 2 plan, for the 3D fp32 eps = 1e-5 workload (N = 128^3 modes,
+M = 2^24 iid uniform points, complex Gaussian strengths and coefficients).  Inputs are
+resident in HBM before timing starts.  `value` is NU points per second through the
+type-1 + type-2 pair (M / step time).
+
+Prints ONE JSON line.  Extra fields give per-type exec-only throughput, per-stage times,
+the roofline of the dominant kernel and the CPU-oracle baseline.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
+
+
+def spread_bytes(M, dim, n, real_size):
+    """Algorithmic bytes of one spread (or interp) launch: sorted coordinates, permutation,
+    strengths gather, one pass over the fine grid: M (d s + 2 s + 4) + prod(n) 2 s."""
+    cells = 1
+    for v in n:
+        cells *= v
+    return M * (dim * real_size + 2 * real_size + 4) + cells * 2 * real_size
+
+
+def cpu_baseline(wl, inp, sample_M):
+    """Time the CPU oracle (serial C + numpy FFT) on the first `sample_M` points of the workload:
+    type 1 (spread, FFT, correct) then type 2 (pad, inverse FFT, interpolate)."""
+    import numpy as np
+
+    import oracle.oracle as orc
+    X = [x[:sample_M] for x in inp["X"]]
+    c = inp["c"][:sample_M]
+    t0 = time.perf_counter()
+    orc.nufft_type1(X, c, wl.N, wl.eps)
+    orc.nufft_type2(X, inp["f"], wl.N, wl.eps)
+    dt = time.perf_counter() - t0
+    return {"value": sample_M / dt, "unit": "NU points/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {sample_M} of {wl.M} points of the same workload, type 1 + type 2 "
+                      f"(serial C spread/interp, single-threaded numpy FFT), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="3d_n128_m16m_f32_e5")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 20,
+                    help="points of the workload timed on the CPU oracle (0 = skip)")
+    ap.add_argument("--method", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nonuniform_fft_amd as nf
+    from nonuniform_fft_amd.workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = make_inputs(wl)
+    X = [torch.from_numpy(x).to(dev) for x in inp["X"]]
+    c = torch.from_numpy(inp["c"]).to(dev)
+    f_in = torch.from_numpy(inp["f"]).to(dev)
+    cdt = torch.complex64 if wl.precision == "f32" else torch.complex128
+    f_out = torch.empty(tuple(reversed(wl.N)), dtype=cdt, device=dev)
+    c_out = torch.empty(wl.M, dtype=cdt, device=dev)
+    stream = torch.cuda.current_stream()
+    p1 = nf.Plan(1, wl.N, wl.eps, wl.precision, stream=stream, timing=True, method=args.method)
+    p2 = nf.Plan(2, wl.N, wl.eps, wl.precision, stream=stream, timing=True)
+
+    def step():
+        p1.setpts(*X)
+        p1.execute(c, f_out)
+        p2.setpts(*X)
+        p2.execute(c_out, f_in)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stages1 = np.zeros(5)
+    stages2 = np.zeros(5)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+        stages1 += np.array(p1.stage_times())
+        stages2 += np.array(p2.stage_times())
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    stages1 /= args.steps
+    stages2 /= args.steps
+
+    rs = 4 if wl.precision == "f32" else 8
+    info = p1.info()
+    # dominant kernel: the spread (type 1 step 1) or the interpolation (type 2 step 3)
+    spread_ms, interp_ms = stages1[1], stages2[1]
+    bytes_alg = spread_bytes(wl.M, wl.dim, info["n"], rs)
+    dom_name, dom_ms = ("spread", spread_ms) if spread_ms >= interp_ms else ("interp", interp_ms)
+    achieved = bytes_alg / (dom_ms * 1e-3) / 1e9
+    exec1 = stages1[1:].sum()
+    exec2 = stages2[1:].sum()
+    out = {
+        "metric": "NU points/sec (type1 & type2, 3D fp32 eps=1e-5, spread+FFT+deconv) and % HBM roofline",
+        "value": wl.M / (ms_step * 1e-3),
+        "unit": "NU points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.precision == "f32" else "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.dim}D type1+type2 N={'x'.join(map(str, wl.N))} M={wl.M} "
+                               f"{wl.dist} {wl.precision} eps={wl.eps:g}",
+                   "fine_grid": list(info["n"]), "w": info["w"], "bins": list(info["bins"]),
+                   "nsubproblems": p1.info()["nsubproblems"]},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": bytes_alg, "avg_ms": dom_ms},
+        "stages_ms": {
+            "type1": {"sort": stages1[0], "clear": stages1[4], "spread": stages1[1], "fft": stages1[2],
+                      "deconv": stages1[3]},
+            "type2": {"sort": stages2[0], "pad": stages2[3], "fft": stages2[2], "interp": stages2[1]},
+        },
+        "exec_pts_per_s": {"type1": wl.M / (exec1 * 1e-3), "type2": wl.M / (exec2 * 1e-3)},
+    }
+    p1.destroy()
+    p2.destroy()
+    if args.cpu_sample > 0:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_sample, wl.M))
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

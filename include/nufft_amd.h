@@ -1,0 +1,172 @@
+/*
+ * nufft_amd.h -- C ABI of the MI355X (gfx950) 2D/3D type 1 / type 2 NUFFT library.
+ *
+ * The transforms (cuFINUFFT paper, "cuFINUFFT: a load-balanced GPU library for
+ * general-purpose nonuniform FFTs", Sec. I):
+ *   type 1, eq. (1):  f_k = sum_{j=1..M} c_j exp(-i k.x_j),  k in I_N1 x I_N2 (x I_N3),
+ *   type 2, eq. (3):  c_j = sum_k f_k exp(+i k.x_j),          j = 1..M,
+ * with I_N = {k integer : -N/2 <= k < N/2} (eq. (2)) and points x_j in [-pi, pi)^d.
+ * Both are approximated to a requested tolerance eps by the three-step scheme of
+ * Sec. II (ES-kernel spreading / interpolation on a 2x upsampled grid, a plain
+ * FFT, and a diagonal correction).  The library follows the paper's "plan,
+ * setup, execute, destroy" interface (Sec. I-A): points are bin-sorted once by
+ * nufft_setpts and reused by every nufft_execute.
+ *
+ * Conventions shared by every entry point
+ *  - All array arguments are DEVICE pointers on the plan's device, in the plan's
+ *    precision: `float` / `double` coordinates, interleaved complex (re, im)
+ *    `float` / `double` strengths and coefficients.  The caller owns them.
+ *  - Coefficient arrays f hold N1*N2(*N3) complex values with k1 varying
+ *    fastest; along each dimension k_i runs upward from -floor(N_i/2).  (A
+ *    C-contiguous torch tensor of shape (N3, N2, N1).)
+ *  - Fine grids hold n1*n2(*n3) complex values, first index fastest; cell l
+ *    sits at position l*2pi/n - pi.
+ *  - Work is enqueued on the stream given at plan creation and is asynchronous
+ *    unless stated otherwise.  A plan is not thread-safe; distinct plans are
+ *    independent.
+ *  - Return values: 0 = success; >0 = success with a warning; <0 = error
+ *    (see nufft_status).  nufft_strerror() names a code; nufft_last_error()
+ *    gives the detail of the last error on a plan.  On error, output arrays
+ *    are unspecified and the plan stays valid unless it was never created.
+ */
+#ifndef NUFFT_AMD_H
+#define NUFFT_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct nufft_plan_s* nufft_plan;
+
+enum nufft_status {
+    NUFFT_OK = 0,
+    NUFFT_WARN_EPS_CLAMPED = 1,   /* eps asked for a kernel width outside [2, 16]; w was clamped */
+    NUFFT_ERR_BAD_ARG = -1,       /* invalid type, dim, N, eps, precision, pointer or size */
+    NUFFT_ERR_BAD_STATE = -2,     /* e.g. execute before setpts */
+    NUFFT_ERR_ALLOC = -3,         /* device allocation failed or exceeded opts.max_device_bytes */
+    NUFFT_ERR_HIP = -4,           /* a HIP runtime call failed */
+    NUFFT_ERR_FFT = -5,           /* a rocFFT call failed */
+    NUFFT_ERR_POINTS = -6,        /* a coordinate is NaN/Inf or outside [-3pi, 3pi) */
+    NUFFT_ERR_UNSUPPORTED = -7    /* a valid request this build does not implement */
+};
+
+enum nufft_spread_method {
+    NUFFT_METHOD_AUTO = 0,
+    NUFFT_METHOD_GM_SORT = 1,     /* one thread per sorted point, global atomics (Sec. III-A "GM-sort") */
+    NUFFT_METHOD_SM = 2           /* subproblems spread into LDS tiles, then flushed (Sec. III-A "SM") */
+};
+
+typedef struct {
+    int method;               /* nufft_spread_method for type 1 spreading; 0 = auto */
+    int bin[3];               /* bin (tile) size in fine cells per dimension; 0 = tuned default */
+    int subproblem_cap;       /* max points per subproblem; 0 = default */
+    size_t max_device_bytes;  /* 0 = no limit; otherwise plan-owned device memory above this fails */
+    int timing;               /* 1 = record per-stage HIP-event times (see nufft_get_stage_times) */
+} nufft_opts;
+
+/* Fill *opts with defaults (all zero = automatic choices).  NUFFT_ERR_BAD_ARG if opts is NULL. */
+int nufft_default_opts(nufft_opts* opts);
+
+/*
+ * Create a plan.
+ *   type      1 (nonuniform -> uniform, eq. (1)) or 2 (uniform -> nonuniform, eq. (3)).
+ *   dim       2 or 3.
+ *   N         host array of dim mode counts (N1, N2[, N3]), each >= 1.
+ *   eps       requested relative tolerance > 0.  Kernel width w = ceil(log10(1/eps)) + 1
+ *             and shape beta = 2.30 w (eq. (6)); w is clamped to [2, 16] with
+ *             NUFFT_WARN_EPS_CLAMPED.
+ *   precision 0 = single (float / complex<float>), 1 = double.
+ *   stream    hipStream_t on the current device, or NULL for the null stream.
+ *   opts      NULL or tuning/test options.
+ *   out       receives the plan.  Nothing is allocated on error.
+ * Allocates the fine grid (n_i = smallest 2^a 3^b 5^c >= max(2 N_i, w)), the
+ * correction factors (eq. (10), computed on the host in fp64) and the rocFFT plan.
+ */
+int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int precision,
+                      void* stream, const nufft_opts* opts, nufft_plan* out);
+
+/*
+ * Set the nonuniform points (Sec. III-A bin-sort and subproblems).
+ *   M        number of points, 0 <= M <= 2^31 - 1.
+ *   x, y, z  device arrays of M coordinates (z is NULL for dim 2).  Values must be
+ *            finite and in [-3pi, 3pi) (one periodic fold is applied), else
+ *            NUFFT_ERR_POINTS and the plan keeps no points.
+ * The library copies what it needs (sorted coordinates, permutation); the caller
+ * may reuse x, y, z once the stream has passed this call.  Blocks the host until
+ * the sort is done (one small device-to-host read of the subproblem count).
+ * Replaces any previous points.
+ */
+int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z);
+
+/*
+ * Run the transform on the points of the last setpts.
+ *   type 1: reads c (M complex), writes f (prod N complex).
+ *   type 2: reads f, writes c.
+ * Asynchronous on the plan's stream.  NUFFT_ERR_BAD_STATE before a successful setpts.
+ */
+int nufft_execute(nufft_plan plan, void* c, void* f);
+
+/* Free everything the plan owns (waits for its stream first).  NULL is accepted. */
+int nufft_destroy(nufft_plan plan);
+
+/* Static string naming a status code. */
+const char* nufft_strerror(int status);
+
+/* Detail text of the last error on this plan ("" if none).  Valid until the next call on it. */
+const char* nufft_last_error(nufft_plan plan);
+
+/*
+ * Plan facts, written to host memory:
+ *   info_i[0..19]: type, dim, precision, w, n1, n2, n3, N1, N2, N3, m1, m2, m3,
+ *                  nbins, nsubproblems (after setpts, else 0), M (after setpts, else -1),
+ *                  subproblem cap, spreading method (nufft_spread_method), 0, 0
+ *   info_d[0..1]:  beta, eps
+ * Either pointer may be NULL.
+ */
+int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d);
+
+/*
+ * Per-stage times (ms) of the last setpts/execute when opts.timing = 1, in host
+ * memory: ms[0] sort (setpts), ms[1] spread or interp, ms[2] FFT, ms[3]
+ * correction (deconvolve+truncate or precorrect+pad), ms[4] grid clear.
+ * Synchronises the plan's stream.
+ */
+int nufft_get_stage_times(nufft_plan plan, double* ms);
+
+/* --------------------------------------------------------------------------------------------
+ * Single steps of the method, for testing and per-step timing.  Same argument
+ * conventions; all asynchronous on the plan's stream; the plan's own fine grid is
+ * not touched unless stated.  Each requires a plan of the matching type.
+ * ------------------------------------------------------------------------------------------ */
+
+/* Type 1 step 1 (eq. (7)): spread c onto the caller's fine grid `grid` (overwritten). Needs setpts. */
+int nufft_spread(nufft_plan plan, const void* c, void* grid);
+
+/* Type 2 step 3 (interpolation after eq. (12)): c_j from the caller's fine grid. Needs setpts. */
+int nufft_interp(nufft_plan plan, const void* grid, void* c);
+
+/* Type 1 step 3 (eq. (10)): f_k = p_k * fhat[k mod n] from a transformed fine grid. */
+int nufft_deconvolve(nufft_plan plan, const void* fhat, void* f);
+
+/* Type 2 step 1 (eq. (11)): fhat[k mod n] = p_k f_k on I_N, zero elsewhere (all n^d cells written). */
+int nufft_precorrect_pad(nufft_plan plan, const void* f, void* fhat);
+
+/*
+ * Copy the bin-sort of the last setpts into caller device buffers (int32):
+ *   perm[M]           original index of the i-th point in sorted order
+ *                     (bins in order, increasing original index within a bin),
+ *   counts[nbins]     points per bin,
+ *   subproblems[3*S]  (bin, start, length) per subproblem, S = nsubproblems.
+ * Any pointer may be NULL.  Bins are numbered b1 + nb1*(b2 + nb2*b3) with
+ * b_i = floor(l_i / m_i), l_i = floor((x_i + pi) n_i / (2 pi)) folded into [0, n_i).
+ */
+int nufft_get_sort(nufft_plan plan, int32_t* perm, int32_t* counts, int32_t* subproblems);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NUFFT_AMD_H */

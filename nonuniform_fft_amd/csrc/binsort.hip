@@ -1,0 +1,389 @@
+// Bin-sort of the nonuniform points (cuFINUFFT paper, Sec. III-A: bins of m1 x m2 (x m3)
+// fine cells ordered x-fastest, a point belongs to the bin holding its cell
+// floor((x + pi)/h), and the permutation lists bin 1's points, then bin 2's, ...), followed
+// by the subproblem split of SM spreading (Sec. III-A "Step 1", chunks of at most `cap`
+// consecutive sorted points of one bin).
+//
+// gfx950 design: the permutation is a least-significant-digit radix sort on the bin key,
+// 8 bits per pass.  Each pass is (1) a per-workgroup digit histogram in LDS (integer LDS
+// atomics), (2) an exclusive scan over digit-major histograms, (3) a stable scatter that ranks
+// equal digits inside a wavefront with 64-bit ballots and across the four wavefronts of a
+// workgroup through LDS counters.  Every pass is stable, so points keep their original order
+// inside a bin and the permutation is deterministic.
+#include "nufft_internal.h"
+
+namespace nufft {
+namespace {
+
+constexpr int kBlock = 256;                 // threads per workgroup (4 wavefronts)
+constexpr int kItems = 16;                  // keys per thread per sort tile
+constexpr int kTile = kBlock * kItems;      // keys per sort tile
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kScanItems = 8;               // elements per thread in the scan
+constexpr int kScanTile = kBlock * kScanItems;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------------------------------
+// Bin keys
+// ------------------------------------------------------------------------------------------
+template <typename T, int DIM>
+__global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __restrict__ keys,
+                                                      int32_t* __restrict__ vals,
+                                                      int* __restrict__ bad) {
+    int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (j >= a.M) return;
+    int bidx[3] = {0, 0, 0};
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < DIM; ++i) {
+        double x = (double)((const T*)a.x[i])[j];
+        double t = grid_t(x, a.s[i]);
+        int l = 0;
+        if (!fold_t(t, a.n[i], l)) { ok = false; l = 0; }
+        bidx[i] = l / a.m[i];
+    }
+    int key = bidx[0] + a.nb[0] * (bidx[1] + a.nb[1] * bidx[2]);
+    if (!ok) {
+        key = 0;
+        atomicOr(bad, 1);
+    }
+    keys[j] = key;
+    vals[j] = (int32_t)j;
+}
+
+// ------------------------------------------------------------------------------------------
+// Exclusive scan of int32 arrays (multi-level, wave64 shuffles)
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int32_t u = __shfl_up(v, off, 64);
+        if (lane >= off) v += u;
+    }
+    return v;
+}
+
+// Exclusive scan of this thread's value across the workgroup; returns the workgroup total in *total.
+__device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t* total) {
+    __shared__ int32_t wsum[kBlock / 64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int32_t inc = wave_incl_scan(v);
+    if (lane == 63) wsum[wv] = inc;
+    __syncthreads();
+    int32_t base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kBlock / 64; ++i) {
+        if (i < wv) base += wsum[i];
+        tot += wsum[i];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + inc - v;
+}
+
+__global__ void __launch_bounds__(kBlock) k_scan_tiles(const int32_t* __restrict__ in,
+                                                        int32_t* __restrict__ out, int64_t n,
+                                                        int32_t* __restrict__ tile_sums) {
+    int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    int32_t v[kScanItems];
+    int32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        v[i] = (base + i < n) ? in[base + i] : 0;
+        s += v[i];
+    }
+    int32_t tot;
+    int32_t run = block_excl_scan(s, &tot);
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        if (base + i < n) out[base + i] = run;
+        run += v[i];
+    }
+    if (threadIdx.x == 0) tile_sums[blockIdx.x] = tot;
+}
+
+__global__ void __launch_bounds__(kBlock) k_scan_add(int32_t* __restrict__ out, int64_t n,
+                                                      const int32_t* __restrict__ tile_pref) {
+    int64_t base = (int64_t)blockIdx.x * kScanTile;
+    int32_t add = tile_pref[blockIdx.x];
+    for (int i = threadIdx.x; i < kScanTile; i += kBlock) {
+        if (base + i < n) out[base + i] += add;
+    }
+}
+
+// Writes total of a scanned array: out[n] = out[n-1] + in[n-1] (or 0 for n == 0).
+__global__ void k_scan_total(const int32_t* __restrict__ in, int32_t* __restrict__ out, int64_t n) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) out[n] = (n > 0) ? out[n - 1] + in[n - 1] : 0;
+}
+
+// Upper bound on the scratch exclusive_scan uses for n elements: per level, the tile sums and
+// their scanned copy (t + 1 entries each).
+size_t scan_scratch_elems(int64_t n) {
+    size_t tot = 0;
+    while (n > 0) {
+        int64_t t = cdiv(n, kScanTile);
+        tot += 2 * (size_t)t + 2;
+        if (t <= 1) break;
+        n = t;
+    }
+    return tot;
+}
+
+// Exclusive scan in -> out (n elements), and out[n] = total.  `scratch` must hold
+// scan_scratch_elems(n) int32.
+hipError_t exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* scratch,
+                          hipStream_t st) {
+    if (n > 0) {
+        int64_t tiles = cdiv(n, kScanTile);
+        int32_t* sums = scratch;
+        k_scan_tiles<<<dim3((unsigned)tiles), dim3(kBlock), 0, st>>>(in, out, n, sums);
+        if (tiles > 1) {
+            int32_t* pref = scratch + tiles + 1;
+            hipError_t e = exclusive_scan(sums, pref, tiles, pref + tiles + 1, st);
+            if (e != hipSuccess) return e;
+            k_scan_add<<<dim3((unsigned)tiles), dim3(kBlock), 0, st>>>(out, n, pref);
+        }
+    }
+    k_scan_total<<<1, 64, 0, st>>>(in, out, n);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Radix sort passes
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(kBlock) k_radix_hist(const int32_t* __restrict__ keys, int64_t M,
+                                                        int shift, int64_t ntiles,
+                                                        int32_t* __restrict__ hist) {
+    __shared__ int32_t h[kRadix];
+    for (int i = threadIdx.x; i < kRadix; i += kBlock) h[i] = 0;
+    __syncthreads();
+    int64_t base = (int64_t)blockIdx.x * kTile;
+#pragma unroll 4
+    for (int r = 0; r < kItems; ++r) {
+        int64_t idx = base + (int64_t)r * kBlock + threadIdx.x;
+        if (idx < M) atomicAdd(&h[(keys[idx] >> shift) & (kRadix - 1)], 1);
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < kRadix; d += kBlock) hist[(int64_t)d * ntiles + blockIdx.x] = h[d];
+}
+
+__global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restrict__ keys_in,
+                                                           const int32_t* __restrict__ vals_in,
+                                                           int32_t* __restrict__ keys_out,
+                                                           int32_t* __restrict__ vals_out,
+                                                           int64_t M, int shift, int64_t ntiles,
+                                                           const int32_t* __restrict__ offs) {
+    __shared__ int32_t running[kRadix];
+    __shared__ int32_t wcount[kBlock / 64][kRadix];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int d = tid; d < kRadix; d += kBlock) {
+        running[d] = offs[(int64_t)d * ntiles + blockIdx.x];
+#pragma unroll
+        for (int i = 0; i < kBlock / 64; ++i) wcount[i][d] = 0;
+    }
+    __syncthreads();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int64_t base = (int64_t)blockIdx.x * kTile;
+    for (int r = 0; r < kItems; ++r) {
+        int64_t idx = base + (int64_t)r * kBlock + tid;
+        bool valid = idx < M;
+        int32_t key = valid ? keys_in[idx] : 0;
+        int32_t val = valid ? vals_in[idx] : 0;
+        int digit = (key >> shift) & (kRadix - 1);
+        // lanes of this wavefront holding the same digit
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < kRadixBits; ++b) {
+            bool bit = (digit >> b) & 1;
+            uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        int rank = __popcll(peers & lt_mask);
+        int leader = peers ? (__ffsll((unsigned long long)peers) - 1) : 64;
+        if (valid && lane == leader) wcount[wv][digit] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int32_t pos = running[digit] + rank;
+            for (int i = 0; i < wv; ++i) pos += wcount[i][digit];
+            keys_out[pos] = key;
+            vals_out[pos] = val;
+        }
+        __syncthreads();
+        for (int d = tid; d < kRadix; d += kBlock) {
+            int32_t add = 0;
+#pragma unroll
+            for (int i = 0; i < kBlock / 64; ++i) {
+                add += wcount[i][d];
+                wcount[i][d] = 0;
+            }
+            running[d] += add;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void k_iota(int32_t* __restrict__ v, int64_t M) {
+    int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < M) v[j] = (int32_t)j;
+}
+
+// offsets[b] = first sorted position whose bin is >= b (offsets[nbins] = M).
+__global__ void k_bin_offsets(const int32_t* __restrict__ skeys, int64_t M, int nbins,
+                              int32_t* __restrict__ offsets) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i > M) return;
+    int lo = (i == 0) ? 0 : skeys[i - 1] + 1;
+    int hi = (i == M) ? nbins : skeys[i];
+    for (int b = lo; b <= hi; ++b) offsets[b] = (int32_t)i;
+}
+
+__global__ void k_counts_nsub(const int32_t* __restrict__ offsets, int nbins, int cap,
+                              int32_t* __restrict__ counts, int32_t* __restrict__ nsp) {
+    int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nbins) return;
+    int32_t c = offsets[b + 1] - offsets[b];
+    counts[b] = c;
+    nsp[b] = (c + cap - 1) / cap;
+}
+
+__global__ void k_build_sub(int nbins, int cap, const int32_t* __restrict__ counts,
+                            const int32_t* __restrict__ offsets,
+                            const int32_t* __restrict__ first, int32_t* __restrict__ sub) {
+    int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nbins) return;
+    int32_t c = counts[b], f = first[b], o = offsets[b];
+    for (int32_t s = 0, k = 0; s < c; s += cap, ++k) {
+        sub[3 * (int64_t)(f + k) + 0] = b;
+        sub[3 * (int64_t)(f + k) + 1] = o + s;
+        sub[3 * (int64_t)(f + k) + 2] = min(cap, c - s);
+    }
+}
+
+template <typename T>
+__global__ void k_gather(const T* __restrict__ x, const int32_t* __restrict__ perm, int64_t M,
+                         T* __restrict__ xs) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < M) xs[i] = x[perm[i]];
+}
+
+struct SortLayout {
+    int64_t ntiles;
+    size_t keysA, valsA, keysB, valsB, hist, hist_scan, scan_tmp, nsp, first, end;
+};
+
+SortLayout layout(int64_t M, int nbins) {
+    SortLayout L{};
+    L.ntiles = std::max<int64_t>(1, cdiv(M, kTile));
+    size_t off = 0;
+    auto take = [&](size_t elems) {
+        size_t o = off;
+        off += ((elems * 4 + 255) / 256) * 256;
+        return o;
+    };
+    size_t Mm = (size_t)std::max<int64_t>(M, 1);
+    L.keysA = take(Mm);
+    L.valsA = take(Mm);
+    L.keysB = take(Mm);
+    L.valsB = take(Mm);
+    size_t nh = (size_t)kRadix * L.ntiles;
+    L.hist = take(nh);
+    L.hist_scan = take(nh + 1);
+    size_t big = std::max(nh, (size_t)nbins + 1);
+    L.scan_tmp = take(scan_scratch_elems((int64_t)big) + 16);
+    L.nsp = take((size_t)nbins + 1);
+    L.first = take((size_t)nbins + 2);
+    L.end = off;
+    return L;
+}
+
+}  // namespace
+
+size_t sort_scratch_bytes(int64_t M, int nbins) { return layout(M, nbins).end; }
+
+hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_t* offsets,
+                       void* scratch, size_t scratch_bytes, int64_t* nsub_dev, int* bad_dev,
+                       hipStream_t st) {
+    SortLayout L = layout(a.M, a.nbins);
+    if (scratch_bytes < L.end) return hipErrorInvalidValue;
+    char* base = (char*)scratch;
+    int32_t* keysA = (int32_t*)(base + L.keysA);
+    int32_t* valsA = (int32_t*)(base + L.valsA);
+    int32_t* keysB = (int32_t*)(base + L.keysB);
+    int32_t* valsB = (int32_t*)(base + L.valsB);
+    int32_t* hist = (int32_t*)(base + L.hist);
+    int32_t* hscan = (int32_t*)(base + L.hist_scan);
+    int32_t* stmp = (int32_t*)(base + L.scan_tmp);
+    int32_t* nsp = (int32_t*)(base + L.nsp);
+    int32_t* first = (int32_t*)(base + L.first);
+    hipError_t e;
+    const int64_t M = a.M;
+    if (M > 0) {
+        dim3 g((unsigned)cdiv(M, kBlock));
+        if (a.prec == 0) {
+            if (a.dim == 2) k_bin_keys<float, 2><<<g, kBlock, 0, st>>>(a, keysA, valsA, bad_dev);
+            else k_bin_keys<float, 3><<<g, kBlock, 0, st>>>(a, keysA, valsA, bad_dev);
+        } else {
+            if (a.dim == 2) k_bin_keys<double, 2><<<g, kBlock, 0, st>>>(a, keysA, valsA, bad_dev);
+            else k_bin_keys<double, 3><<<g, kBlock, 0, st>>>(a, keysA, valsA, bad_dev);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        int passes = (a.nbits + kRadixBits - 1) / kRadixBits;
+        int32_t *ki = keysA, *vi = valsA, *ko = keysB, *vo = valsB;
+        for (int p = 0; p < passes; ++p) {
+            int shift = p * kRadixBits;
+            dim3 gt((unsigned)L.ntiles);
+            k_radix_hist<<<gt, kBlock, 0, st>>>(ki, M, shift, L.ntiles, hist);
+            if ((e = exclusive_scan(hist, hscan, (int64_t)kRadix * L.ntiles, stmp, st)) != hipSuccess)
+                return e;
+            k_radix_scatter<<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            std::swap(ki, ko);
+            std::swap(vi, vo);
+        }
+        if ((e = hipMemcpyAsync(perm, vi, sizeof(int32_t) * M, hipMemcpyDeviceToDevice, st)) !=
+            hipSuccess)
+            return e;
+        k_bin_offsets<<<dim3((unsigned)cdiv(M + 1, kBlock)), kBlock, 0, st>>>(ki, M, a.nbins, offsets);
+    } else {
+        if ((e = hipMemsetAsync(offsets, 0, sizeof(int32_t) * (a.nbins + 1), st)) != hipSuccess)
+            return e;
+    }
+    k_counts_nsub<<<dim3((unsigned)cdiv(a.nbins, kBlock)), kBlock, 0, st>>>(offsets, a.nbins, a.cap,
+                                                                          counts, nsp);
+    if ((e = exclusive_scan(nsp, first, a.nbins, stmp, st)) != hipSuccess) return e;
+    // total number of subproblems = first[nbins]; widen to int64 for the host read-back
+    if ((e = hipMemsetAsync(nsub_dev, 0, sizeof(int64_t), st)) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(nsub_dev, first + a.nbins, sizeof(int32_t), hipMemcpyDeviceToDevice,
+                            st)) != hipSuccess)
+        return e;
+    return hipGetLastError();
+}
+
+// Subproblem list from the scratch of the last launch_sort (bins, cap, counts, offsets as there).
+hipError_t launch_build_subproblems_from(int64_t M, int nbins, int cap, const int32_t* counts,
+                                         const int32_t* offsets, const void* scratch,
+                                         int32_t* sub, hipStream_t st) {
+    SortLayout L = layout(M, nbins);
+    const int32_t* first = (const int32_t*)((const char*)scratch + L.first);
+    k_build_sub<<<dim3((unsigned)cdiv(nbins, kBlock)), kBlock, 0, st>>>(nbins, cap, counts, offsets,
+                                                                       first, sub);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_coords(int dim, int prec, int64_t M, const void* const* x,
+                                const int32_t* perm, void* xs, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    dim3 g((unsigned)cdiv(M, kBlock));
+    for (int i = 0; i < dim; ++i) {
+        if (prec == 0)
+            k_gather<float><<<g, kBlock, 0, st>>>((const float*)x[i], perm, M, (float*)xs + i * M);
+        else
+            k_gather<double><<<g, kBlock, 0, st>>>((const double*)x[i], perm, M, (double*)xs + i * M);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace nufft

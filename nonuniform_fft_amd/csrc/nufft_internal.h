@@ -1,0 +1,186 @@
+// Internal declarations of the gfx950 NUFFT library: plan state, kernel launchers and the
+// device helpers every kernel shares (grid coordinates, ES kernel weights).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <rocfft/rocfft.h>
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/nufft_amd.h"
+
+namespace nufft {
+
+// Largest kernel width supported (the tolerance rule is clamped to [2, 16]).
+constexpr int kMaxW = 16;
+constexpr int kMinW = 2;
+
+// The double nearest pi (bit-identical to M_PI).
+constexpr double kPi = 3.141592653589793115997963468544185161590576171875;
+
+// ------------------------------------------------------------------------------------------------
+// Device helpers
+// ------------------------------------------------------------------------------------------------
+
+// Scaled coordinate t = (x + pi) * s, s = n / (2 pi), as two separately rounded fp64 operations
+// (no contraction), so that the bin of every point is reproducible bit for bit.
+__device__ __forceinline__ double grid_t(double x, double s) {
+    return __dmul_rn(__dadd_rn(x, kPi), s);
+}
+
+// One periodic fold of t into [0, n).  Returns false for NaN or values outside [-n, 2n).
+__device__ __forceinline__ bool fold_t(double& t, int n, int& l) {
+    double fl = floor(t);
+    if (!(fl >= -(double)n && fl < 2.0 * (double)n)) return false;
+    l = (int)fl;
+    if (l >= n) { l -= n; t = __dsub_rn(t, (double)n); }
+    else if (l < 0) { l += n; t = __dadd_rn(t, (double)n); }
+    return true;
+}
+
+// ES kernel weights (cuFINUFFT paper eq. (5), rescaled as in eq. (8)) of a point with folded
+// scaled coordinate t along one dimension: the support is the W cells starting at
+// l0 = ceil(t - W/2); weight q has argument z = (l0 + q - t) * 2/W.  The offset l0 - t is
+// formed in fp64 and the rest in the plan precision T.
+template <typename T, int W>
+__device__ __forceinline__ int es_weights(double t, T beta, T* phi) {
+    double l0d = ceil(__dsub_rn(t, 0.5 * (double)W));
+    T delta = (T)__dsub_rn(l0d, t);
+    const T scale = (T)2 / (T)W;
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+        T z = (delta + (T)q) * scale;
+        T zz = z * z;
+        phi[q] = (zz <= (T)1) ? exp(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
+    }
+    return (int)l0d;
+}
+
+template <typename T> struct cplx { T re, im; };
+
+// ------------------------------------------------------------------------------------------------
+// Plan
+// ------------------------------------------------------------------------------------------------
+
+struct DevBuf {
+    void* p = nullptr;
+    size_t bytes = 0;
+};
+
+}  // namespace nufft
+
+struct nufft_plan_s {
+    int type = 0, dim = 0, prec = 0;   // prec 0 = fp32, 1 = fp64
+    int64_t N[3] = {1, 1, 1};
+    int64_t n[3] = {1, 1, 1};
+    int w = 0;
+    double beta = 0, eps = 0;
+    double s[3] = {0, 0, 0};            // n_i / (2 pi)
+    hipStream_t stream = nullptr;
+    int device = 0;
+    nufft_opts opts{};
+    int method = NUFFT_METHOD_SM;
+
+    // bin geometry
+    int m[3] = {1, 1, 1};
+    int nb[3] = {1, 1, 1};
+    int64_t nbins = 0;
+    int cap = 0;
+    int nbits = 0;                      // bits of the largest bin index
+
+    size_t bytes_in_use = 0;
+    std::string last_error;
+
+    // plan-owned device memory
+    nufft::DevBuf grid;                 // fine grid, n^d complex
+    nufft::DevBuf pcorr;                // correction factors p_1 | p_2 | p_3 in precision T
+    nufft::DevBuf fft_work;
+
+    // points (setpts)
+    int64_t M = -1;
+    int64_t nsub = 0;
+    nufft::DevBuf xs;                   // sorted coordinates, d arrays of M (precision T)
+    nufft::DevBuf perm;                 // int32[M]
+    nufft::DevBuf counts;               // int32[nbins]
+    nufft::DevBuf offsets;              // int32[nbins + 1]
+    nufft::DevBuf sub;                  // int32[3 * nsub] (bin, start, len)
+    nufft::DevBuf sort_tmp;             // radix-sort scratch
+    size_t sort_tmp_cap = 0;
+    size_t pts_cap = 0;                 // capacity (points) of xs / perm
+
+    // rocFFT
+    rocfft_plan fft_fwd = nullptr;
+    rocfft_plan fft_bwd = nullptr;
+    rocfft_execution_info fft_info = nullptr;
+
+    // timing
+    hipEvent_t ev[8] = {};
+    bool ev_ok = false;
+    double stage_ms[5] = {0, 0, 0, 0, 0};
+    int stage_recorded = 0;             // bit mask of stages recorded by the last call
+};
+
+namespace nufft {
+
+// Kernel launchers (defined in the .hip files).  All return hipError_t of the launch.
+
+// binsort.hip
+struct SortArgs {
+    int dim;
+    int prec;
+    int64_t M;
+    const void* x[3];
+    int n[3];
+    double s[3];
+    int m[3];
+    int nb[3];
+    int nbins;
+    int nbits;
+    int cap;
+};
+// Bytes of scratch the sort needs for M points and the plan's bin count.
+size_t sort_scratch_bytes(int64_t M, int nbins);
+// Runs bin index + radix sort + counts/offsets + subproblem counts.  Writes perm, counts,
+// offsets; writes the number of subproblems into *nsub_dev (device int64) and a nonzero value
+// into *bad_dev when a point is invalid (*bad_dev must be zeroed by the caller).  Then the
+// caller reads back, allocates `sub`, and calls launch_build_subproblems_from and
+// launch_gather_coords.
+hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_t* offsets,
+                       void* scratch, size_t scratch_bytes, int64_t* nsub_dev, int* bad_dev,
+                       hipStream_t st);
+// (bin, start, len) rows from the per-bin subproblem prefix left in the sort scratch.
+hipError_t launch_build_subproblems_from(int64_t M, int nbins, int cap, const int32_t* counts,
+                                         const int32_t* offsets, const void* scratch,
+                                         int32_t* sub, hipStream_t st);
+hipError_t launch_gather_coords(int dim, int prec, int64_t M, const void* const* x,
+                                const int32_t* perm, void* xs, hipStream_t st);
+
+// spread.hip / interp.hip / deconv.hip
+struct GeomArgs {
+    int dim;
+    int w;
+    int n[3];
+    double s[3];
+    int m[3];
+    int nb[3];
+    double beta;
+    int64_t M;
+    const void* xs[3];     // sorted coordinates
+    const int32_t* perm;
+    const int32_t* sub;    // (bin, start, len)
+    int64_t nsub;
+};
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_spread(int prec, int method, const GeomArgs& g, const void* c, void* grid,
+                         hipStream_t st);
+hipError_t launch_interp(int prec, const GeomArgs& g, const void* grid, void* c, hipStream_t st);
+hipError_t launch_deconvolve(int prec, int dim, const int64_t* N, const int64_t* n,
+                             const void* pcorr, const void* fhat, void* f, hipStream_t st);
+hipError_t launch_precorrect_pad(int prec, int dim, const int64_t* N, const int64_t* n,
+                                 const void* pcorr, const void* f, void* fhat, hipStream_t st);
+// Largest LDS tile (bytes) the SM spreading kernel may use.
+size_t spread_lds_limit();
+size_t spread_tile_bytes(int prec, int dim, int w, const int* m);
+
+}  // namespace nufft

@@ -1,0 +1,629 @@
+// Host side of the gfx950 NUFFT library: the C ABI of include/nufft_amd.h.
+//
+// Planning follows the cuFINUFFT paper ("cuFINUFFT: a load-balanced GPU library for
+// general-purpose nonuniform FFTs"), Sec. II: kernel width and shape from the tolerance
+// (eq. (6)), fine grid sizes, and correction factors from the Fourier transform of the ES
+// kernel (eqs. (4), (5), (10)).  Execution chains the device kernels of Sec. III with rocFFT
+// for the plain FFT of eqs. (9) and (12).
+#include <hip/hip_runtime.h>
+#include <rocfft/rocfft.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "nufft_internal.h"
+
+using nufft::DevBuf;
+
+namespace {
+
+// ------------------------------------------------------------------------------------------------
+// Kernel Fourier transform by quadrature (host, fp64)
+// ------------------------------------------------------------------------------------------------
+
+// Gauss-Legendre nodes/weights on [-1, 1] by Newton iteration on the Legendre polynomial.
+void gauss_legendre(int q, std::vector<double>& x, std::vector<double>& wts) {
+    x.assign(q, 0.0);
+    wts.assign(q, 0.0);
+    for (int i = 0; i < (q + 1) / 2; ++i) {
+        double z = std::cos(nufft::kPi * (i + 0.75) / (q + 0.5));
+        double dp = 0.0;
+        for (int it = 0; it < 100; ++it) {
+            double p0 = 1.0, p1 = z;
+            for (int k = 2; k <= q; ++k) {
+                double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+                p0 = p1;
+                p1 = p2;
+            }
+            dp = q * (z * p1 - p0) / (z * z - 1.0);
+            double dz = p1 / dp;
+            z -= dz;
+            if (std::fabs(dz) < 1e-16) break;
+        }
+        double p0 = 1.0, p1 = z;
+        for (int k = 2; k <= q; ++k) {
+            double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+            p0 = p1;
+            p1 = p2;
+        }
+        dp = q * (z * p1 - p0) / (z * z - 1.0);
+        x[i] = -z;
+        x[q - 1 - i] = z;
+        wts[i] = wts[q - 1 - i] = 2.0 / ((1.0 - z * z) * dp * dp);
+    }
+}
+
+// phihat(xi) = int_{-1}^{1} exp(beta (sqrt(1 - z^2) - 1)) cos(xi z) dz  (eq. (4) applied to the
+// even kernel of eq. (5)).  With z = sin(theta) the integrand is smooth on [0, pi/2]:
+//   phihat(xi) = 2 int_0^{pi/2} exp(beta (cos(theta) - 1)) cos(xi sin(theta)) cos(theta) dtheta,
+// integrated here by composite Gauss-Legendre (16 panels of 24 nodes).
+struct PhiHat {
+    std::vector<double> th, wt;
+    PhiHat() {
+        std::vector<double> g, gw;
+        gauss_legendre(24, g, gw);
+        const int panels = 16;
+        const double a = 0.0, b = 0.5 * nufft::kPi, h = (b - a) / panels;
+        for (int p = 0; p < panels; ++p) {
+            for (size_t i = 0; i < g.size(); ++i) {
+                th.push_back(a + h * (p + 0.5 * (g[i] + 1.0)));
+                wt.push_back(0.5 * h * gw[i]);
+            }
+        }
+    }
+    double operator()(double xi, double beta) const {
+        double s = 0.0;
+        for (size_t i = 0; i < th.size(); ++i)
+            s += wt[i] * std::exp(beta * (std::cos(th[i]) - 1.0)) * std::cos(xi * std::sin(th[i])) *
+                 std::cos(th[i]);
+        return 2.0 * s;
+    }
+};
+
+bool is_5smooth(int64_t v) {
+    for (int p : {2, 3, 5})
+        while (v % p == 0) v /= p;
+    return v == 1;
+}
+
+int64_t next_5smooth(int64_t v) {
+    if (v < 1) v = 1;
+    while (!is_5smooth(v)) ++v;
+    return v;
+}
+
+int bit_length(int64_t v) {
+    int b = 0;
+    while (v > 0) {
+        ++b;
+        v >>= 1;
+    }
+    return b;
+}
+
+int fail(nufft_plan p, int code, const std::string& msg) {
+    if (p) p->last_error = msg;
+    return code;
+}
+
+int hip_fail(nufft_plan p, hipError_t e, const char* where) {
+    return fail(p, NUFFT_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define NUFFT_HIP(call)                                          \
+    do {                                                         \
+        hipError_t _e = (call);                                  \
+        if (_e != hipSuccess) return hip_fail(plan, _e, #call);  \
+    } while (0)
+
+int dev_alloc(nufft_plan plan, DevBuf& b, size_t bytes, const char* what) {
+    if (b.p && b.bytes >= bytes) return NUFFT_OK;
+    size_t old = b.bytes;
+    if (plan->opts.max_device_bytes && plan->bytes_in_use - old + bytes > plan->opts.max_device_bytes)
+        return fail(plan, NUFFT_ERR_ALLOC, std::string("allocation of ") + what +
+                                               " exceeds opts.max_device_bytes");
+    if (b.p) {
+        hipError_t e = hipFree(b.p);
+        b.p = nullptr;
+        b.bytes = 0;
+        plan->bytes_in_use -= old;
+        if (e != hipSuccess) return hip_fail(plan, e, "hipFree");
+    }
+    if (bytes == 0) return NUFFT_OK;
+    hipError_t e = hipMalloc(&b.p, bytes);
+    if (e != hipSuccess) {
+        b.p = nullptr;
+        (void)hipGetLastError();
+        return fail(plan, NUFFT_ERR_ALLOC, std::string("hipMalloc of ") + what + " failed: " +
+                                               hipGetErrorString(e));
+    }
+    b.bytes = bytes;
+    plan->bytes_in_use += bytes;
+    return NUFFT_OK;
+}
+
+void dev_free(nufft_plan plan, DevBuf& b) {
+    if (b.p) {
+        (void)hipFree(b.p);
+        plan->bytes_in_use -= b.bytes;
+    }
+    b.p = nullptr;
+    b.bytes = 0;
+}
+
+std::once_flag g_rocfft_once;
+rocfft_status g_rocfft_setup = rocfft_status_success;
+
+size_t real_size(const nufft_plan p) { return p->prec == 0 ? sizeof(float) : sizeof(double); }
+
+int64_t grid_cells(const nufft_plan p) { return p->n[0] * p->n[1] * p->n[2]; }
+
+int64_t mode_count(const nufft_plan p) { return p->N[0] * p->N[1] * p->N[2]; }
+
+// Default bin (tile) sizes per (dim, precision, w): the largest candidate whose padded fp64 LDS
+// tile plus point staging fits the LDS limit.
+void default_bins(nufft_plan p, int* m) {
+    static const int c2[][2] = {{32, 32}, {32, 16}, {16, 16}, {16, 8}, {8, 8}, {4, 4}, {2, 2}, {1, 1}};
+    static const int c3[][3] = {{16, 16, 8}, {16, 8, 8}, {8, 8, 8}, {8, 8, 4}, {8, 4, 4},
+                                {4, 4, 4}, {4, 4, 2}, {2, 2, 2}, {1, 1, 1}};
+    if (p->dim == 2) {
+        for (auto& c : c2) {
+            int mm[3] = {c[0], c[1], 1};
+            if (nufft::spread_tile_bytes(p->prec, 2, p->w, mm) <= nufft::spread_lds_limit()) {
+                m[0] = c[0];
+                m[1] = c[1];
+                m[2] = 1;
+                return;
+            }
+        }
+    } else {
+        for (auto& c : c3) {
+            int mm[3] = {c[0], c[1], c[2]};
+            if (nufft::spread_tile_bytes(p->prec, 3, p->w, mm) <= nufft::spread_lds_limit()) {
+                m[0] = c[0];
+                m[1] = c[1];
+                m[2] = c[2];
+                return;
+            }
+        }
+    }
+    m[0] = m[1] = m[2] = 1;
+}
+
+nufft::GeomArgs geom(const nufft_plan p) {
+    nufft::GeomArgs g{};
+    g.dim = p->dim;
+    g.w = p->w;
+    for (int i = 0; i < 3; ++i) {
+        g.n[i] = (int)p->n[i];
+        g.s[i] = p->s[i];
+        g.m[i] = p->m[i];
+        g.nb[i] = p->nb[i];
+        g.xs[i] = nullptr;
+    }
+    g.beta = p->beta;
+    g.M = p->M;
+    for (int i = 0; i < p->dim; ++i)
+        g.xs[i] = (const char*)p->xs.p + (size_t)i * (size_t)std::max<int64_t>(p->M, 0) * real_size(p);
+    g.perm = (const int32_t*)p->perm.p;
+    g.sub = (const int32_t*)p->sub.p;
+    g.nsub = p->nsub;
+    return g;
+}
+
+void record(nufft_plan p, int i) {
+    if (p->opts.timing && p->ev_ok) (void)hipEventRecord(p->ev[i], p->stream);
+}
+
+int fft_exec(nufft_plan plan, rocfft_plan fp, void* data) {
+    void* in[1] = {data};
+    rocfft_status s = rocfft_execute(fp, in, nullptr, plan->fft_info);
+    if (s != rocfft_status_success) return fail(plan, NUFFT_ERR_FFT, "rocfft_execute failed");
+    return NUFFT_OK;
+}
+
+int check_plan(nufft_plan p) {
+    if (!p) return NUFFT_ERR_BAD_ARG;
+    return NUFFT_OK;
+}
+
+int check_points(nufft_plan p) {
+    if (p->M < 0) return fail(p, NUFFT_ERR_BAD_STATE, "no points: call nufft_setpts first");
+    return NUFFT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nufft_default_opts(nufft_opts* opts) {
+    if (!opts) return NUFFT_ERR_BAD_ARG;
+    std::memset(opts, 0, sizeof(*opts));
+    return NUFFT_OK;
+}
+
+const char* nufft_strerror(int status) {
+    switch (status) {
+        case NUFFT_OK: return "success";
+        case NUFFT_WARN_EPS_CLAMPED: return "warning: tolerance outside the supported range; kernel width clamped";
+        case NUFFT_ERR_BAD_ARG: return "invalid argument";
+        case NUFFT_ERR_BAD_STATE: return "invalid plan state (e.g. execute before setpts)";
+        case NUFFT_ERR_ALLOC: return "device allocation failed or exceeded the configured limit";
+        case NUFFT_ERR_HIP: return "HIP runtime error";
+        case NUFFT_ERR_FFT: return "rocFFT error";
+        case NUFFT_ERR_POINTS: return "nonuniform point is not finite or outside [-3pi, 3pi)";
+        case NUFFT_ERR_UNSUPPORTED: return "unsupported request";
+        default: return "unknown status";
+    }
+}
+
+const char* nufft_last_error(nufft_plan plan) { return plan ? plan->last_error.c_str() : ""; }
+
+int nufft_destroy(nufft_plan plan) {
+    if (!plan) return NUFFT_OK;
+    (void)hipStreamSynchronize(plan->stream);
+    if (plan->fft_fwd) rocfft_plan_destroy(plan->fft_fwd);
+    if (plan->fft_bwd) rocfft_plan_destroy(plan->fft_bwd);
+    if (plan->fft_info) rocfft_execution_info_destroy(plan->fft_info);
+    for (DevBuf* b : {&plan->grid, &plan->pcorr, &plan->fft_work, &plan->xs, &plan->perm, &plan->counts,
+                      &plan->offsets, &plan->sub, &plan->sort_tmp})
+        dev_free(plan, *b);
+    if (plan->ev_ok)
+        for (auto& e : plan->ev) (void)hipEventDestroy(e);
+    delete plan;
+    return NUFFT_OK;
+}
+
+int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int precision, void* stream,
+                      const nufft_opts* opts, nufft_plan* out) {
+    if (!out) return NUFFT_ERR_BAD_ARG;
+    *out = nullptr;
+    if ((type != 1 && type != 2) || (dim != 2 && dim != 3) || !N || (precision != 0 && precision != 1))
+        return NUFFT_ERR_BAD_ARG;
+    if (!(eps > 0.0) || !std::isfinite(eps)) return NUFFT_ERR_BAD_ARG;
+    for (int i = 0; i < dim; ++i)
+        if (N[i] < 1 || N[i] > (int64_t(1) << 28)) return NUFFT_ERR_BAD_ARG;
+
+    nufft_plan plan = new (std::nothrow) nufft_plan_s();
+    if (!plan) return NUFFT_ERR_ALLOC;
+    plan->type = type;
+    plan->dim = dim;
+    plan->prec = precision;
+    plan->eps = eps;
+    plan->stream = (hipStream_t)stream;
+    if (opts) plan->opts = *opts;
+    int status = NUFFT_OK;
+
+    // eq. (6): w = ceil(log10(1/eps)) + 1 (an exact power of ten counts as its integer log), beta = 2.30 w
+    int w = (int)std::ceil(std::log10(1.0 / eps) - 1e-9) + 1;
+    if (w < nufft::kMinW || w > nufft::kMaxW) {
+        w = std::min(std::max(w, nufft::kMinW), nufft::kMaxW);
+        status = NUFFT_WARN_EPS_CLAMPED;
+    }
+    plan->w = w;
+    plan->beta = 2.30 * w;
+    for (int i = 0; i < 3; ++i) {
+        plan->N[i] = i < dim ? N[i] : 1;
+        plan->n[i] = i < dim ? next_5smooth(std::max<int64_t>(2 * N[i], w)) : 1;
+        plan->s[i] = (double)plan->n[i] / (2.0 * nufft::kPi);
+    }
+    if (grid_cells(plan) > (int64_t(1) << 31) - 1) {
+        nufft_destroy(plan);
+        return NUFFT_ERR_BAD_ARG;
+    }
+    hipError_t he = hipGetDevice(&plan->device);
+    if (he != hipSuccess) {
+        nufft_destroy(plan);
+        return NUFFT_ERR_HIP;
+    }
+
+    // method, bins and subproblem cap
+    plan->method = (plan->opts.method == NUFFT_METHOD_GM_SORT) ? NUFFT_METHOD_GM_SORT : NUFFT_METHOD_SM;
+    int m[3] = {1, 1, 1};
+    if (plan->opts.bin[0] > 0) {
+        for (int i = 0; i < dim; ++i) m[i] = std::max(1, plan->opts.bin[i]);
+    } else {
+        default_bins(plan, m);
+    }
+    for (int i = 0; i < 3; ++i) {
+        plan->m[i] = i < dim ? (int)std::min<int64_t>(m[i], plan->n[i]) : 1;
+        plan->nb[i] = (int)((plan->n[i] + plan->m[i] - 1) / plan->m[i]);
+    }
+    if (nufft::spread_tile_bytes(plan->prec, dim, w, plan->m) > nufft::spread_lds_limit()) {
+        plan->last_error = "bin size too large for LDS";
+        nufft_destroy(plan);
+        return NUFFT_ERR_BAD_ARG;
+    }
+    plan->nbins = (int64_t)plan->nb[0] * plan->nb[1] * plan->nb[2];
+    plan->nbits = bit_length(plan->nbins - 1);
+    int64_t vol = (int64_t)plan->m[0] * plan->m[1] * plan->m[2];
+    plan->cap = plan->opts.subproblem_cap > 0 ? plan->opts.subproblem_cap
+                                              : (int)std::max<int64_t>(1024, 2 * vol);
+
+    // fine grid and correction factors (eq. (10)): p_i(k) = (2/w) (-1)^k / phihat(alpha_i k),
+    // alpha_i = w pi / n_i; (-1)^k is the phase of the grid origin at -pi.
+    const size_t rs = real_size(plan);
+    int rc;
+    if ((rc = dev_alloc(plan, plan->grid, (size_t)grid_cells(plan) * 2 * rs, "fine grid")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->pcorr, (size_t)(plan->N[0] + plan->N[1] + plan->N[2]) * rs,
+                        "correction factors")) != NUFFT_OK) {
+        nufft_destroy(plan);
+        return rc;
+    }
+    {
+        PhiHat ph;
+        std::vector<double> p;
+        for (int i = 0; i < 3; ++i) {
+            const int64_t Ni = plan->N[i];
+            const double alpha = w * nufft::kPi / (double)plan->n[i];
+            for (int64_t idx = 0; idx < Ni; ++idx) {
+                int64_t k = idx - Ni / 2;
+                double v = (i < dim) ? (2.0 / w) * ((k % 2 == 0) ? 1.0 : -1.0) / ph(alpha * (double)k, plan->beta)
+                                     : 1.0;
+                p.push_back(v);
+            }
+        }
+        hipError_t e;
+        if (plan->prec == 0) {
+            std::vector<float> pf(p.begin(), p.end());
+            e = hipMemcpy(plan->pcorr.p, pf.data(), pf.size() * sizeof(float), hipMemcpyHostToDevice);
+        } else {
+            e = hipMemcpy(plan->pcorr.p, p.data(), p.size() * sizeof(double), hipMemcpyHostToDevice);
+        }
+        if (e != hipSuccess) {
+            hip_fail(plan, e, "hipMemcpy correction factors");
+            nufft_destroy(plan);
+            return NUFFT_ERR_HIP;
+        }
+    }
+
+    // rocFFT plans (forward for type 1, backward for type 2), in place, unnormalised
+    std::call_once(g_rocfft_once, [] { g_rocfft_setup = rocfft_setup(); });
+    if (g_rocfft_setup != rocfft_status_success) {
+        nufft_destroy(plan);
+        return NUFFT_ERR_FFT;
+    }
+    size_t lengths[3] = {(size_t)plan->n[0], (size_t)plan->n[1], (size_t)plan->n[2]};
+    rocfft_precision fprec = plan->prec == 0 ? rocfft_precision_single : rocfft_precision_double;
+    rocfft_transform_type tt = (type == 1) ? rocfft_transform_type_complex_forward
+                                           : rocfft_transform_type_complex_inverse;
+    rocfft_plan fp = nullptr;
+    if (rocfft_plan_create(&fp, rocfft_placement_inplace, tt, fprec, (size_t)dim, lengths, 1, nullptr) !=
+        rocfft_status_success) {
+        nufft_destroy(plan);
+        return NUFFT_ERR_FFT;
+    }
+    if (type == 1) plan->fft_fwd = fp;
+    else plan->fft_bwd = fp;
+    size_t work = 0;
+    if (rocfft_plan_get_work_buffer_size(fp, &work) != rocfft_status_success ||
+        rocfft_execution_info_create(&plan->fft_info) != rocfft_status_success) {
+        nufft_destroy(plan);
+        return NUFFT_ERR_FFT;
+    }
+    if (work > 0) {
+        if ((rc = dev_alloc(plan, plan->fft_work, work, "FFT work buffer")) != NUFFT_OK) {
+            nufft_destroy(plan);
+            return rc;
+        }
+        if (rocfft_execution_info_set_work_buffer(plan->fft_info, plan->fft_work.p, work) !=
+            rocfft_status_success) {
+            nufft_destroy(plan);
+            return NUFFT_ERR_FFT;
+        }
+    }
+    if (rocfft_execution_info_set_stream(plan->fft_info, plan->stream) != rocfft_status_success) {
+        nufft_destroy(plan);
+        return NUFFT_ERR_FFT;
+    }
+    if (plan->opts.timing) {
+        plan->ev_ok = true;
+        for (auto& e : plan->ev)
+            if (hipEventCreate(&e) != hipSuccess) plan->ev_ok = false;
+    }
+    *out = plan;
+    return status;
+}
+
+int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (M < 0 || M > INT32_MAX) return fail(plan, NUFFT_ERR_BAD_ARG, "M out of range [0, 2^31-1]");
+    const void* X[3] = {x, y, z};
+    if (M > 0)
+        for (int i = 0; i < plan->dim; ++i)
+            if (!X[i]) return fail(plan, NUFFT_ERR_BAD_ARG, "null coordinate array");
+    plan->M = -1;
+    plan->nsub = 0;
+    const size_t rs = real_size(plan);
+    const size_t Mm = (size_t)std::max<int64_t>(M, 1);
+    int rc;
+    size_t sort_bytes = nufft::sort_scratch_bytes(M, (int)plan->nbins) + 256;
+    if ((rc = dev_alloc(plan, plan->xs, Mm * plan->dim * rs, "sorted coordinates")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->perm, Mm * sizeof(int32_t), "permutation")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->counts, (size_t)plan->nbins * sizeof(int32_t), "bin counts")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->offsets, (size_t)(plan->nbins + 1) * sizeof(int32_t), "bin offsets")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->sort_tmp, sort_bytes, "sort scratch")) != NUFFT_OK)
+        return rc;
+    // two small result slots at the end of the scratch: int64 subproblem count, int bad-point flag
+    char* tail = (char*)plan->sort_tmp.p + (plan->sort_tmp.bytes - 256);
+    int64_t* nsub_dev = (int64_t*)tail;
+    int* bad_dev = (int*)(tail + 64);
+
+    record(plan, 5);
+    NUFFT_HIP(hipMemsetAsync(bad_dev, 0, sizeof(int), plan->stream));
+    nufft::SortArgs a{};
+    a.dim = plan->dim;
+    a.prec = plan->prec;
+    a.M = M;
+    for (int i = 0; i < 3; ++i) {
+        a.x[i] = i < plan->dim ? X[i] : nullptr;
+        a.n[i] = (int)plan->n[i];
+        a.s[i] = plan->s[i];
+        a.m[i] = plan->m[i];
+        a.nb[i] = plan->nb[i];
+    }
+    a.nbins = (int)plan->nbins;
+    a.nbits = plan->nbits;
+    a.cap = plan->cap;
+    NUFFT_HIP(nufft::launch_sort(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p,
+                                 (int32_t*)plan->offsets.p, plan->sort_tmp.p, plan->sort_tmp.bytes - 256,
+                                 nsub_dev, bad_dev, plan->stream));
+    int64_t host_nsub = 0;
+    int host_bad = 0;
+    NUFFT_HIP(hipMemcpyAsync(&host_nsub, nsub_dev, sizeof(int64_t), hipMemcpyDeviceToHost, plan->stream));
+    NUFFT_HIP(hipMemcpyAsync(&host_bad, bad_dev, sizeof(int), hipMemcpyDeviceToHost, plan->stream));
+    NUFFT_HIP(hipStreamSynchronize(plan->stream));
+    if (host_bad) return fail(plan, NUFFT_ERR_POINTS, "a coordinate is not finite or outside [-3pi, 3pi)");
+    if ((rc = dev_alloc(plan, plan->sub, (size_t)std::max<int64_t>(host_nsub, 1) * 3 * sizeof(int32_t),
+                        "subproblem list")) != NUFFT_OK)
+        return rc;
+    NUFFT_HIP(nufft::launch_build_subproblems_from(M, (int)plan->nbins, plan->cap,
+                                                   (const int32_t*)plan->counts.p,
+                                                   (const int32_t*)plan->offsets.p, plan->sort_tmp.p,
+                                                   (int32_t*)plan->sub.p, plan->stream));
+    NUFFT_HIP(nufft::launch_gather_coords(plan->dim, plan->prec, M, X, (const int32_t*)plan->perm.p,
+                                          plan->xs.p, plan->stream));
+    record(plan, 6);
+    plan->M = M;
+    plan->nsub = host_nsub;
+    if (plan->opts.timing && plan->ev_ok) {
+        NUFFT_HIP(hipEventSynchronize(plan->ev[6]));
+        float ms = 0;
+        if (hipEventElapsedTime(&ms, plan->ev[5], plan->ev[6]) == hipSuccess) plan->stage_ms[0] = ms;
+    }
+    return NUFFT_OK;
+}
+
+int nufft_execute(nufft_plan plan, void* c, void* f) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    int rc;
+    if ((rc = check_points(plan)) != NUFFT_OK) return rc;
+    if ((plan->M > 0 && !c) || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
+    nufft::GeomArgs g = geom(plan);
+    const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan);
+    if (plan->type == 1) {
+        record(plan, 0);
+        NUFFT_HIP(nufft::launch_fill_zero(plan->grid.p, gbytes, plan->stream));
+        record(plan, 1);
+        NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, plan->grid.p, plan->stream));
+        record(plan, 2);
+        if ((rc = fft_exec(plan, plan->fft_fwd, plan->grid.p)) != NUFFT_OK) return rc;
+        record(plan, 3);
+        NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p,
+                                           plan->grid.p, f, plan->stream));
+        record(plan, 4);
+    } else {
+        record(plan, 0);
+        record(plan, 1);
+        NUFFT_HIP(nufft::launch_precorrect_pad(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p,
+                                               f, plan->grid.p, plan->stream));
+        record(plan, 2);
+        if ((rc = fft_exec(plan, plan->fft_bwd, plan->grid.p)) != NUFFT_OK) return rc;
+        record(plan, 3);
+        NUFFT_HIP(nufft::launch_interp(plan->prec, g, plan->grid.p, c, plan->stream));
+        record(plan, 4);
+    }
+    plan->stage_recorded = 1;
+    return NUFFT_OK;
+}
+
+int nufft_get_stage_times(nufft_plan plan, double* ms) {
+    if (!plan || !ms) return NUFFT_ERR_BAD_ARG;
+    if (!plan->opts.timing || !plan->ev_ok) return fail(plan, NUFFT_ERR_BAD_STATE, "timing not enabled");
+    NUFFT_HIP(hipStreamSynchronize(plan->stream));
+    if (plan->stage_recorded) {
+        float t[4] = {0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i)
+            if (hipEventElapsedTime(&t[i], plan->ev[i], plan->ev[i + 1]) != hipSuccess) t[i] = 0;
+        if (plan->type == 1) {
+            plan->stage_ms[4] = t[0];
+            plan->stage_ms[1] = t[1];
+            plan->stage_ms[2] = t[2];
+            plan->stage_ms[3] = t[3];
+        } else {
+            plan->stage_ms[4] = 0;
+            plan->stage_ms[3] = t[1];
+            plan->stage_ms[2] = t[2];
+            plan->stage_ms[1] = t[3];
+        }
+    }
+    for (int i = 0; i < 5; ++i) ms[i] = plan->stage_ms[i];
+    return NUFFT_OK;
+}
+
+int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d) {
+    if (!plan) return NUFFT_ERR_BAD_ARG;
+    if (info_i) {
+        int64_t v[20] = {plan->type, plan->dim, plan->prec, plan->w, plan->n[0], plan->n[1], plan->n[2],
+                         plan->N[0], plan->N[1], plan->N[2], plan->m[0], plan->m[1], plan->m[2],
+                         plan->nbins, plan->M >= 0 ? plan->nsub : 0, plan->M, plan->cap, plan->method,
+                         0, 0};
+        std::memcpy(info_i, v, sizeof(v));
+    }
+    if (info_d) {
+        info_d[0] = plan->beta;
+        info_d[1] = plan->eps;
+    }
+    return NUFFT_OK;
+}
+
+int nufft_spread(nufft_plan plan, const void* c, void* grid) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    int rc;
+    if ((rc = check_points(plan)) != NUFFT_OK) return rc;
+    if (!grid || (plan->M > 0 && !c)) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
+    nufft::GeomArgs g = geom(plan);
+    NUFFT_HIP(nufft::launch_fill_zero(grid, (size_t)grid_cells(plan) * 2 * real_size(plan), plan->stream));
+    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, grid, plan->stream));
+    return NUFFT_OK;
+}
+
+int nufft_interp(nufft_plan plan, const void* grid, void* c) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    int rc;
+    if ((rc = check_points(plan)) != NUFFT_OK) return rc;
+    if (!grid || (plan->M > 0 && !c)) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
+    nufft::GeomArgs g = geom(plan);
+    NUFFT_HIP(nufft::launch_interp(plan->prec, g, grid, c, plan->stream));
+    return NUFFT_OK;
+}
+
+int nufft_deconvolve(nufft_plan plan, const void* fhat, void* f) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (!fhat || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
+    NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, fhat, f,
+                                       plan->stream));
+    return NUFFT_OK;
+}
+
+int nufft_precorrect_pad(nufft_plan plan, const void* f, void* fhat) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (!fhat || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
+    NUFFT_HIP(nufft::launch_precorrect_pad(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, f, fhat,
+                                           plan->stream));
+    return NUFFT_OK;
+}
+
+int nufft_get_sort(nufft_plan plan, int32_t* perm, int32_t* counts, int32_t* subproblems) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    int rc;
+    if ((rc = check_points(plan)) != NUFFT_OK) return rc;
+    if (perm && plan->M > 0)
+        NUFFT_HIP(hipMemcpyAsync(perm, plan->perm.p, sizeof(int32_t) * plan->M, hipMemcpyDeviceToDevice,
+                                 plan->stream));
+    if (counts)
+        NUFFT_HIP(hipMemcpyAsync(counts, plan->counts.p, sizeof(int32_t) * plan->nbins,
+                                 hipMemcpyDeviceToDevice, plan->stream));
+    if (subproblems && plan->nsub > 0)
+        NUFFT_HIP(hipMemcpyAsync(subproblems, plan->sub.p, sizeof(int32_t) * 3 * plan->nsub,
+                                 hipMemcpyDeviceToDevice, plan->stream));
+    return NUFFT_OK;
+}
+
+}  // extern "C"

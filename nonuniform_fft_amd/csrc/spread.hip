@@ -1,0 +1,255 @@
+// Type 1 step 1: spreading of the nonuniform points onto the fine grid
+// (cuFINUFFT paper, Sec. II-A eq. (7) with the periodised tensor-product ES kernel of eq. (8)).
+//
+// Two schemes, both on the bin-sorted points of setpts (Sec. III-A):
+//  * SM: one workgroup per subproblem (at most `cap` sorted points of one bin).  The workgroup
+//    accumulates into an LDS copy of its padded bin (the bin plus the kernel's reach on each
+//    side, eq. (13)-(14)), then adds the padded bin into the fine grid with periodic wrap
+//    (eq. (15)).
+//  * GM-sort: one thread per sorted point adding its w^d contributions straight into the fine
+//    grid with global atomics.
+//
+// gfx950 notes.  LDS float atomics are slow on this part (ds_add_f32 measured ~0.33 lane-op per
+// clock per CU against ~7.8 for ds_add_f64), so the LDS tile accumulates in fp64 for both
+// precisions: each complex update is two ds_add_f64.  Work inside a chunk of staged points is
+// split as (point, stencil row) items: a lane takes one row of w cells along x of one point,
+// so the lanes of a wavefront cover whole rows of a few points.
+#include "nufft_internal.h"
+
+namespace nufft {
+namespace {
+
+constexpr int kSpreadBlock = 256;
+constexpr int kChunk = 64;            // points staged per round
+constexpr int kGmBlock = 128;
+
+template <typename T, int DIM, int W>
+struct Stage {
+    T ker[kChunk][DIM][W];
+    int l0[kChunk][3];
+    T cre[kChunk], cim[kChunk];
+};
+
+template <typename T, int DIM, int W>
+__global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c,
+                                                            cplx<T>* __restrict__ grid, int p1, int p2,
+                                                            int p3) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    double* tile = (double*)smem;
+    const int P = p1 * p2 * p3;
+    Stage<T, DIM, W>* st = (Stage<T, DIM, W>*)(smem + (size_t)P * 2 * sizeof(double));
+
+    const int sid = blockIdx.x;
+    const int bin = g.sub[3 * sid + 0];
+    const int start = g.sub[3 * sid + 1];
+    const int len = g.sub[3 * sid + 2];
+    int bcoord[3];
+    bcoord[0] = bin % g.nb[0];
+    bcoord[1] = (bin / g.nb[0]) % g.nb[1];
+    bcoord[2] = bin / (g.nb[0] * g.nb[1]);
+    int origin[3] = {0, 0, 0};
+    const int pd[3] = {p1, p2, p3};
+#pragma unroll
+    for (int i = 0; i < DIM; ++i) origin[i] = bcoord[i] * g.m[i] - W / 2;
+
+    for (int k = threadIdx.x; k < 2 * P; k += kSpreadBlock) tile[k] = 0.0;
+
+    const T beta = (T)g.beta;
+    constexpr int ROWS = (DIM == 3) ? W * W : W;
+    for (int c0 = 0; c0 < len; c0 += kChunk) {
+        const int np = min(kChunk, len - c0);
+        __syncthreads();   // previous chunk consumed (and tile zeroed on the first round)
+        if (threadIdx.x < np) {
+            const int p = threadIdx.x;
+            const int64_t j = (int64_t)start + c0 + p;
+#pragma unroll
+            for (int i = 0; i < DIM; ++i) {
+                double t = grid_t((double)((const T*)g.xs[i])[j], g.s[i]);
+                int l;
+                fold_t(t, g.n[i], l);
+                int l0 = es_weights<T, W>(t, beta, st->ker[p][i]) - origin[i];
+                st->l0[p][i] = min(max(l0, 0), pd[i] - W);
+            }
+            cplx<T> v = c[g.perm[j]];
+            st->cre[p] = v.re;
+            st->cim[p] = v.im;
+        }
+        __syncthreads();
+        const int items = np * ROWS;
+        for (int it = threadIdx.x; it < items; it += kSpreadBlock) {
+            const int p = it / ROWS;
+            const int r = it - p * ROWS;
+            const int q2 = r % W;
+            T wr = st->ker[p][1][q2];
+            int row = st->l0[p][1] + q2;
+            if (DIM == 3) {
+                const int q3 = r / W;
+                wr *= st->ker[p][DIM - 1][q3];
+                row += p2 * (st->l0[p][2] + q3);
+            }
+            const double vre = (double)(st->cre[p] * wr);
+            const double vim = (double)(st->cim[p] * wr);
+            double* dst = tile + 2 * ((size_t)row * p1 + st->l0[p][0]);
+#pragma unroll
+            for (int q1 = 0; q1 < W; ++q1) {
+                const double k1 = (double)st->ker[p][0][q1];
+                atomicAdd(dst + 2 * q1, vre * k1);
+                atomicAdd(dst + 2 * q1 + 1, vim * k1);
+            }
+        }
+    }
+    __syncthreads();
+    // flush the padded bin with periodic wrap (eq. (15))
+    for (int k = threadIdx.x; k < P; k += kSpreadBlock) {
+        const double re = tile[2 * k], im = tile[2 * k + 1];
+        if (re == 0.0 && im == 0.0) continue;
+        int s1 = k % p1;
+        int rest = k / p1;
+        int s2 = rest % p2;
+        int s3 = rest / p2;
+        int g1 = origin[0] + s1, g2 = origin[1] + s2, g3 = (DIM == 3) ? origin[2] + s3 : 0;
+        while (g1 < 0) g1 += g.n[0];
+        while (g1 >= g.n[0]) g1 -= g.n[0];
+        while (g2 < 0) g2 += g.n[1];
+        while (g2 >= g.n[1]) g2 -= g.n[1];
+        if (DIM == 3) {
+            while (g3 < 0) g3 += g.n[2];
+            while (g3 >= g.n[2]) g3 -= g.n[2];
+        }
+        const size_t gi = (size_t)g1 + (size_t)g.n[0] * ((size_t)g2 + (size_t)g.n[1] * (size_t)g3);
+        unsafeAtomicAdd(&grid[gi].re, (T)re);
+        unsafeAtomicAdd(&grid[gi].im, (T)im);
+    }
+}
+
+template <typename T, int DIM, int W>
+__global__ void __launch_bounds__(kGmBlock) k_spread_gm(GeomArgs g, const cplx<T>* __restrict__ c,
+                                                        cplx<T>* __restrict__ grid) {
+    const int64_t i = (int64_t)blockIdx.x * kGmBlock + threadIdx.x;
+    if (i >= g.M) return;
+    const T beta = (T)g.beta;
+    T ker[DIM][W];
+    int idx[DIM][W];
+#pragma unroll
+    for (int d = 0; d < DIM; ++d) {
+        double t = grid_t((double)((const T*)g.xs[d])[i], g.s[d]);
+        int l;
+        fold_t(t, g.n[d], l);
+        int l0 = es_weights<T, W>(t, beta, ker[d]);
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+            int v = l0 + q;
+            v = (v < 0) ? v + g.n[d] : (v >= g.n[d] ? v - g.n[d] : v);
+            idx[d][q] = v;
+        }
+    }
+    const cplx<T> v = c[g.perm[i]];
+    const int n1 = g.n[0], n2 = g.n[1];
+#pragma unroll
+    for (int q3 = 0; q3 < (DIM == 3 ? W : 1); ++q3) {
+        for (int q2 = 0; q2 < W; ++q2) {
+            T wr = ker[1][q2];
+            size_t row = (size_t)idx[1][q2];
+            if (DIM == 3) {
+                wr *= ker[DIM - 1][q3];
+                row += (size_t)n2 * (size_t)idx[DIM - 1][q3];
+            }
+            const T vre = v.re * wr, vim = v.im * wr;
+            cplx<T>* dst = grid + row * (size_t)n1;
+#pragma unroll
+            for (int q1 = 0; q1 < W; ++q1) {
+                unsafeAtomicAdd(&dst[idx[0][q1]].re, vre * ker[0][q1]);
+                unsafeAtomicAdd(&dst[idx[0][q1]].im, vim * ker[0][q1]);
+            }
+        }
+    }
+}
+
+__global__ void k_fill_zero(uint4* __restrict__ p, size_t n16) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+template <typename T, int DIM, int W>
+size_t stage_bytes() { return sizeof(Stage<T, DIM, W>); }
+
+template <typename T, int DIM, int W>
+hipError_t spread_w(int method, const GeomArgs& g, const void* c, void* grid, hipStream_t st) {
+    if (g.M <= 0) return hipSuccess;
+    if (method == NUFFT_METHOD_GM_SORT) {
+        dim3 grd((unsigned)((g.M + kGmBlock - 1) / kGmBlock));
+        k_spread_gm<T, DIM, W><<<grd, kGmBlock, 0, st>>>(g, (const cplx<T>*)c, (cplx<T>*)grid);
+        return hipGetLastError();
+    }
+    if (g.nsub <= 0) return hipSuccess;
+    int p1 = g.m[0] + W, p2 = g.m[1] + W, p3 = (DIM == 3) ? g.m[2] + W : 1;
+    size_t lds = (size_t)p1 * p2 * p3 * 2 * sizeof(double) + sizeof(Stage<T, DIM, W>);
+    if (lds > spread_lds_limit()) return hipErrorInvalidConfiguration;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_spread_sm<T, DIM, W>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)spread_lds_limit());
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    k_spread_sm<T, DIM, W><<<dim3((unsigned)g.nsub), kSpreadBlock, lds, st>>>(
+        g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2, p3);
+    return hipGetLastError();
+}
+
+template <typename T, int DIM>
+hipError_t spread_dim(int method, const GeomArgs& g, const void* c, void* grid, hipStream_t st) {
+    switch (g.w) {
+#define NUFFT_CASE(WW) case WW: return spread_w<T, DIM, WW>(method, g, c, grid, st);
+        NUFFT_CASE(2) NUFFT_CASE(3) NUFFT_CASE(4) NUFFT_CASE(5) NUFFT_CASE(6) NUFFT_CASE(7)
+        NUFFT_CASE(8) NUFFT_CASE(9) NUFFT_CASE(10) NUFFT_CASE(11) NUFFT_CASE(12) NUFFT_CASE(13)
+        NUFFT_CASE(14) NUFFT_CASE(15) NUFFT_CASE(16)
+#undef NUFFT_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int DIM>
+size_t stage_bytes_dim(int w) {
+    switch (w) {
+#define NUFFT_CASE(WW) case WW: return stage_bytes<T, DIM, WW>();
+        NUFFT_CASE(2) NUFFT_CASE(3) NUFFT_CASE(4) NUFFT_CASE(5) NUFFT_CASE(6) NUFFT_CASE(7)
+        NUFFT_CASE(8) NUFFT_CASE(9) NUFFT_CASE(10) NUFFT_CASE(11) NUFFT_CASE(12) NUFFT_CASE(13)
+        NUFFT_CASE(14) NUFFT_CASE(15) NUFFT_CASE(16)
+#undef NUFFT_CASE
+        default: return 0;
+    }
+}
+
+}  // namespace
+
+size_t spread_lds_limit() { return 160 * 1024; }
+
+size_t spread_tile_bytes(int prec, int dim, int w, const int* m) {
+    size_t cells = 1;
+    for (int i = 0; i < dim; ++i) cells *= (size_t)(m[i] + w);
+    size_t stage = (prec == 0) ? (dim == 2 ? stage_bytes_dim<float, 2>(w) : stage_bytes_dim<float, 3>(w))
+                               : (dim == 2 ? stage_bytes_dim<double, 2>(w) : stage_bytes_dim<double, 3>(w));
+    return cells * 2 * sizeof(double) + stage;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+    if (bytes == 0) return hipSuccess;
+    if (bytes % 16 != 0 || ((uintptr_t)p % 16) != 0) return hipMemsetAsync(p, 0, bytes, st);
+    size_t n16 = bytes / 16;
+    unsigned blocks = (unsigned)std::min<size_t>((n16 + 255) / 256, 256 * 64);
+    k_fill_zero<<<blocks, 256, 0, st>>>((uint4*)p, n16);
+    return hipGetLastError();
+}
+
+hipError_t launch_spread(int prec, int method, const GeomArgs& g, const void* c, void* grid,
+                         hipStream_t st) {
+    if (prec == 0) return g.dim == 2 ? spread_dim<float, 2>(method, g, c, grid, st)
+                                     : spread_dim<float, 3>(method, g, c, grid, st);
+    return g.dim == 2 ? spread_dim<double, 2>(method, g, c, grid, st)
+                      : spread_dim<double, 3>(method, g, c, grid, st);
+}
+
+}  // namespace nufft

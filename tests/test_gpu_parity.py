@@ -1,0 +1,319 @@
+"""GPU parity tests: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Sizes are chosen so the oracle finishes in seconds while the GPU path still spans several bins
+(tiles), several subproblems per bin where forced, and ragged tails in M and in the grid.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from nonuniform_fft_amd.workloads import WORKLOADS, Workload, make_inputs, scaled  # noqa: E402
+
+from _gpu_util import cdtype, dev, gpu_type1, gpu_type2, to_dev, tol_for  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def nf():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import nonuniform_fft_amd as nf
+    nf.load_library()
+    return nf
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle.oracle as o
+    o._load()
+    return o
+
+
+def _announce(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------------------------------------
+# Bin-sort: bit-exact
+# ---------------------------------------------------------------------------------------------
+
+SORT_CASES = [
+    ("2d_uniform_f32", Workload("s", 2, (100, 72), 50_001, 1e-5, "f32", seed=21)),
+    ("2d_uniform_f64", Workload("s", 2, (64, 64), 30_000, 1e-12, "f64", seed=22)),
+    ("3d_uniform_f32", Workload("s", 3, (24, 20, 18), 40_000, 1e-5, "f32", seed=23)),
+    ("3d_cluster_f32", Workload("s", 3, (32, 32, 32), 60_000, 1e-5, "f32", dist="cluster", seed=24)),
+    ("3d_box_f64", Workload("s", 3, (16, 16, 16), 20_000, 1e-9, "f64", dist="box", seed=25)),
+    ("2d_tiny", Workload("s", 2, (5, 7), 3, 1e-3, "f32", seed=26)),
+]
+
+
+@pytest.mark.parametrize("name,wl", SORT_CASES, ids=[c[0] for c in SORT_CASES])
+@pytest.mark.parametrize("cap", [0, 37])
+def test_binsort_bit_exact(nf, orc, name, wl, cap):
+    _announce(f"binsort {name} cap={cap}")
+    inp = make_inputs(wl, want_f=False)
+    X = inp["X"]
+    p = nf.Plan(1, wl.N, wl.eps, wl.precision, subproblem_cap=cap)
+    p.setpts(*[to_dev(x) for x in X])
+    info = p.info()
+    perm, counts, sub = [t.cpu().numpy().astype(np.int64) for t in p.get_sort()]
+    _, ocounts, operm = orc.binsort(X, info["n"], info["bins"])
+    np.testing.assert_array_equal(counts, ocounts)
+    np.testing.assert_array_equal(perm, operm)
+    if cap > 0:
+        assert info["cap"] == cap
+    osub = orc.subproblems(ocounts, info["cap"])
+    np.testing.assert_array_equal(sub, osub)
+    p.destroy()
+
+
+def test_binsort_boundary_points(nf, orc):
+    """Coordinates at -pi, just below pi, values that round to pi in fp32, and the fold range."""
+    N = (32, 24)
+    xs = np.array([-math.pi, np.nextafter(math.pi, 0), math.pi - 1e-9, 0.0, 1e-30, -1e-30,
+                   -2.9 * math.pi, 2.5 * math.pi, math.pi, -math.pi + 1e-7])
+    ys = np.array([0.1, -0.2, math.pi - 1e-12, -math.pi, 3.0, -3.0, 0.0, 0.0, 1.0, 2.9])
+    for prec, dt in (("f32", np.float32), ("f64", np.float64)):
+        X = [xs.astype(dt), ys.astype(dt)]
+        p = nf.Plan(1, N, 1e-6, prec)
+        p.setpts(*[to_dev(x) for x in X])
+        info = p.info()
+        perm, counts, _ = [t.cpu().numpy().astype(np.int64) for t in p.get_sort()]
+        _, ocounts, operm = orc.binsort(X, info["n"], info["bins"])
+        np.testing.assert_array_equal(counts, ocounts)
+        np.testing.assert_array_equal(perm, operm)
+        p.destroy()
+
+
+def test_setpts_rejects_bad_points(nf):
+    p = nf.Plan(1, (16, 16), 1e-5, "f32")
+    for bad in (np.nan, np.inf, 20.0, -10.0):
+        x = np.array([0.0, bad, 1.0], np.float32)
+        y = np.zeros(3, np.float32)
+        with pytest.raises(nf.NufftError) as ei:
+            p.setpts(to_dev(x), to_dev(y))
+        assert ei.value.code == -6
+    # the plan stays usable
+    p.setpts(to_dev(np.zeros(3, np.float32)), to_dev(np.zeros(3, np.float32)))
+    c = torch.ones(3, dtype=torch.complex64, device=dev())
+    f = torch.empty((16, 16), dtype=torch.complex64, device=dev())
+    p.execute(c, f)
+    torch.cuda.synchronize()
+    p.destroy()
+
+
+def test_execute_before_setpts_is_state_error(nf):
+    p = nf.Plan(1, (16, 16), 1e-5, "f32")
+    c = torch.ones(3, dtype=torch.complex64, device=dev())
+    f = torch.empty((16, 16), dtype=torch.complex64, device=dev())
+    p.M = 3  # bypass the Python-side check to reach the C ABI
+    with pytest.raises(nf.NufftError) as ei:
+        p.execute(c, f)
+    assert ei.value.code == -2
+    p.destroy()
+
+
+# ---------------------------------------------------------------------------------------------
+# Single steps
+# ---------------------------------------------------------------------------------------------
+
+STEP_CASES = [
+    Workload("st", 2, (100, 72), 50_001, 1e-5, "f32", seed=31),
+    Workload("st", 2, (64, 48), 20_000, 1e-12, "f64", seed=32),
+    Workload("st", 3, (24, 20, 18), 40_000, 1e-5, "f32", seed=33),
+    Workload("st", 3, (16, 16, 16), 20_000, 1e-2, "f32", seed=34),
+    Workload("st", 3, (20, 16, 12), 15_000, 1e-9, "f64", seed=35),
+    Workload("st", 3, (16, 16, 16), 30_000, 1e-5, "f32", dist="box", seed=36),
+]
+
+
+def _step_tol(prec, fp32_atomics=False):
+    """Single-step bars.  fp32 kernel weights and one fp32 rounding per output give ~1e-7; the
+    GM-sort spread adds every contribution with an fp32 global atomic, whose rounding error grows
+    like sqrt(contributions per cell) * 2^-24 (~1e-5 for thousands of points per cell)."""
+    if prec == "f64":
+        return 1e-12
+    return 1e-5 if fp32_atomics else 1e-6
+
+
+@pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: f"{w.dim}d_{w.N}_{w.precision}_{w.eps:g}_{w.dist}")
+@pytest.mark.parametrize("method", [2, 1], ids=["SM", "GMsort"])
+def test_spread_step(nf, orc, wl, method):
+    _announce(f"spread {wl.N} {wl.precision} eps={wl.eps} {wl.dist} method={method}")
+    inp = make_inputs(wl, want_f=False)
+    p = nf.Plan(1, wl.N, wl.eps, wl.precision, method=method, subproblem_cap=500 if wl.dist == "box" else 0)
+    p.setpts(*[to_dev(x) for x in inp["X"]])
+    grid = torch.empty(p.fine_cells, dtype=cdtype(wl.precision), device=dev())
+    p.spread(to_dev(inp["c"]), grid)
+    torch.cuda.synchronize()
+    ref = orc.spread(inp["X"], inp["c"], p.n, p.w, p.beta)
+    err = orc.rel_l2(grid.cpu().numpy(), ref.ravel())
+    assert err <= _step_tol(wl.precision, fp32_atomics=(method == 1)), err
+    p.destroy()
+
+
+@pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: f"{w.dim}d_{w.N}_{w.precision}_{w.eps:g}_{w.dist}")
+def test_interp_step(nf, orc, wl):
+    _announce(f"interp {wl.N} {wl.precision} eps={wl.eps} {wl.dist}")
+    inp = make_inputs(wl, want_f=False)
+    p = nf.Plan(2, wl.N, wl.eps, wl.precision)
+    p.setpts(*[to_dev(x) for x in inp["X"]])
+    rng = np.random.default_rng(99)
+    g = (rng.standard_normal(p.fine_cells) + 1j * rng.standard_normal(p.fine_cells)).astype(
+        np.complex64 if wl.precision == "f32" else np.complex128)
+    c = torch.empty(wl.M, dtype=cdtype(wl.precision), device=dev())
+    p.interp(to_dev(g), c)
+    torch.cuda.synchronize()
+    ref = orc.interp(inp["X"], g.reshape(tuple(reversed(p.n))), p.w, p.beta)
+    err = orc.rel_l2(c.cpu().numpy(), ref)
+    assert err <= _step_tol(wl.precision), err
+    p.destroy()
+
+
+@pytest.mark.parametrize("N,prec", [((100, 72), "f32"), ((33, 17), "f64"), ((24, 20, 18), "f32"),
+                                    ((9, 16, 7), "f64")])
+def test_correction_steps(nf, orc, N, prec):
+    eps = 1e-5 if prec == "f32" else 1e-11
+    prm = orc.Params(N, eps)
+    rng = np.random.default_rng(5)
+    cd = np.complex64 if prec == "f32" else np.complex128
+    # type 1 step 3
+    p1 = nf.Plan(1, N, eps, prec)
+    fhat = (rng.standard_normal(tuple(reversed(prm.n))) + 1j * rng.standard_normal(tuple(reversed(prm.n)))).astype(cd)
+    f = torch.empty(tuple(reversed(N)), dtype=cdtype(prec), device=dev())
+    p1.deconvolve(to_dev(fhat), f)
+    torch.cuda.synchronize()
+    ref = orc.truncate_correct(fhat.astype(np.complex128), prm)
+    assert orc.rel_l2(f.cpu().numpy(), ref) <= (1e-6 if prec == "f32" else 1e-13)
+    p1.destroy()
+    # type 2 step 1
+    p2 = nf.Plan(2, N, eps, prec)
+    fin = (rng.standard_normal(tuple(reversed(N))) + 1j * rng.standard_normal(tuple(reversed(N)))).astype(cd)
+    out = torch.full((int(np.prod(prm.n)),), 7.0, dtype=cdtype(prec), device=dev())
+    p2.precorrect_pad(to_dev(fin), out)
+    torch.cuda.synchronize()
+    ref2 = orc.precorrect_pad(fin.astype(np.complex128), prm)
+    assert orc.rel_l2(out.cpu().numpy(), ref2.ravel()) <= (1e-6 if prec == "f32" else 1e-13)
+    p2.destroy()
+
+
+# ---------------------------------------------------------------------------------------------
+# Whole transforms vs the oracle NUFFT (1e-5 fp32, 1e-10 fp64) and vs the exact sums (10 eps)
+# ---------------------------------------------------------------------------------------------
+
+E2E_CASES = [
+    WORKLOADS["2d_n64_m1e4_f32_e5"],                                   # full configuration
+    Workload("e", 2, (100, 72), 50_001, 1e-5, "f32", seed=41),
+    Workload("e", 2, (64, 64), 30_000, 1e-12, "f64", seed=42),
+    Workload("e", 2, (33, 17), 5_000, 1e-9, "f64", seed=43),
+    Workload("e", 3, (24, 20, 18), 40_000, 1e-5, "f32", seed=44),
+    Workload("e", 3, (32, 32, 32), 40_000, 1e-2, "f32", seed=45),
+    Workload("e", 3, (32, 32, 32), 60_000, 1e-5, "f32", dist="cluster", seed=46),
+    Workload("e", 3, (20, 16, 12), 15_000, 1e-9, "f64", seed=47),
+    Workload("e", 3, (16, 16, 16), 30_000, 1e-5, "f32", dist="box", seed=48),
+    Workload("e", 3, (9, 16, 7), 2_000, 1e-12, "f64", seed=49),
+]
+
+
+@pytest.mark.parametrize("wl", E2E_CASES, ids=lambda w: f"{w.dim}d_{w.N}_{w.M}_{w.precision}_{w.eps:g}_{w.dist}")
+def test_type1_vs_oracle(nf, orc, wl):
+    _announce(f"type1 {wl.N} M={wl.M} {wl.precision} eps={wl.eps} {wl.dist}")
+    inp = make_inputs(wl, want_f=False)
+    f = gpu_type1(nf, inp["X"], inp["c"], wl.N, wl.eps, wl.precision)
+    ref = orc.nufft_type1(inp["X"], inp["c"], wl.N, wl.eps)
+    err = orc.rel_l2(f, ref)
+    assert err <= tol_for(wl.precision), err
+
+
+@pytest.mark.parametrize("wl", E2E_CASES, ids=lambda w: f"{w.dim}d_{w.N}_{w.M}_{w.precision}_{w.eps:g}_{w.dist}")
+def test_type2_vs_oracle(nf, orc, wl):
+    _announce(f"type2 {wl.N} M={wl.M} {wl.precision} eps={wl.eps} {wl.dist}")
+    inp = make_inputs(wl)
+    c = gpu_type2(nf, inp["X"], inp["f"], wl.N, wl.eps, wl.precision)
+    ref = orc.nufft_type2(inp["X"], inp["f"], wl.N, wl.eps)
+    err = orc.rel_l2(c, ref)
+    assert err <= tol_for(wl.precision), err
+
+
+def test_small_config_vs_exact_sums(nf, orc):
+    """2D 64x64 modes, M = 10,000, fp32 eps = 1e-5: both types within 10 eps of eqs. (1), (3)."""
+    wl = WORKLOADS["2d_n64_m1e4_f32_e5"]
+    inp = make_inputs(wl)
+    f = gpu_type1(nf, inp["X"], inp["c"], wl.N, wl.eps, wl.precision)
+    assert orc.rel_l2(f, orc.direct_type1(inp["X"], inp["c"], wl.N)) <= 10 * wl.eps
+    c = gpu_type2(nf, inp["X"], inp["f"], wl.N, wl.eps, wl.precision)
+    assert orc.rel_l2(c, orc.direct_type2(inp["X"], inp["f"], wl.N)) <= 10 * wl.eps
+
+
+@pytest.mark.parametrize("N,prec,eps", [((64, 64), "f32", 1e-5), ((24, 20, 18), "f64", 1e-12)])
+def test_adjointness_on_gpu(nf, N, prec, eps):
+    """<type1(c), f> = <c, type2(f)> (the steps are exact transposes)."""
+    wl = Workload("a", len(N), N, 20_000, eps, prec, seed=51)
+    inp = make_inputs(wl)
+    f1 = gpu_type1(nf, inp["X"], inp["c"], N, eps, prec).astype(np.complex128)
+    c2 = gpu_type2(nf, inp["X"], inp["f"], N, eps, prec).astype(np.complex128)
+    lhs = np.vdot(inp["f"].astype(np.complex128).ravel(), f1.ravel())
+    rhs = np.vdot(c2, inp["c"].astype(np.complex128))
+    rel = abs(lhs - rhs) / (np.linalg.norm(f1) * np.linalg.norm(inp["f"]))
+    assert rel <= (1e-5 if prec == "f32" else 1e-12), rel
+
+
+def test_methods_agree_and_caps(nf, orc):
+    """GM-sort and SM with several subproblem caps all match the oracle."""
+    wl = Workload("m", 3, (24, 20, 18), 40_000, 1e-5, "f32", seed=52)
+    inp = make_inputs(wl, want_f=False)
+    ref = orc.nufft_type1(inp["X"], inp["c"], wl.N, wl.eps)
+    for kw in ({"method": 1}, {"method": 2, "subproblem_cap": 1}, {"method": 2, "subproblem_cap": 100},
+               {"method": 2, "bins": (8, 8, 8)}, {"method": 2, "bins": (4, 8, 16)}):
+        f = gpu_type1(nf, inp["X"], inp["c"], wl.N, wl.eps, wl.precision, **kw)
+        assert orc.rel_l2(f, ref) <= 1e-5, kw
+
+
+def test_empty_and_single_point(nf, orc):
+    N = (16, 12)
+    for prec in ("f32", "f64"):
+        # M = 0: type 1 gives zeros, type 2 writes nothing
+        X0 = [np.zeros(0, np.float32 if prec == "f32" else np.float64)] * 2
+        f = gpu_type1(nf, X0, np.zeros(0, np.complex64), N, 1e-6, prec)
+        assert np.all(f == 0)
+        # M = 1: closed form exp(-i k.x0)
+        x0 = [np.array([0.3], np.float64), np.array([-2.0], np.float64)]
+        X1 = [x.astype(np.float32 if prec == "f32" else np.float64) for x in x0]
+        f = gpu_type1(nf, X1, np.ones(1, np.complex64 if prec == "f32" else np.complex128), N, 1e-6, prec)
+        ref = orc.nufft_type1(X1, np.ones(1, complex), N, 1e-6)
+        assert orc.rel_l2(f, ref) <= tol_for(prec)
+
+
+def test_type2_bitwise_reproducible_type1_close(nf):
+    wl = Workload("r", 3, (32, 32, 32), 50_000, 1e-5, "f32", seed=53)
+    inp = make_inputs(wl)
+    a = gpu_type2(nf, inp["X"], inp["f"], wl.N, wl.eps, wl.precision)
+    b = gpu_type2(nf, inp["X"], inp["f"], wl.N, wl.eps, wl.precision)
+    np.testing.assert_array_equal(a, b)
+    f1 = gpu_type1(nf, inp["X"], inp["c"], wl.N, wl.eps, wl.precision)
+    f2 = gpu_type1(nf, inp["X"], inp["c"], wl.N, wl.eps, wl.precision)
+    assert np.linalg.norm(f1 - f2) <= 1e-6 * np.linalg.norm(f1)
+
+
+def test_repeated_execute_and_resetpts(nf, orc):
+    """One plan: several executes with new strengths, then new points (plan reuse)."""
+    N = (40, 36)
+    p = nf.Plan(1, N, 1e-5, "f32")
+    f = torch.empty((36, 40), dtype=torch.complex64, device=dev())
+    for seed in (61, 62):
+        wl = Workload("p", 2, N, 7_000 + seed, 1e-5, "f32", seed=seed)
+        inp = make_inputs(wl, want_f=False)
+        p.setpts(*[to_dev(x) for x in inp["X"]])
+        for k in range(2):
+            c = inp["c"] * (k + 1)
+            p.execute(to_dev(c), f)
+            torch.cuda.synchronize()
+            ref = orc.nufft_type1(inp["X"], c, N, 1e-5)
+            assert orc.rel_l2(f.cpu().numpy(), ref) <= 1e-5
+    p.destroy()
