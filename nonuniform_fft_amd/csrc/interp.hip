@@ -1,9 +1,13 @@
 // Type 2 step 3: interpolation from the fine grid at the nonuniform points
 // (cuFINUFFT paper, Sec. II-B, the weighted sum that follows eq. (12); kernel as in eq. (8)).
 //
-// GM-sort scheme (Sec. III-B): one thread per point in bin-sorted order, so neighbouring lanes
-// read neighbouring grid cells; each thread gathers its w^d cells, sums along x first, and
-// writes c at the point's original index.
+// Two schemes on the bin-sorted points of setpts:
+//  * GM-sort (Sec. III-B): one thread per point in bin-sorted order, so neighbouring lanes read
+//    neighbouring grid cells; each thread gathers its w^d cells from the fine grid in HBM.
+//  * SM (the read-side counterpart of the SM spreading subproblems): one workgroup per
+//    subproblem copies the padded bin of the fine grid into LDS with coalesced row reads, then
+//    each lane evaluates one point from LDS.
+// Both sum along x first and write c at the point's original index.
 #include "nufft_internal.h"
 
 namespace nufft {
@@ -61,15 +65,120 @@ __global__ void __launch_bounds__(kInterpBlock) k_interp_gm(GeomArgs g, const cp
     c[g.perm[i]] = out;
 }
 
-template <typename T, int DIM>
-hipError_t interp_dim(const GeomArgs& g, const void* grid, void* c, hipStream_t st) {
+constexpr int kInterpSmBlock = 512;
+
+__host__ __device__ inline int interp_row_pitch(int p1) { return p1; }
+
+template <typename T, int DIM, int W>
+__global__ void __launch_bounds__(kInterpSmBlock) k_interp_sm(GeomArgs g, const cplx<T>* __restrict__ grid,
+                                                              cplx<T>* __restrict__ c, int p1, int p2,
+                                                              int p3) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    cplx<T>* tile = (cplx<T>*)smem;
+    const int pc = p1, pp = p1 * p2;
+    const int sid = blockIdx.x;
+    const int bin = g.sub[3 * sid + 0];
+    const int start = g.sub[3 * sid + 1];
+    const int len = g.sub[3 * sid + 2];
+    int origin[3] = {0, 0, 0};
+    {
+        int b0 = bin % g.nb[0];
+        int b1 = (bin / g.nb[0]) % g.nb[1];
+        int b2 = bin / (g.nb[0] * g.nb[1]);
+        origin[0] = b0 * g.m[0] - W / 2;
+        origin[1] = b1 * g.m[1] - W / 2;
+        if (DIM == 3) origin[2] = b2 * g.m[2] - W / 2;
+    }
+    // copy the padded bin (with periodic wrap) into LDS; consecutive lanes read consecutive x
+    const int P = p1 * p2 * p3;
+    for (int k = threadIdx.x; k < P; k += kInterpSmBlock) {
+        const int s1 = k % p1;
+        const int rest = k / p1;
+        const int s2 = rest % p2;
+        const int s3 = rest / p2;
+        int g1 = origin[0] + s1, g2 = origin[1] + s2, g3 = (DIM == 3) ? origin[2] + s3 : 0;
+        while (g1 < 0) g1 += g.n[0];
+        while (g1 >= g.n[0]) g1 -= g.n[0];
+        while (g2 < 0) g2 += g.n[1];
+        while (g2 >= g.n[1]) g2 -= g.n[1];
+        if (DIM == 3) {
+            while (g3 < 0) g3 += g.n[2];
+            while (g3 >= g.n[2]) g3 -= g.n[2];
+        }
+        tile[k] = grid[(size_t)g1 + (size_t)g.n[0] * ((size_t)g2 + (size_t)g.n[1] * (size_t)g3)];
+    }
+    __syncthreads();
+    const T beta = (T)g.beta;
+    const int pd[3] = {p1, p2, p3};
+    for (int i = threadIdx.x; i < len; i += kInterpSmBlock) {
+        const int64_t j = (int64_t)start + i;
+        T ker[DIM][W];
+        int l0[3] = {0, 0, 0};
+#pragma unroll
+        for (int d = 0; d < DIM; ++d) {
+            double t = grid_t((double)((const T*)g.xs[d])[j], g.s[d]);
+            int l;
+            fold_t(t, g.n[d], l);
+            int v = es_weights<T, W>(t, beta, ker[d]) - origin[d];
+            l0[d] = min(max(v, 0), pd[d] - W);
+        }
+        T are = 0, aim = 0;
+#pragma unroll
+        for (int q3 = 0; q3 < (DIM == 3 ? W : 1); ++q3) {
+            T pre = 0, pim = 0;
+#pragma unroll
+            for (int q2 = 0; q2 < W; ++q2) {
+                const cplx<T>* row = tile + l0[0] + (l0[1] + q2) * pc + (DIM == 3 ? (l0[2] + q3) * pp : 0);
+                T rre = 0, rim = 0;
+#pragma unroll
+                for (int q1 = 0; q1 < W; ++q1) {
+                    const cplx<T> v = row[q1];
+                    rre += v.re * ker[0][q1];
+                    rim += v.im * ker[0][q1];
+                }
+                pre += rre * ker[1][q2];
+                pim += rim * ker[1][q2];
+            }
+            const T kz = (DIM == 3) ? ker[DIM - 1][q3] : (T)1;
+            are += pre * kz;
+            aim += pim * kz;
+        }
+        cplx<T> out;
+        out.re = are;
+        out.im = aim;
+        c[g.perm[j]] = out;
+    }
+}
+
+template <typename T, int DIM, int W>
+hipError_t interp_w(int method, const GeomArgs& g, const void* grid, void* c, hipStream_t st) {
     if (g.M <= 0) return hipSuccess;
-    dim3 grd((unsigned)((g.M + kInterpBlock - 1) / kInterpBlock));
-    switch (g.w) {
-#define NUFFT_CASE(WW)                                                                          \
-    case WW:                                                                                    \
-        k_interp_gm<T, DIM, WW><<<grd, kInterpBlock, 0, st>>>(g, (const cplx<T>*)grid, (cplx<T>*)c); \
+    if (method == NUFFT_METHOD_GM_SORT) {
+        dim3 grd((unsigned)((g.M + kInterpBlock - 1) / kInterpBlock));
+        k_interp_gm<T, DIM, W><<<grd, kInterpBlock, 0, st>>>(g, (const cplx<T>*)grid, (cplx<T>*)c);
         return hipGetLastError();
+    }
+    if (g.nsub <= 0) return hipSuccess;
+    const int p1 = g.m[0] + W, p2 = g.m[1] + W, p3 = (DIM == 3) ? g.m[2] + W : 1;
+    const size_t lds = (size_t)p1 * p2 * p3 * sizeof(cplx<T>);
+    if (lds > spread_lds_limit()) return hipErrorInvalidConfiguration;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_interp_sm<T, DIM, W>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)spread_lds_limit());
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    k_interp_sm<T, DIM, W><<<dim3((unsigned)g.nsub), kInterpSmBlock, lds, st>>>(
+        g, (const cplx<T>*)grid, (cplx<T>*)c, p1, p2, p3);
+    return hipGetLastError();
+}
+
+template <typename T, int DIM>
+hipError_t interp_dim(int method, const GeomArgs& g, const void* grid, void* c, hipStream_t st) {
+    switch (g.w) {
+#define NUFFT_CASE(WW) case WW: return interp_w<T, DIM, WW>(method, g, grid, c, st);
         NUFFT_CASE(2) NUFFT_CASE(3) NUFFT_CASE(4) NUFFT_CASE(5) NUFFT_CASE(6) NUFFT_CASE(7)
         NUFFT_CASE(8) NUFFT_CASE(9) NUFFT_CASE(10) NUFFT_CASE(11) NUFFT_CASE(12) NUFFT_CASE(13)
         NUFFT_CASE(14) NUFFT_CASE(15) NUFFT_CASE(16)
@@ -80,9 +189,17 @@ hipError_t interp_dim(const GeomArgs& g, const void* grid, void* c, hipStream_t 
 
 }  // namespace
 
-hipError_t launch_interp(int prec, const GeomArgs& g, const void* grid, void* c, hipStream_t st) {
-    if (prec == 0) return g.dim == 2 ? interp_dim<float, 2>(g, grid, c, st) : interp_dim<float, 3>(g, grid, c, st);
-    return g.dim == 2 ? interp_dim<double, 2>(g, grid, c, st) : interp_dim<double, 3>(g, grid, c, st);
+hipError_t launch_interp(int prec, int method, const GeomArgs& g, const void* grid, void* c,
+                         hipStream_t st) {
+    if (prec == 0)
+        return g.dim == 2 ? interp_dim<float, 2>(method, g, grid, c, st) : interp_dim<float, 3>(method, g, grid, c, st);
+    return g.dim == 2 ? interp_dim<double, 2>(method, g, grid, c, st) : interp_dim<double, 3>(method, g, grid, c, st);
+}
+
+size_t interp_tile_bytes(int prec, int dim, int w, const int* m) {
+    size_t cells = 1;
+    for (int i = 0; i < dim; ++i) cells *= (size_t)(m[i] + w);
+    return cells * 2 * (prec == 0 ? sizeof(float) : sizeof(double));
 }
 
 }  // namespace nufft

@@ -174,7 +174,9 @@ struct GeomArgs {
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_spread(int prec, int method, const GeomArgs& g, const void* c, void* grid,
                          hipStream_t st);
-hipError_t launch_interp(int prec, const GeomArgs& g, const void* grid, void* c, hipStream_t st);
+hipError_t launch_interp(int prec, int method, const GeomArgs& g, const void* grid, void* c,
+                         hipStream_t st);
+size_t interp_tile_bytes(int prec, int dim, int w, const int* m);
 hipError_t launch_deconvolve(int prec, int dim, const int64_t* N, const int64_t* n,
                              const void* pcorr, const void* fhat, void* f, hipStream_t st);
 hipError_t launch_precorrect_pad(int prec, int dim, const int64_t* N, const int64_t* n,

@@ -526,7 +526,7 @@ int nufft_execute(nufft_plan plan, void* c, void* f) {
         record(plan, 2);
         if ((rc = fft_exec(plan, plan->fft_bwd, plan->grid.p)) != NUFFT_OK) return rc;
         record(plan, 3);
-        NUFFT_HIP(nufft::launch_interp(plan->prec, g, plan->grid.p, c, plan->stream));
+        NUFFT_HIP(nufft::launch_interp(plan->prec, plan->method, g, plan->grid.p, c, plan->stream));
         record(plan, 4);
     }
     plan->stage_recorded = 1;
@@ -590,7 +590,7 @@ int nufft_interp(nufft_plan plan, const void* grid, void* c) {
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
     if (!grid || (plan->M > 0 && !c)) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
     nufft::GeomArgs g = geom(plan);
-    NUFFT_HIP(nufft::launch_interp(plan->prec, g, grid, c, plan->stream));
+    NUFFT_HIP(nufft::launch_interp(plan->prec, plan->method, g, grid, c, plan->stream));
     return NUFFT_OK;
 }
 

@@ -11,102 +11,130 @@
 //
 // gfx950 notes.  LDS float atomics are slow on this part (ds_add_f32 measured ~0.33 lane-op per
 // clock per CU against ~7.8 for ds_add_f64), so the LDS tile accumulates in fp64 for both
-// precisions: each complex update is two ds_add_f64.  Work inside a chunk of staged points is
-// split as (point, stencil row) items: a lane takes one row of w cells along x of one point,
-// so the lanes of a wavefront cover whole rows of a few points.
+// precisions: each complex update is two ds_add_f64 into separate real/imaginary planes.  Work
+// in a chunk of staged points is split into (point, q1, q2) items -- the x-y patch of a point's
+// stencil -- and each item walks the w cells along z, so a wavefront's lanes hit one or two
+// w x w patches whose rows are spread over the LDS banks by the padded row pitch.  Workgroups
+// of 1024 lanes keep 16 wavefronts per CU even when one padded bin fills most of the LDS.
 #include "nufft_internal.h"
 
 namespace nufft {
 namespace {
 
-constexpr int kSpreadBlock = 256;
-constexpr int kChunk = 64;            // points staged per round
+constexpr int kSpreadBlock = 1024;   // 16 wavefronts: one workgroup keeps a CU busy on its own
 constexpr int kGmBlock = 128;
+
+// Points staged per round: about 24 KB of LDS for kernel weights, local offsets and strengths.
+template <typename T, int DIM, int W>
+struct SmCfg {
+    static constexpr int kPerPoint = DIM * W * (int)sizeof(T) + 4 * (int)sizeof(int) + 2 * (int)sizeof(T);
+    static constexpr int kRaw = 24576 / kPerPoint;
+    static constexpr int kChunk = kRaw >= 256 ? 256 : (kRaw < 32 ? 32 : (kRaw & ~31));
+};
 
 template <typename T, int DIM, int W>
 struct Stage {
-    T ker[kChunk][DIM][W];
-    int l0[kChunk][3];
-    T cre[kChunk], cim[kChunk];
+    static constexpr int CH = SmCfg<T, DIM, W>::kChunk;
+    T ker[CH][DIM][W];
+    int l0[CH][4];
+    T cre[CH], cim[CH];
 };
+
+// LDS tile of a padded bin: separate fp64 planes for real and imaginary parts, row pitch pc with
+// pc = W (mod 16), so the w x w patch of one point's x-y stencil covers the 16 bank pairs evenly.
+__host__ __device__ inline int tile_row_pitch(int p1, int w) {
+    int pc = p1;
+    while (((pc - w) % 16 + 16) % 16 != 0) ++pc;
+    return pc;
+}
 
 template <typename T, int DIM, int W>
 __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c,
                                                             cplx<T>* __restrict__ grid, int p1, int p2,
-                                                            int p3) {
+                                                            int p3, int pc) {
+    using St = Stage<T, DIM, W>;
+    constexpr int CH = St::CH;
+    constexpr int WW = W * W;
     extern __shared__ __align__(16) unsigned char smem[];
-    double* tile = (double*)smem;
-    const int P = p1 * p2 * p3;
-    Stage<T, DIM, W>* st = (Stage<T, DIM, W>*)(smem + (size_t)P * 2 * sizeof(double));
+    const int pp = pc * p2;                 // plane pitch
+    const int PL = pp * p3;                 // padded cells
+    double* tre = (double*)smem;
+    double* tim = tre + PL;
+    St* st = (St*)(tim + PL);
 
     const int sid = blockIdx.x;
     const int bin = g.sub[3 * sid + 0];
     const int start = g.sub[3 * sid + 1];
     const int len = g.sub[3 * sid + 2];
-    int bcoord[3];
-    bcoord[0] = bin % g.nb[0];
-    bcoord[1] = (bin / g.nb[0]) % g.nb[1];
-    bcoord[2] = bin / (g.nb[0] * g.nb[1]);
     int origin[3] = {0, 0, 0};
+    {
+        int b0 = bin % g.nb[0];
+        int b1 = (bin / g.nb[0]) % g.nb[1];
+        int b2 = bin / (g.nb[0] * g.nb[1]);
+        origin[0] = b0 * g.m[0] - W / 2;
+        origin[1] = b1 * g.m[1] - W / 2;
+        if (DIM == 3) origin[2] = b2 * g.m[2] - W / 2;
+    }
     const int pd[3] = {p1, p2, p3};
-#pragma unroll
-    for (int i = 0; i < DIM; ++i) origin[i] = bcoord[i] * g.m[i] - W / 2;
-
-    for (int k = threadIdx.x; k < 2 * P; k += kSpreadBlock) tile[k] = 0.0;
+    for (int k = threadIdx.x; k < 2 * PL; k += kSpreadBlock) tre[k] = 0.0;
 
     const T beta = (T)g.beta;
-    constexpr int ROWS = (DIM == 3) ? W * W : W;
-    for (int c0 = 0; c0 < len; c0 += kChunk) {
-        const int np = min(kChunk, len - c0);
+    for (int c0 = 0; c0 < len; c0 += CH) {
+        const int np = min(CH, len - c0);
         __syncthreads();   // previous chunk consumed (and tile zeroed on the first round)
-        if (threadIdx.x < np) {
-            const int p = threadIdx.x;
+        // stage kernel weights: one thread per (point, dimension)
+        if (threadIdx.x < np * DIM) {
+            const int p = threadIdx.x / DIM;
+            const int i = threadIdx.x - p * DIM;
             const int64_t j = (int64_t)start + c0 + p;
-#pragma unroll
-            for (int i = 0; i < DIM; ++i) {
-                double t = grid_t((double)((const T*)g.xs[i])[j], g.s[i]);
-                int l;
-                fold_t(t, g.n[i], l);
-                int l0 = es_weights<T, W>(t, beta, st->ker[p][i]) - origin[i];
-                st->l0[p][i] = min(max(l0, 0), pd[i] - W);
+            double t = grid_t((double)((const T*)g.xs[i])[j], g.s[i]);
+            int l;
+            fold_t(t, g.n[i], l);
+            int l0 = es_weights<T, W>(t, beta, st->ker[p][i]) - origin[i];
+            st->l0[p][i] = min(max(l0, 0), pd[i] - W);
+            if (i == 0) {
+                const cplx<T> v = c[g.perm[j]];
+                st->cre[p] = v.re;
+                st->cim[p] = v.im;
             }
-            cplx<T> v = c[g.perm[j]];
-            st->cre[p] = v.re;
-            st->cim[p] = v.im;
         }
         __syncthreads();
-        const int items = np * ROWS;
+        // (point, q1, q2) items; 3D loops over q3
+        const int items = np * WW;
         for (int it = threadIdx.x; it < items; it += kSpreadBlock) {
-            const int p = it / ROWS;
-            const int r = it - p * ROWS;
-            const int q2 = r % W;
-            T wr = st->ker[p][1][q2];
-            int row = st->l0[p][1] + q2;
-            if (DIM == 3) {
-                const int q3 = r / W;
-                wr *= st->ker[p][DIM - 1][q3];
-                row += p2 * (st->l0[p][2] + q3);
-            }
-            const double vre = (double)(st->cre[p] * wr);
-            const double vim = (double)(st->cim[p] * wr);
-            double* dst = tile + 2 * ((size_t)row * p1 + st->l0[p][0]);
+            const int p = it / WW;
+            const int r = it - p * WW;
+            const int q2 = r / W;
+            const int q1 = r - q2 * W;
+            const T wxy = st->ker[p][0][q1] * st->ker[p][1][q2];
+            const double vre = (double)(st->cre[p] * wxy);
+            const double vim = (double)(st->cim[p] * wxy);
+            int base = st->l0[p][0] + q1 + (st->l0[p][1] + q2) * pc;
+            if (DIM == 2) {
+                atomicAdd(tre + base, vre);
+                atomicAdd(tim + base, vim);
+            } else {
+                base += st->l0[p][2] * pp;
 #pragma unroll
-            for (int q1 = 0; q1 < W; ++q1) {
-                const double k1 = (double)st->ker[p][0][q1];
-                atomicAdd(dst + 2 * q1, vre * k1);
-                atomicAdd(dst + 2 * q1 + 1, vim * k1);
+                for (int q3 = 0; q3 < W; ++q3) {
+                    const double kz = (double)st->ker[p][DIM - 1][q3];
+                    atomicAdd(tre + base + q3 * pp, vre * kz);
+                    atomicAdd(tim + base + q3 * pp, vim * kz);
+                }
             }
         }
     }
     __syncthreads();
     // flush the padded bin with periodic wrap (eq. (15))
+    const int P = p1 * p2 * p3;
     for (int k = threadIdx.x; k < P; k += kSpreadBlock) {
-        const double re = tile[2 * k], im = tile[2 * k + 1];
+        const int s1 = k % p1;
+        const int rest = k / p1;
+        const int s2 = rest % p2;
+        const int s3 = rest / p2;
+        const int li = s1 + s2 * pc + s3 * pp;
+        const double re = tre[li], im = tim[li];
         if (re == 0.0 && im == 0.0) continue;
-        int s1 = k % p1;
-        int rest = k / p1;
-        int s2 = rest % p2;
-        int s3 = rest / p2;
         int g1 = origin[0] + s1, g2 = origin[1] + s2, g3 = (DIM == 3) ? origin[2] + s3 : 0;
         while (g1 < 0) g1 += g.n[0];
         while (g1 >= g.n[0]) g1 -= g.n[0];
@@ -183,8 +211,9 @@ hipError_t spread_w(int method, const GeomArgs& g, const void* c, void* grid, hi
         return hipGetLastError();
     }
     if (g.nsub <= 0) return hipSuccess;
-    int p1 = g.m[0] + W, p2 = g.m[1] + W, p3 = (DIM == 3) ? g.m[2] + W : 1;
-    size_t lds = (size_t)p1 * p2 * p3 * 2 * sizeof(double) + sizeof(Stage<T, DIM, W>);
+    const int p1 = g.m[0] + W, p2 = g.m[1] + W, p3 = (DIM == 3) ? g.m[2] + W : 1;
+    const int pc = tile_row_pitch(p1, W);
+    const size_t lds = (size_t)pc * p2 * p3 * 2 * sizeof(double) + sizeof(Stage<T, DIM, W>);
     if (lds > spread_lds_limit()) return hipErrorInvalidConfiguration;
     static bool attr_set = false;
     if (!attr_set) {
@@ -195,7 +224,7 @@ hipError_t spread_w(int method, const GeomArgs& g, const void* c, void* grid, hi
         attr_set = true;
     }
     k_spread_sm<T, DIM, W><<<dim3((unsigned)g.nsub), kSpreadBlock, lds, st>>>(
-        g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2, p3);
+        g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2, p3, pc);
     return hipGetLastError();
 }
 
@@ -228,8 +257,8 @@ size_t stage_bytes_dim(int w) {
 size_t spread_lds_limit() { return 160 * 1024; }
 
 size_t spread_tile_bytes(int prec, int dim, int w, const int* m) {
-    size_t cells = 1;
-    for (int i = 0; i < dim; ++i) cells *= (size_t)(m[i] + w);
+    size_t cells = (size_t)tile_row_pitch(m[0] + w, w);
+    for (int i = 1; i < dim; ++i) cells *= (size_t)(m[i] + w);
     size_t stage = (prec == 0) ? (dim == 2 ? stage_bytes_dim<float, 2>(w) : stage_bytes_dim<float, 3>(w))
                                : (dim == 2 ? stage_bytes_dim<double, 2>(w) : stage_bytes_dim<double, 3>(w));
     return cells * 2 * sizeof(double) + stage;

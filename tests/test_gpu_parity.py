@@ -159,10 +159,11 @@ def test_spread_step(nf, orc, wl, method):
 
 
 @pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: f"{w.dim}d_{w.N}_{w.precision}_{w.eps:g}_{w.dist}")
-def test_interp_step(nf, orc, wl):
-    _announce(f"interp {wl.N} {wl.precision} eps={wl.eps} {wl.dist}")
+@pytest.mark.parametrize("method", [2, 1], ids=["SM", "GMsort"])
+def test_interp_step(nf, orc, wl, method):
+    _announce(f"interp {wl.N} {wl.precision} eps={wl.eps} {wl.dist} method={method}")
     inp = make_inputs(wl, want_f=False)
-    p = nf.Plan(2, wl.N, wl.eps, wl.precision)
+    p = nf.Plan(2, wl.N, wl.eps, wl.precision, method=method, subproblem_cap=500 if wl.dist == "box" else 0)
     p.setpts(*[to_dev(x) for x in inp["X"]])
     rng = np.random.default_rng(99)
     g = (rng.standard_normal(p.fine_cells) + 1j * rng.standard_normal(p.fine_cells)).astype(
