@@ -1,12 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the 3D type 1 + type 2 NUFFT on one MI355X.
 
-One step = the whole hot path over one batch of points: bin-sort (setpts) + type 1
-(spread, FFT, deconvolve) on a type 1 plan, then setpts + type 2 (pre-correct/pad, FFT,
-interpolate) on a type 2 plan, for the 3D fp32 eps = 1e-5 workload (N = 128^3 modes,
-M = 2^24 iid uniform points, complex Gaussian strengths and coefficients).  Inputs are
-resident in HBM before timing starts.  `value` is NU points per second through the
-type-1 + type-2 pair (M / step time).
+One step = the whole hot path over one batch of points: bin-sort (setpts), type 1
+(clear, spread, FFT, deconvolve) and type 2 on the same sorted points (pre-correct/pad,
+FFT, interpolate), for the 3D fp32 eps = 1e-5 workload (N = 128^3 modes, M = 2^24 iid
+uniform points, complex Gaussian strengths and coefficients).  Inputs are resident in
+HBM before timing starts.  `value` is NU points per second through the type-1 + type-2
+pair including the sort (M / step time).
 
 Prints ONE JSON line.  Extra fields give per-type exec-only throughput, per-stage times,
 the roofline of the dominant kernel and the CPU-oracle baseline.
@@ -82,42 +82,40 @@ def main():
     f_out = torch.empty(tuple(reversed(wl.N)), dtype=cdt, device=dev)
     c_out = torch.empty(wl.M, dtype=cdt, device=dev)
     stream = torch.cuda.current_stream()
-    p1 = nf.Plan(1, wl.N, wl.eps, wl.precision, stream=stream, timing=True, method=args.method)
-    p2 = nf.Plan(2, wl.N, wl.eps, wl.precision, stream=stream, timing=True)
+    plan = nf.Plan(1, wl.N, wl.eps, wl.precision, stream=stream, timing=True, method=args.method)
 
     def step():
-        p1.setpts(*X)
-        p1.execute(c, f_out)
-        p2.setpts(*X)
-        p2.execute(c_out, f_in)
+        plan.setpts(*X)                   # bin-sort + subproblems
+        plan.execute(c, f_out)            # type 1: spread, FFT, deconvolve
+        plan.execute_adjoint(c_out, f_in)  # type 2 on the same sorted points
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    stages1 = np.zeros(5)
-    stages2 = np.zeros(5)
+    keys = ["sort", "spread", "fft1", "deconv", "clear", "interp", "fft2", "pad"]
+    acc = {k: 0.0 for k in keys}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
-        stages1 += np.array(p1.stage_times())
-        stages2 += np.array(p2.stage_times())
+        st = plan.stage_times()
+        for k in keys:
+            acc[k] += st[k]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    stages1 /= args.steps
-    stages2 /= args.steps
+    stg = {k: v / args.steps for k, v in acc.items()}
 
     rs = 4 if wl.precision == "f32" else 8
-    info = p1.info()
+    info = plan.info()
     # dominant kernel: the spread (type 1 step 1) or the interpolation (type 2 step 3)
-    spread_ms, interp_ms = stages1[1], stages2[1]
     bytes_alg = spread_bytes(wl.M, wl.dim, info["n"], rs)
-    dom_name, dom_ms = ("spread", spread_ms) if spread_ms >= interp_ms else ("interp", interp_ms)
+    dom_name = "spread" if stg["spread"] >= stg["interp"] else "interp"
+    dom_ms = stg[dom_name]
     achieved = bytes_alg / (dom_ms * 1e-3) / 1e9
-    exec1 = stages1[1:].sum()
-    exec2 = stages2[1:].sum()
+    exec1 = stg["clear"] + stg["spread"] + stg["fft1"] + stg["deconv"]
+    exec2 = stg["pad"] + stg["fft2"] + stg["interp"]
     out = {
         "metric": "NU points/sec (type1 & type2, 3D fp32 eps=1e-5, spread+FFT+deconv) and % HBM roofline",
         "value": wl.M / (ms_step * 1e-3),
@@ -131,22 +129,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if wl.precision == "f32" else "f64",
         "data": "synthetic",
-        "config": {"workload": f"{wl.dim}D type1+type2 N={'x'.join(map(str, wl.N))} M={wl.M} "
+        "config": {"workload": f"{wl.dim}D type1+type2 pair N={'x'.join(map(str, wl.N))} M={wl.M} "
                                f"{wl.dist} {wl.precision} eps={wl.eps:g}",
                    "fine_grid": list(info["n"]), "w": info["w"], "bins": list(info["bins"]),
-                   "nsubproblems": p1.info()["nsubproblems"]},
+                   "nsubproblems": info["nsubproblems"]},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes": bytes_alg, "avg_ms": dom_ms},
-        "stages_ms": {
-            "type1": {"sort": stages1[0], "clear": stages1[4], "spread": stages1[1], "fft": stages1[2],
-                      "deconv": stages1[3]},
-            "type2": {"sort": stages2[0], "pad": stages2[3], "fft": stages2[2], "interp": stages2[1]},
-        },
+        "stages_ms": stg,
         "exec_pts_per_s": {"type1": wl.M / (exec1 * 1e-3), "type2": wl.M / (exec2 * 1e-3)},
     }
-    p1.destroy()
-    p2.destroy()
+    plan.destroy()
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_sample, wl.M))
     print(json.dumps(out))

@@ -109,6 +109,15 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
  */
 int nufft_execute(nufft_plan plan, void* c, void* f);
 
+/*
+ * Run the adjoint transform on the same sorted points: type 2 (f -> c) on a type 1 plan,
+ * type 1 (c -> f) on a type 2 plan.  Type 2 is the adjoint of type 1 (cuFINUFFT paper,
+ * Sec. I), and iterative solvers apply both to one point set; the bin-sort of setpts is
+ * reused.  The first call creates the rocFFT plan of the other direction.  Same argument
+ * conventions and errors as nufft_execute.
+ */
+int nufft_execute_adjoint(nufft_plan plan, void* c, void* f);
+
 /* Free everything the plan owns (waits for its stream first).  NULL is accepted. */
 int nufft_destroy(nufft_plan plan);
 
@@ -129,10 +138,12 @@ const char* nufft_last_error(nufft_plan plan);
 int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d);
 
 /*
- * Per-stage times (ms) of the last setpts/execute when opts.timing = 1, in host
- * memory: ms[0] sort (setpts), ms[1] spread or interp, ms[2] FFT, ms[3]
- * correction (deconvolve+truncate or precorrect+pad), ms[4] grid clear.
- * Synchronises the plan's stream.
+ * Per-step times (ms) when opts.timing = 1, written to ms[0..7] in host memory:
+ *   ms[0] sort (last setpts),
+ *   ms[1] spread, ms[2] type 1 FFT, ms[3] deconvolve + truncate, ms[4] grid clear
+ *         (last type 1 execution),
+ *   ms[5] interp, ms[6] type 2 FFT, ms[7] precorrect + pad (last type 2 execution).
+ * A direction never executed reports zeros.  Synchronises the plan's stream.
  */
 int nufft_get_stage_times(nufft_plan plan, double* ms);
 

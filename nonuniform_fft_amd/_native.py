@@ -31,6 +31,7 @@ SIGNATURES = {
                                ctypes.POINTER(_P)]),
     "nufft_setpts": (_I, [_P, _L, _P, _P, _P]),
     "nufft_execute": (_I, [_P, _P, _P]),
+    "nufft_execute_adjoint": (_I, [_P, _P, _P]),
     "nufft_destroy": (_I, [_P]),
     "nufft_strerror": (ctypes.c_char_p, [_I]),
     "nufft_last_error": (ctypes.c_char_p, [_P]),
@@ -217,6 +218,16 @@ class Plan:
         self._check(self._lib.nufft_execute(self._h, cp, fp))
         return f if self.type == 1 else c
 
+    def execute_adjoint(self, c, f):
+        """The adjoint transform on the same points (type 2 for a type 1 plan, and back)."""
+        if self.M < 0:
+            raise NufftError(NUFFT_ERR_BAD_STATE, "setpts first")
+        cd = _complex_dtype(self.prec)
+        cp = self._dev_tensor(c, cd, self.M, "c")
+        fp = self._dev_tensor(f, cd, self.nmodes, "f")
+        self._check(self._lib.nufft_execute_adjoint(self._h, cp, fp))
+        return c if self.type == 1 else f
+
     def spread(self, c, grid):
         cd = _complex_dtype(self.prec)
         self._check(self._lib.nufft_spread(self._h, self._dev_tensor(c, cd, self.M, "c"),
@@ -255,10 +266,12 @@ class Plan:
         return perm, counts, sub
 
     def stage_times(self):
-        """ms of [sort, spread|interp, fft, correction, grid clear] (needs timing=True)."""
-        ms = (ctypes.c_double * 5)()
+        """ms per step (needs timing=True): sort, spread, type-1 FFT, deconvolve, clear,
+        interp, type-2 FFT, precorrect+pad (zeros for a direction not run)."""
+        ms = (ctypes.c_double * 8)()
         self._check(self._lib.nufft_get_stage_times(self._h, ms))
-        return list(ms)
+        keys = ["sort", "spread", "fft1", "deconv", "clear", "interp", "fft2", "pad"]
+        return dict(zip(keys, list(ms)))
 
     def destroy(self):
         if self._h is not None:

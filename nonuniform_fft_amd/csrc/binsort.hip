@@ -16,7 +16,7 @@ namespace nufft {
 namespace {
 
 constexpr int kBlock = 256;                 // threads per workgroup (4 wavefronts)
-constexpr int kItems = 16;                  // keys per thread per sort tile
+constexpr int kItems = 8;                   // keys per thread per sort tile
 constexpr int kTile = kBlock * kItems;      // keys per sort tile
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
@@ -170,30 +170,91 @@ __global__ void __launch_bounds__(kBlock) k_radix_hist(const int32_t* __restrict
     for (int d = threadIdx.x; d < kRadix; d += kBlock) hist[(int64_t)d * ntiles + blockIdx.x] = h[d];
 }
 
+template <typename T, int NP>
+struct Payload {
+    const T* in[3];
+    T* out[3];
+};
+
+// Stable scatter of one radix pass.  Besides (key, original index), the NP coordinate arrays
+// travel with the keys, so the last pass leaves the coordinates in sorted order without a
+// random gather (the first pass reads them in the caller's order, coalesced).
+// The tile is first ranked (ballots within a wavefront, LDS counters across wavefronts) and
+// reordered by digit in LDS; the write-out then stores each digit's run of the tile to
+// consecutive addresses, so global stores are coalesced within runs.
+template <typename T, int NP>
 __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restrict__ keys_in,
                                                            const int32_t* __restrict__ vals_in,
                                                            int32_t* __restrict__ keys_out,
                                                            int32_t* __restrict__ vals_out,
                                                            int64_t M, int shift, int64_t ntiles,
-                                                           const int32_t* __restrict__ offs) {
-    __shared__ int32_t running[kRadix];
+                                                           const int32_t* __restrict__ offs,
+                                                           Payload<T, NP> pl) {
+    __shared__ int32_t gbase[kRadix];          // global start of each digit's run of this tile
+    __shared__ int32_t tbase[kRadix];          // start of each digit's run inside the tile
+    __shared__ int32_t running[kRadix];        // items of each digit placed so far
     __shared__ int32_t wcount[kBlock / 64][kRadix];
+    __shared__ int32_t sk[kTile];
+    __shared__ int32_t sv[kTile];
+    __shared__ T sc[NP > 0 ? NP : 1][kTile];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t base = (int64_t)blockIdx.x * kTile;
+    const int count = (int)min<int64_t>(kTile, M - base);
+
+    // load the tile (coalesced) and build its digit histogram
+    int32_t keys[kItems], vals[kItems];
+    T cvs[kItems][NP > 0 ? NP : 1];
     for (int d = tid; d < kRadix; d += kBlock) {
-        running[d] = offs[(int64_t)d * ntiles + blockIdx.x];
+        running[d] = 0;
 #pragma unroll
         for (int i = 0; i < kBlock / 64; ++i) wcount[i][d] = 0;
     }
     __syncthreads();
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int64_t base = (int64_t)blockIdx.x * kTile;
+#pragma unroll
     for (int r = 0; r < kItems; ++r) {
-        int64_t idx = base + (int64_t)r * kBlock + tid;
-        bool valid = idx < M;
-        int32_t key = valid ? keys_in[idx] : 0;
-        int32_t val = valid ? vals_in[idx] : 0;
-        int digit = (key >> shift) & (kRadix - 1);
-        // lanes of this wavefront holding the same digit
+        const int li = r * kBlock + tid;
+        const bool valid = li < count;
+        keys[r] = valid ? keys_in[base + li] : 0;
+        vals[r] = valid ? vals_in[base + li] : 0;
+#pragma unroll
+        for (int d = 0; d < NP; ++d) cvs[r][d] = valid ? pl.in[d][base + li] : (T)0;
+        if (valid) atomicAdd(&running[(keys[r] >> shift) & (kRadix - 1)], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the tile histogram (one wavefront, 4 digits per lane)
+    if (wv == 0) {
+        int32_t c4[kRadix / 64], s = 0;
+#pragma unroll
+        for (int i = 0; i < kRadix / 64; ++i) {
+            c4[i] = running[lane * (kRadix / 64) + i];
+            s += c4[i];
+        }
+        int32_t inc = s;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            int32_t u = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += u;
+        }
+        int32_t run = inc - s;
+#pragma unroll
+        for (int i = 0; i < kRadix / 64; ++i) {
+            const int d = lane * (kRadix / 64) + i;
+            tbase[d] = run;
+            gbase[d] = offs[(int64_t)d * ntiles + blockIdx.x];
+            run += c4[i];
+        }
+    }
+    __syncthreads();
+    for (int d = tid; d < kRadix; d += kBlock) running[d] = 0;
+    __syncthreads();
+
+    // stable rank: items in tile order (r major, then thread), placed into LDS by digit
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        const bool valid = r * kBlock + tid < count;
+        const int32_t key = keys[r];
+        const int digit = (key >> shift) & (kRadix - 1);
         uint64_t peers = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
@@ -201,15 +262,17 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
             uint64_t m = __ballot(bit);
             peers &= bit ? m : ~m;
         }
-        int rank = __popcll(peers & lt_mask);
-        int leader = peers ? (__ffsll((unsigned long long)peers) - 1) : 64;
+        const int rank = __popcll(peers & lt_mask);
+        const int leader = peers ? (__ffsll((unsigned long long)peers) - 1) : 64;
         if (valid && lane == leader) wcount[wv][digit] = __popcll(peers);
         __syncthreads();
         if (valid) {
-            int32_t pos = running[digit] + rank;
+            int32_t pos = tbase[digit] + running[digit] + rank;
             for (int i = 0; i < wv; ++i) pos += wcount[i][digit];
-            keys_out[pos] = key;
-            vals_out[pos] = val;
+            sk[pos] = key;
+            sv[pos] = vals[r];
+#pragma unroll
+            for (int d = 0; d < NP; ++d) sc[d][pos] = cvs[r][d];
         }
         __syncthreads();
         for (int d = tid; d < kRadix; d += kBlock) {
@@ -222,6 +285,16 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
             running[d] += add;
         }
         __syncthreads();
+    }
+    // write out: position i of the reordered tile goes to gbase[digit] + (i - tbase[digit])
+    for (int i = tid; i < count; i += kBlock) {
+        const int32_t key = sk[i];
+        const int digit = (key >> shift) & (kRadix - 1);
+        const int64_t pos = (int64_t)gbase[digit] + (i - tbase[digit]);
+        keys_out[pos] = key;
+        vals_out[pos] = sv[i];
+#pragma unroll
+        for (int d = 0; d < NP; ++d) pl.out[d][pos] = sc[d][i];
     }
 }
 
@@ -262,19 +335,12 @@ __global__ void k_build_sub(int nbins, int cap, const int32_t* __restrict__ coun
     }
 }
 
-template <typename T>
-__global__ void k_gather(const T* __restrict__ x, const int32_t* __restrict__ perm, int64_t M,
-                         T* __restrict__ xs) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < M) xs[i] = x[perm[i]];
-}
-
 struct SortLayout {
     int64_t ntiles;
-    size_t keysA, valsA, keysB, valsB, hist, hist_scan, scan_tmp, nsp, first, end;
+    size_t keysA, valsA, keysB, valsB, coords, hist, hist_scan, scan_tmp, nsp, first, end;
 };
 
-SortLayout layout(int64_t M, int nbins) {
+SortLayout layout(int64_t M, int nbins, int dim, int prec) {
     SortLayout L{};
     L.ntiles = std::max<int64_t>(1, cdiv(M, kTile));
     size_t off = 0;
@@ -288,6 +354,7 @@ SortLayout layout(int64_t M, int nbins) {
     L.valsA = take(Mm);
     L.keysB = take(Mm);
     L.valsB = take(Mm);
+    L.coords = take(Mm * (size_t)dim * (prec == 0 ? 1 : 2));
     size_t nh = (size_t)kRadix * L.ntiles;
     L.hist = take(nh);
     L.hist_scan = take(nh + 1);
@@ -301,12 +368,12 @@ SortLayout layout(int64_t M, int nbins) {
 
 }  // namespace
 
-size_t sort_scratch_bytes(int64_t M, int nbins) { return layout(M, nbins).end; }
+size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec) { return layout(M, nbins, dim, prec).end; }
 
 hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_t* offsets,
-                       void* scratch, size_t scratch_bytes, int64_t* nsub_dev, int* bad_dev,
-                       hipStream_t st) {
-    SortLayout L = layout(a.M, a.nbins);
+                       void* xs_out, void* scratch, size_t scratch_bytes, int64_t* nsub_dev,
+                       int* bad_dev, hipStream_t st) {
+    SortLayout L = layout(a.M, a.nbins, a.dim, a.prec);
     if (scratch_bytes < L.end) return hipErrorInvalidValue;
     char* base = (char*)scratch;
     int32_t* keysA = (int32_t*)(base + L.keysA);
@@ -332,16 +399,56 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
         if ((e = hipGetLastError()) != hipSuccess) return e;
         int passes = (a.nbits + kRadixBits - 1) / kRadixBits;
         int32_t *ki = keysA, *vi = valsA, *ko = keysB, *vo = valsB;
+        const size_t rs = a.prec == 0 ? 4 : 8;
+        char* ctmp = base + L.coords;
         for (int p = 0; p < passes; ++p) {
             int shift = p * kRadixBits;
             dim3 gt((unsigned)L.ntiles);
             k_radix_hist<<<gt, kBlock, 0, st>>>(ki, M, shift, L.ntiles, hist);
             if ((e = exclusive_scan(hist, hscan, (int64_t)kRadix * L.ntiles, stmp, st)) != hipSuccess)
                 return e;
-            k_radix_scatter<<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan);
+            // coordinates: caller's arrays -> ... -> sorted output; the last pass writes xs_out
+            const bool last = (p == passes - 1);
+            const bool to_tmp = ((passes - 1 - p) % 2) == 1;
+            const void* cin[3];
+            void* cout[3];
+            for (int d = 0; d < 3; ++d) {
+                cin[d] = (p == 0) ? a.x[d] : ((passes - p) % 2 == 1 ? (const void*)(ctmp + (size_t)d * M * rs)
+                                                                     : (const void*)((char*)xs_out + (size_t)d * M * rs));
+                cout[d] = to_tmp ? (void*)(ctmp + (size_t)d * M * rs) : (void*)((char*)xs_out + (size_t)d * M * rs);
+            }
+            (void)last;
+            if (a.prec == 0) {
+                Payload<float, 3> pl{};
+                for (int d = 0; d < a.dim; ++d) { pl.in[d] = (const float*)cin[d]; pl.out[d] = (float*)cout[d]; }
+                if (a.dim == 2) {
+                    Payload<float, 2> p2{};
+                    for (int d = 0; d < 2; ++d) { p2.in[d] = pl.in[d]; p2.out[d] = pl.out[d]; }
+                    k_radix_scatter<float, 2><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan, p2);
+                } else {
+                    k_radix_scatter<float, 3><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan, pl);
+                }
+            } else {
+                Payload<double, 3> pl{};
+                for (int d = 0; d < a.dim; ++d) { pl.in[d] = (const double*)cin[d]; pl.out[d] = (double*)cout[d]; }
+                if (a.dim == 2) {
+                    Payload<double, 2> p2{};
+                    for (int d = 0; d < 2; ++d) { p2.in[d] = pl.in[d]; p2.out[d] = pl.out[d]; }
+                    k_radix_scatter<double, 2><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan, p2);
+                } else {
+                    k_radix_scatter<double, 3><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan, pl);
+                }
+            }
             if ((e = hipGetLastError()) != hipSuccess) return e;
             std::swap(ki, ko);
             std::swap(vi, vo);
+        }
+        if (passes == 0) {
+            // a single bin: the order is unchanged
+            for (int d = 0; d < a.dim; ++d)
+                if ((e = hipMemcpyAsync((char*)xs_out + (size_t)d * M * rs, a.x[d], M * rs, hipMemcpyDeviceToDevice,
+                                        st)) != hipSuccess)
+                    return e;
         }
         if ((e = hipMemcpyAsync(perm, vi, sizeof(int32_t) * M, hipMemcpyDeviceToDevice, st)) !=
             hipSuccess)
@@ -363,26 +470,13 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
 }
 
 // Subproblem list from the scratch of the last launch_sort (bins, cap, counts, offsets as there).
-hipError_t launch_build_subproblems_from(int64_t M, int nbins, int cap, const int32_t* counts,
-                                         const int32_t* offsets, const void* scratch,
-                                         int32_t* sub, hipStream_t st) {
-    SortLayout L = layout(M, nbins);
+hipError_t launch_build_subproblems_from(int64_t M, int nbins, int dim, int prec, int cap,
+                                         const int32_t* counts, const int32_t* offsets,
+                                         const void* scratch, int32_t* sub, hipStream_t st) {
+    SortLayout L = layout(M, nbins, dim, prec);
     const int32_t* first = (const int32_t*)((const char*)scratch + L.first);
     k_build_sub<<<dim3((unsigned)cdiv(nbins, kBlock)), kBlock, 0, st>>>(nbins, cap, counts, offsets,
                                                                        first, sub);
-    return hipGetLastError();
-}
-
-hipError_t launch_gather_coords(int dim, int prec, int64_t M, const void* const* x,
-                                const int32_t* perm, void* xs, hipStream_t st) {
-    if (M <= 0) return hipSuccess;
-    dim3 g((unsigned)cdiv(M, kBlock));
-    for (int i = 0; i < dim; ++i) {
-        if (prec == 0)
-            k_gather<float><<<g, kBlock, 0, st>>>((const float*)x[i], perm, M, (float*)xs + i * M);
-        else
-            k_gather<double><<<g, kBlock, 0, st>>>((const double*)x[i], perm, M, (double*)xs + i * M);
-    }
     return hipGetLastError();
 }
 

@@ -115,10 +115,10 @@ struct nufft_plan_s {
     rocfft_execution_info fft_info = nullptr;
 
     // timing
-    hipEvent_t ev[8] = {};
+    hipEvent_t ev[16] = {};
     bool ev_ok = false;
-    double stage_ms[5] = {0, 0, 0, 0, 0};
-    int stage_recorded = 0;             // bit mask of stages recorded by the last call
+    double stage_ms[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int stage_recorded = 0;             // bit 0: type 1 steps recorded, bit 1: type 2 steps
 };
 
 namespace nufft {
@@ -140,21 +140,19 @@ struct SortArgs {
     int cap;
 };
 // Bytes of scratch the sort needs for M points and the plan's bin count.
-size_t sort_scratch_bytes(int64_t M, int nbins);
+size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec);
 // Runs bin index + radix sort + counts/offsets + subproblem counts.  Writes perm, counts,
-// offsets; writes the number of subproblems into *nsub_dev (device int64) and a nonzero value
-// into *bad_dev when a point is invalid (*bad_dev must be zeroed by the caller).  Then the
-// caller reads back, allocates `sub`, and calls launch_build_subproblems_from and
-// launch_gather_coords.
+// offsets and the coordinates in sorted order (xs_out: dim arrays of M, plan precision);
+// writes the number of subproblems into *nsub_dev (device int64) and a nonzero value into
+// *bad_dev when a point is invalid (*bad_dev must be zeroed by the caller).  Then the caller
+// reads back and calls launch_build_subproblems_from.
 hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_t* offsets,
-                       void* scratch, size_t scratch_bytes, int64_t* nsub_dev, int* bad_dev,
-                       hipStream_t st);
+                       void* xs_out, void* scratch, size_t scratch_bytes, int64_t* nsub_dev,
+                       int* bad_dev, hipStream_t st);
 // (bin, start, len) rows from the per-bin subproblem prefix left in the sort scratch.
-hipError_t launch_build_subproblems_from(int64_t M, int nbins, int cap, const int32_t* counts,
-                                         const int32_t* offsets, const void* scratch,
-                                         int32_t* sub, hipStream_t st);
-hipError_t launch_gather_coords(int dim, int prec, int64_t M, const void* const* x,
-                                const int32_t* perm, void* xs, hipStream_t st);
+hipError_t launch_build_subproblems_from(int64_t M, int nbins, int dim, int prec, int cap,
+                                         const int32_t* counts, const int32_t* offsets,
+                                         const void* scratch, int32_t* sub, hipStream_t st);
 
 // spread.hip / interp.hip / deconv.hip
 struct GeomArgs {

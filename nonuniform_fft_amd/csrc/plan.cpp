@@ -228,6 +228,81 @@ int fft_exec(nufft_plan plan, rocfft_plan fp, void* data) {
     return NUFFT_OK;
 }
 
+// rocFFT plan for one direction (forward for type 1, backward for type 2), in place,
+// unnormalised; the work buffer is shared by both directions and grown when needed.
+int make_fft_plan(nufft_plan plan, int direction) {
+    rocfft_plan& slot = (direction == 1) ? plan->fft_fwd : plan->fft_bwd;
+    if (slot) return NUFFT_OK;
+    std::call_once(g_rocfft_once, [] { g_rocfft_setup = rocfft_setup(); });
+    if (g_rocfft_setup != rocfft_status_success) return fail(plan, NUFFT_ERR_FFT, "rocfft_setup failed");
+    size_t lengths[3] = {(size_t)plan->n[0], (size_t)plan->n[1], (size_t)plan->n[2]};
+    rocfft_precision fprec = plan->prec == 0 ? rocfft_precision_single : rocfft_precision_double;
+    rocfft_transform_type tt = (direction == 1) ? rocfft_transform_type_complex_forward
+                                                : rocfft_transform_type_complex_inverse;
+    rocfft_plan fp = nullptr;
+    if (rocfft_plan_create(&fp, rocfft_placement_inplace, tt, fprec, (size_t)plan->dim, lengths, 1, nullptr) !=
+        rocfft_status_success)
+        return fail(plan, NUFFT_ERR_FFT, "rocfft_plan_create failed");
+    slot = fp;
+    if (!plan->fft_info) {
+        if (rocfft_execution_info_create(&plan->fft_info) != rocfft_status_success)
+            return fail(plan, NUFFT_ERR_FFT, "rocfft_execution_info_create failed");
+        if (rocfft_execution_info_set_stream(plan->fft_info, plan->stream) != rocfft_status_success)
+            return fail(plan, NUFFT_ERR_FFT, "rocfft_execution_info_set_stream failed");
+    }
+    size_t work = 0;
+    if (rocfft_plan_get_work_buffer_size(fp, &work) != rocfft_status_success)
+        return fail(plan, NUFFT_ERR_FFT, "rocfft_plan_get_work_buffer_size failed");
+    if (work > plan->fft_work.bytes) {
+        int rc = dev_alloc(plan, plan->fft_work, work, "FFT work buffer");
+        if (rc != NUFFT_OK) return rc;
+        if (rocfft_execution_info_set_work_buffer(plan->fft_info, plan->fft_work.p, work) != rocfft_status_success)
+            return fail(plan, NUFFT_ERR_FFT, "rocfft_execution_info_set_work_buffer failed");
+    }
+    return NUFFT_OK;
+}
+
+// Timing slots: events [0..4] bracket the type 1 steps (clear, spread, FFT, deconvolve),
+// [8..11] the type 2 steps (pad, FFT, interp), [5..6] the sort.
+enum { EV_T1 = 0, EV_SORT0 = 5, EV_SORT1 = 6, EV_T2 = 8 };
+
+// Type 1 on the plan's points: c (M) -> f (N^d).
+int run_type1(nufft_plan plan, const void* c, void* f) {
+    int rc;
+    if ((rc = make_fft_plan(plan, 1)) != NUFFT_OK) return rc;
+    nufft::GeomArgs g = geom(plan);
+    const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan);
+    record(plan, EV_T1 + 0);
+    NUFFT_HIP(nufft::launch_fill_zero(plan->grid.p, gbytes, plan->stream));
+    record(plan, EV_T1 + 1);
+    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, plan->grid.p, plan->stream));
+    record(plan, EV_T1 + 2);
+    if ((rc = fft_exec(plan, plan->fft_fwd, plan->grid.p)) != NUFFT_OK) return rc;
+    record(plan, EV_T1 + 3);
+    NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, plan->grid.p, f,
+                                       plan->stream));
+    record(plan, EV_T1 + 4);
+    plan->stage_recorded |= 1;
+    return NUFFT_OK;
+}
+
+// Type 2 on the plan's points: f (N^d) -> c (M).
+int run_type2(nufft_plan plan, void* c, const void* f) {
+    int rc;
+    if ((rc = make_fft_plan(plan, 2)) != NUFFT_OK) return rc;
+    nufft::GeomArgs g = geom(plan);
+    record(plan, EV_T2 + 0);
+    NUFFT_HIP(nufft::launch_precorrect_pad(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, f, plan->grid.p,
+                                           plan->stream));
+    record(plan, EV_T2 + 1);
+    if ((rc = fft_exec(plan, plan->fft_bwd, plan->grid.p)) != NUFFT_OK) return rc;
+    record(plan, EV_T2 + 2);
+    NUFFT_HIP(nufft::launch_interp(plan->prec, plan->method, g, plan->grid.p, c, plan->stream));
+    record(plan, EV_T2 + 3);
+    plan->stage_recorded |= 2;
+    return NUFFT_OK;
+}
+
 int check_plan(nufft_plan p) {
     if (!p) return NUFFT_ERR_BAD_ARG;
     return NUFFT_OK;
@@ -383,44 +458,10 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
         }
     }
 
-    // rocFFT plans (forward for type 1, backward for type 2), in place, unnormalised
-    std::call_once(g_rocfft_once, [] { g_rocfft_setup = rocfft_setup(); });
-    if (g_rocfft_setup != rocfft_status_success) {
+    // rocFFT plan of the plan's own direction (the adjoint direction is made on first use)
+    if ((rc = make_fft_plan(plan, type)) != NUFFT_OK) {
         nufft_destroy(plan);
-        return NUFFT_ERR_FFT;
-    }
-    size_t lengths[3] = {(size_t)plan->n[0], (size_t)plan->n[1], (size_t)plan->n[2]};
-    rocfft_precision fprec = plan->prec == 0 ? rocfft_precision_single : rocfft_precision_double;
-    rocfft_transform_type tt = (type == 1) ? rocfft_transform_type_complex_forward
-                                           : rocfft_transform_type_complex_inverse;
-    rocfft_plan fp = nullptr;
-    if (rocfft_plan_create(&fp, rocfft_placement_inplace, tt, fprec, (size_t)dim, lengths, 1, nullptr) !=
-        rocfft_status_success) {
-        nufft_destroy(plan);
-        return NUFFT_ERR_FFT;
-    }
-    if (type == 1) plan->fft_fwd = fp;
-    else plan->fft_bwd = fp;
-    size_t work = 0;
-    if (rocfft_plan_get_work_buffer_size(fp, &work) != rocfft_status_success ||
-        rocfft_execution_info_create(&plan->fft_info) != rocfft_status_success) {
-        nufft_destroy(plan);
-        return NUFFT_ERR_FFT;
-    }
-    if (work > 0) {
-        if ((rc = dev_alloc(plan, plan->fft_work, work, "FFT work buffer")) != NUFFT_OK) {
-            nufft_destroy(plan);
-            return rc;
-        }
-        if (rocfft_execution_info_set_work_buffer(plan->fft_info, plan->fft_work.p, work) !=
-            rocfft_status_success) {
-            nufft_destroy(plan);
-            return NUFFT_ERR_FFT;
-        }
-    }
-    if (rocfft_execution_info_set_stream(plan->fft_info, plan->stream) != rocfft_status_success) {
-        nufft_destroy(plan);
-        return NUFFT_ERR_FFT;
+        return rc;
     }
     if (plan->opts.timing) {
         plan->ev_ok = true;
@@ -443,7 +484,7 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     const size_t rs = real_size(plan);
     const size_t Mm = (size_t)std::max<int64_t>(M, 1);
     int rc;
-    size_t sort_bytes = nufft::sort_scratch_bytes(M, (int)plan->nbins) + 256;
+    size_t sort_bytes = nufft::sort_scratch_bytes(M, (int)plan->nbins, plan->dim, plan->prec) + 256;
     if ((rc = dev_alloc(plan, plan->xs, Mm * plan->dim * rs, "sorted coordinates")) != NUFFT_OK ||
         (rc = dev_alloc(plan, plan->perm, Mm * sizeof(int32_t), "permutation")) != NUFFT_OK ||
         (rc = dev_alloc(plan, plan->counts, (size_t)plan->nbins * sizeof(int32_t), "bin counts")) != NUFFT_OK ||
@@ -455,7 +496,7 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     int64_t* nsub_dev = (int64_t*)tail;
     int* bad_dev = (int*)(tail + 64);
 
-    record(plan, 5);
+    record(plan, EV_SORT0);
     NUFFT_HIP(hipMemsetAsync(bad_dev, 0, sizeof(int), plan->stream));
     nufft::SortArgs a{};
     a.dim = plan->dim;
@@ -472,8 +513,8 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     a.nbits = plan->nbits;
     a.cap = plan->cap;
     NUFFT_HIP(nufft::launch_sort(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p,
-                                 (int32_t*)plan->offsets.p, plan->sort_tmp.p, plan->sort_tmp.bytes - 256,
-                                 nsub_dev, bad_dev, plan->stream));
+                                 (int32_t*)plan->offsets.p, plan->xs.p, plan->sort_tmp.p,
+                                 plan->sort_tmp.bytes - 256, nsub_dev, bad_dev, plan->stream));
     int64_t host_nsub = 0;
     int host_bad = 0;
     NUFFT_HIP(hipMemcpyAsync(&host_nsub, nsub_dev, sizeof(int64_t), hipMemcpyDeviceToHost, plan->stream));
@@ -483,19 +524,17 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     if ((rc = dev_alloc(plan, plan->sub, (size_t)std::max<int64_t>(host_nsub, 1) * 3 * sizeof(int32_t),
                         "subproblem list")) != NUFFT_OK)
         return rc;
-    NUFFT_HIP(nufft::launch_build_subproblems_from(M, (int)plan->nbins, plan->cap,
+    NUFFT_HIP(nufft::launch_build_subproblems_from(M, (int)plan->nbins, plan->dim, plan->prec, plan->cap,
                                                    (const int32_t*)plan->counts.p,
                                                    (const int32_t*)plan->offsets.p, plan->sort_tmp.p,
                                                    (int32_t*)plan->sub.p, plan->stream));
-    NUFFT_HIP(nufft::launch_gather_coords(plan->dim, plan->prec, M, X, (const int32_t*)plan->perm.p,
-                                          plan->xs.p, plan->stream));
-    record(plan, 6);
+    record(plan, EV_SORT1);
     plan->M = M;
     plan->nsub = host_nsub;
     if (plan->opts.timing && plan->ev_ok) {
-        NUFFT_HIP(hipEventSynchronize(plan->ev[6]));
+        NUFFT_HIP(hipEventSynchronize(plan->ev[EV_SORT1]));
         float ms = 0;
-        if (hipEventElapsedTime(&ms, plan->ev[5], plan->ev[6]) == hipSuccess) plan->stage_ms[0] = ms;
+        if (hipEventElapsedTime(&ms, plan->ev[EV_SORT0], plan->ev[EV_SORT1]) == hipSuccess) plan->stage_ms[0] = ms;
     }
     return NUFFT_OK;
 }
@@ -505,55 +544,37 @@ int nufft_execute(nufft_plan plan, void* c, void* f) {
     int rc;
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
     if ((plan->M > 0 && !c) || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
-    nufft::GeomArgs g = geom(plan);
-    const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan);
-    if (plan->type == 1) {
-        record(plan, 0);
-        NUFFT_HIP(nufft::launch_fill_zero(plan->grid.p, gbytes, plan->stream));
-        record(plan, 1);
-        NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, plan->grid.p, plan->stream));
-        record(plan, 2);
-        if ((rc = fft_exec(plan, plan->fft_fwd, plan->grid.p)) != NUFFT_OK) return rc;
-        record(plan, 3);
-        NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p,
-                                           plan->grid.p, f, plan->stream));
-        record(plan, 4);
-    } else {
-        record(plan, 0);
-        record(plan, 1);
-        NUFFT_HIP(nufft::launch_precorrect_pad(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p,
-                                               f, plan->grid.p, plan->stream));
-        record(plan, 2);
-        if ((rc = fft_exec(plan, plan->fft_bwd, plan->grid.p)) != NUFFT_OK) return rc;
-        record(plan, 3);
-        NUFFT_HIP(nufft::launch_interp(plan->prec, plan->method, g, plan->grid.p, c, plan->stream));
-        record(plan, 4);
-    }
-    plan->stage_recorded = 1;
-    return NUFFT_OK;
+    return plan->type == 1 ? run_type1(plan, c, f) : run_type2(plan, c, f);
+}
+
+int nufft_execute_adjoint(nufft_plan plan, void* c, void* f) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    int rc;
+    if ((rc = check_points(plan)) != NUFFT_OK) return rc;
+    if ((plan->M > 0 && !c) || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
+    return plan->type == 1 ? run_type2(plan, c, f) : run_type1(plan, c, f);
 }
 
 int nufft_get_stage_times(nufft_plan plan, double* ms) {
     if (!plan || !ms) return NUFFT_ERR_BAD_ARG;
     if (!plan->opts.timing || !plan->ev_ok) return fail(plan, NUFFT_ERR_BAD_STATE, "timing not enabled");
     NUFFT_HIP(hipStreamSynchronize(plan->stream));
-    if (plan->stage_recorded) {
-        float t[4] = {0, 0, 0, 0};
-        for (int i = 0; i < 4; ++i)
-            if (hipEventElapsedTime(&t[i], plan->ev[i], plan->ev[i + 1]) != hipSuccess) t[i] = 0;
-        if (plan->type == 1) {
-            plan->stage_ms[4] = t[0];
-            plan->stage_ms[1] = t[1];
-            plan->stage_ms[2] = t[2];
-            plan->stage_ms[3] = t[3];
-        } else {
-            plan->stage_ms[4] = 0;
-            plan->stage_ms[3] = t[1];
-            plan->stage_ms[2] = t[2];
-            plan->stage_ms[1] = t[3];
-        }
+    auto span = [&](int a, int b) {
+        float t = 0;
+        return (hipEventElapsedTime(&t, plan->ev[a], plan->ev[b]) == hipSuccess) ? (double)t : 0.0;
+    };
+    if (plan->stage_recorded & 1) {
+        plan->stage_ms[4] = span(EV_T1 + 0, EV_T1 + 1);
+        plan->stage_ms[1] = span(EV_T1 + 1, EV_T1 + 2);
+        plan->stage_ms[2] = span(EV_T1 + 2, EV_T1 + 3);
+        plan->stage_ms[3] = span(EV_T1 + 3, EV_T1 + 4);
     }
-    for (int i = 0; i < 5; ++i) ms[i] = plan->stage_ms[i];
+    if (plan->stage_recorded & 2) {
+        plan->stage_ms[7] = span(EV_T2 + 0, EV_T2 + 1);
+        plan->stage_ms[6] = span(EV_T2 + 1, EV_T2 + 2);
+        plan->stage_ms[5] = span(EV_T2 + 2, EV_T2 + 3);
+    }
+    for (int i = 0; i < 8; ++i) ms[i] = plan->stage_ms[i];
     return NUFFT_OK;
 }
 

@@ -27,17 +27,21 @@ constexpr int kGmBlock = 128;
 // Points staged per round: about 24 KB of LDS for kernel weights, local offsets and strengths.
 template <typename T, int DIM, int W>
 struct SmCfg {
-    static constexpr int kPerPoint = DIM * W * (int)sizeof(T) + 4 * (int)sizeof(int) + 2 * (int)sizeof(T);
+    static constexpr int kWP = (W + 3) & ~3;                      // padded row of T weights (16 B aligned)
+    static constexpr int kWD = (W + 1) & ~1;                      // padded row of fp64 z weights
+    static constexpr int kPerPoint = 2 * kWP * (int)sizeof(T) + (DIM == 3 ? kWD * 8 : 0) + 16 + 2 * (int)sizeof(T);
     static constexpr int kRaw = 24576 / kPerPoint;
     static constexpr int kChunk = kRaw >= 256 ? 256 : (kRaw < 32 ? 32 : (kRaw & ~31));
 };
 
 template <typename T, int DIM, int W>
 struct Stage {
-    static constexpr int CH = SmCfg<T, DIM, W>::kChunk;
-    T ker[CH][DIM][W];
-    int l0[CH][4];
-    T cre[CH], cim[CH];
+    using C = SmCfg<T, DIM, W>;
+    static constexpr int CH = C::kChunk;
+    int4 l0[CH];                                   // local stencil start per dimension
+    cplx<T> cv[CH];                                // strength
+    T kxy[CH][2][C::kWP];                          // x and y weights
+    double kz[DIM == 3 ? CH : 1][C::kWD];          // z weights, widened once
 };
 
 // LDS tile of a padded bin: separate fp64 planes for real and imaginary parts, row pitch pc with
@@ -48,6 +52,28 @@ __host__ __device__ inline int tile_row_pitch(int p1, int w) {
     return pc;
 }
 
+// (s1, s2, s3) of cell index k = s1 + p1 (s2 + p2 s3), advanced by a fixed stride without division.
+struct CellWalk {
+    int s1, s2, s3, d1, d2, d3, p1, p2;
+    __device__ CellWalk(int k, int stride, int p1_, int p2_) : p1(p1_), p2(p2_) {
+        s1 = k % p1; int r = k / p1; s2 = r % p2; s3 = r / p2;
+        d1 = stride % p1; r = stride / p1; d2 = r % p2; d3 = r / p2;
+    }
+    __device__ void next() {
+        s1 += d1; int c = s1 >= p1; s1 -= c ? p1 : 0;
+        s2 += d2 + c; c = s2 >= p2; s2 -= c ? p2 : 0;
+        s3 += d3 + c;
+    }
+};
+
+// Periodic wrap of a padded-tile coordinate onto [0, n).  A padded bin can reach past the grid
+// end by up to m + w cells, which is more than one period on small grids, hence the loops.
+__device__ __forceinline__ int wrap_grid(int v, int n) {
+    while (v >= n) v -= n;
+    while (v < 0) v += n;
+    return v;
+}
+
 template <typename T, int DIM, int W>
 __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c,
                                                             cplx<T>* __restrict__ grid, int p1, int p2,
@@ -55,9 +81,10 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
     using St = Stage<T, DIM, W>;
     constexpr int CH = St::CH;
     constexpr int WW = W * W;
+    constexpr int PPP = kSpreadBlock / WW;          // points per pass of the workgroup
     extern __shared__ __align__(16) unsigned char smem[];
-    const int pp = pc * p2;                 // plane pitch
-    const int PL = pp * p3;                 // padded cells
+    const int pp = pc * p2;                          // plane pitch
+    const int PL = pp * p3;                          // padded cells
     double* tre = (double*)smem;
     double* tim = tre + PL;
     St* st = (St*)(tim + PL);
@@ -78,6 +105,14 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
     const int pd[3] = {p1, p2, p3};
     for (int k = threadIdx.x; k < 2 * PL; k += kSpreadBlock) tre[k] = 0.0;
 
+    // this thread's fixed slot (q1, q2) of the x-y stencil patch
+    const int t = threadIdx.x;
+    const int p_first = t / WW;
+    const int slot = t - p_first * WW;
+    const int q2 = slot / W;
+    const int q1 = slot - q2 * W;
+    const bool active = p_first < PPP;
+
     const T beta = (T)g.beta;
     for (int c0 = 0; c0 < len; c0 += CH) {
         const int np = min(CH, len - c0);
@@ -87,63 +122,68 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
             const int p = threadIdx.x / DIM;
             const int i = threadIdx.x - p * DIM;
             const int64_t j = (int64_t)start + c0 + p;
-            double t = grid_t((double)((const T*)g.xs[i])[j], g.s[i]);
+            double tt = grid_t((double)((const T*)g.xs[i])[j], g.s[i]);
             int l;
-            fold_t(t, g.n[i], l);
-            int l0 = es_weights<T, W>(t, beta, st->ker[p][i]) - origin[i];
-            st->l0[p][i] = min(max(l0, 0), pd[i] - W);
+            fold_t(tt, g.n[i], l);
+            T ker[W];
+            int l0 = es_weights<T, W>(tt, beta, ker) - origin[i];
+            l0 = min(max(l0, 0), pd[i] - W);
+            if (i < 2) {
+#pragma unroll
+                for (int q = 0; q < W; ++q) st->kxy[p][i][q] = ker[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < W; ++q) st->kz[DIM == 3 ? p : 0][q] = (double)ker[q];
+            }
             if (i == 0) {
-                const cplx<T> v = c[g.perm[j]];
-                st->cre[p] = v.re;
-                st->cim[p] = v.im;
+                st->l0[p].x = l0;
+                st->cv[p] = c[g.perm[j]];
+            } else if (i == 1) {
+                st->l0[p].y = l0;
+            } else {
+                st->l0[p].z = l0;
             }
         }
         __syncthreads();
-        // (point, q1, q2) items; 3D loops over q3
-        const int items = np * WW;
-        for (int it = threadIdx.x; it < items; it += kSpreadBlock) {
-            const int p = it / WW;
-            const int r = it - p * WW;
-            const int q2 = r / W;
-            const int q1 = r - q2 * W;
-            const T wxy = st->ker[p][0][q1] * st->ker[p][1][q2];
-            const double vre = (double)(st->cre[p] * wxy);
-            const double vim = (double)(st->cim[p] * wxy);
-            int base = st->l0[p][0] + q1 + (st->l0[p][1] + q2) * pc;
-            if (DIM == 2) {
-                atomicAdd(tre + base, vre);
-                atomicAdd(tim + base, vim);
-            } else {
-                base += st->l0[p][2] * pp;
+        if (active) {
+            for (int p = p_first; p < np; p += PPP) {
+                // read everything this item needs before the first atomic, so the LDS counter
+                // waits only on these reads and the atomics then issue back to back
+                const int4 l0 = st->l0[p];
+                const cplx<T> cv = st->cv[p];
+                double kz[DIM == 3 ? W : 1];
+                if (DIM == 3) {
 #pragma unroll
-                for (int q3 = 0; q3 < W; ++q3) {
-                    const double kz = (double)st->ker[p][DIM - 1][q3];
-                    atomicAdd(tre + base + q3 * pp, vre * kz);
-                    atomicAdd(tim + base + q3 * pp, vim * kz);
+                    for (int q3 = 0; q3 < W; ++q3) kz[q3] = st->kz[DIM == 3 ? p : 0][q3];
+                }
+                const T wxy = st->kxy[p][0][q1] * st->kxy[p][1][q2];
+                const double vre = (double)(cv.re * wxy);
+                const double vim = (double)(cv.im * wxy);
+                const int base = l0.x + q1 + (l0.y + q2) * pc + (DIM == 3 ? l0.z * pp : 0);
+                if (DIM == 2) {
+                    atomicAdd(tre + base, vre);
+                    atomicAdd(tim + base, vim);
+                } else {
+#pragma unroll
+                    for (int q3 = 0; q3 < W; ++q3) {
+                        atomicAdd(tre + base + q3 * pp, vre * kz[q3]);
+                        atomicAdd(tim + base + q3 * pp, vim * kz[q3]);
+                    }
                 }
             }
         }
     }
     __syncthreads();
-    // flush the padded bin with periodic wrap (eq. (15))
+    // flush the padded bin with periodic wrap (eq. (15)); consecutive lanes take consecutive x
     const int P = p1 * p2 * p3;
-    for (int k = threadIdx.x; k < P; k += kSpreadBlock) {
-        const int s1 = k % p1;
-        const int rest = k / p1;
-        const int s2 = rest % p2;
-        const int s3 = rest / p2;
-        const int li = s1 + s2 * pc + s3 * pp;
+    CellWalk cw(threadIdx.x, kSpreadBlock, p1, p2);
+    for (int k = threadIdx.x; k < P; k += kSpreadBlock, cw.next()) {
+        const int li = cw.s1 + cw.s2 * pc + cw.s3 * pp;
         const double re = tre[li], im = tim[li];
         if (re == 0.0 && im == 0.0) continue;
-        int g1 = origin[0] + s1, g2 = origin[1] + s2, g3 = (DIM == 3) ? origin[2] + s3 : 0;
-        while (g1 < 0) g1 += g.n[0];
-        while (g1 >= g.n[0]) g1 -= g.n[0];
-        while (g2 < 0) g2 += g.n[1];
-        while (g2 >= g.n[1]) g2 -= g.n[1];
-        if (DIM == 3) {
-            while (g3 < 0) g3 += g.n[2];
-            while (g3 >= g.n[2]) g3 -= g.n[2];
-        }
+        const int g1 = wrap_grid(origin[0] + cw.s1, g.n[0]);
+        const int g2 = wrap_grid(origin[1] + cw.s2, g.n[1]);
+        const int g3 = (DIM == 3) ? wrap_grid(origin[2] + cw.s3, g.n[2]) : 0;
         const size_t gi = (size_t)g1 + (size_t)g.n[0] * ((size_t)g2 + (size_t)g.n[1] * (size_t)g3);
         unsafeAtomicAdd(&grid[gi].re, (T)re);
         unsafeAtomicAdd(&grid[gi].im, (T)im);

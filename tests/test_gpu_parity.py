@@ -318,3 +318,32 @@ def test_repeated_execute_and_resetpts(nf, orc):
             ref = orc.nufft_type1(inp["X"], c, N, 1e-5)
             assert orc.rel_l2(f.cpu().numpy(), ref) <= 1e-5
     p.destroy()
+
+
+@pytest.mark.parametrize("wl", [Workload("adj", 3, (24, 20, 18), 40_000, 1e-5, "f32", seed=71),
+                                Workload("adj", 2, (64, 48), 20_000, 1e-12, "f64", seed=72)],
+                         ids=["3d_f32", "2d_f64"])
+def test_execute_adjoint_matches_oracle(nf, orc, wl):
+    """A type 1 plan runs type 2 on its sorted points and vice versa (one sort for the pair)."""
+    inp = make_inputs(wl)
+    X = [to_dev(x) for x in inp["X"]]
+    cd = cdtype(wl.precision)
+    ref1 = orc.nufft_type1(inp["X"], inp["c"], wl.N, wl.eps)
+    ref2 = orc.nufft_type2(inp["X"], inp["f"], wl.N, wl.eps)
+    for t in (1, 2):
+        p = nf.Plan(t, wl.N, wl.eps, wl.precision, timing=True)
+        p.setpts(*X)
+        f = torch.empty(tuple(reversed(wl.N)), dtype=cd, device=dev())
+        c = torch.empty(wl.M, dtype=cd, device=dev())
+        if t == 1:
+            p.execute(to_dev(inp["c"]), f)
+            p.execute_adjoint(c, to_dev(inp["f"]))
+        else:
+            p.execute(c, to_dev(inp["f"]))
+            p.execute_adjoint(to_dev(inp["c"]), f)
+        torch.cuda.synchronize()
+        assert orc.rel_l2(f.cpu().numpy(), ref1) <= tol_for(wl.precision)
+        assert orc.rel_l2(c.cpu().numpy(), ref2) <= tol_for(wl.precision)
+        st = p.stage_times()
+        assert st["sort"] > 0 and st["spread"] > 0 and st["interp"] > 0 and st["fft1"] > 0 and st["fft2"] > 0
+        p.destroy()
