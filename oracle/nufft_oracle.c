@@ -1,5 +1,5 @@
 /*
- * Plain serial CPU oracle for the 2D/3D type 1 and type 2 NUFFT (fp64).
+ * Plain CPU oracle for the 2D/3D type 1 and type 2 NUFFT (fp64).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  It shares no source,
@@ -14,7 +14,10 @@
  *
  * Everything is fp64, IEEE round-to-nearest, compiled without FP contraction
  * and without fast-math.  Loops are written in the order the equations state
- * them; nothing is blocked, fused or reordered for speed.  Arrays of complex
+ * them; nothing is blocked, fused or reordered for speed.  The only
+ * parallelism (OpenMP) is over independent outputs of the exact sums and over
+ * point ranges of the sampled type 1 evaluation, whose partial sums are added
+ * in range order; spreading, interpolation and the bin-sort are serial.  Arrays of complex
  * numbers are interleaved (re, im).  Grids are stored with the first index
  * fastest: cell (l1, l2, l3) sits at l1 + n1*(l2 + n2*l3).
  */
@@ -22,6 +25,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* The double nearest pi. */
 static const double PI_D = 3.141592653589793115997963468544185161590576171875;
@@ -246,6 +252,11 @@ int oracle_direct_type1(int d, const int64_t* N, int64_t M, const double* const*
     for (int64_t s = 0; s < count; ++s) {
         int64_t pos = sel ? sel[s] : s;
         if (pos < 0 || pos >= total) return ORACLE_BAD_ARG;
+    }
+    /* each output is one serial sum; outputs are independent (threads over outputs) */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t s = 0; s < count; ++s) {
+        int64_t pos = sel ? sel[s] : s;
         int64_t k1 = mode_of(pos % NN[0], NN[0]);
         int64_t k2 = mode_of((pos / NN[0]) % NN[1], NN[1]);
         int64_t k3 = mode_of(pos / (NN[0] * NN[1]), NN[2]);
@@ -280,6 +291,10 @@ int oracle_direct_type2(int d, const int64_t* N, int64_t M, const double* const*
     for (int64_t s = 0; s < count; ++s) {
         int64_t j = sel ? sel[s] : s;
         if (j < 0 || j >= M) return ORACLE_BAD_ARG;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t s = 0; s < count; ++s) {
+        int64_t j = sel ? sel[s] : s;
         double sre = 0.0, sim = 0.0;
         for (int64_t pos = 0; pos < total; ++pos) {
             int64_t k1 = mode_of(pos % NN[0], NN[0]);
@@ -316,34 +331,70 @@ int oracle_type1_bhat_at(int d, const int64_t* n, int w, double beta, int64_t M,
 {
     if (d < 1 || d > 3 || w < 1 || w > 32 || M < 0 || nk < 0) return ORACLE_BAD_ARG;
     for (int64_t s = 0; s < 2 * nk; ++s) bhat[s] = 0.0;
-    double phi[3][32];
-    int64_t cell[3][32];
-    for (int64_t j = 0; j < M; ++j) {
+    for (int64_t j = 0; j < M; ++j)
         for (int i = 0; i < d; ++i) {
             double t; int64_t l;
             if (grid_coord(X[i][j], n[i], oracle_grid_scale(n[i]), &t, &l) != ORACLE_OK)
                 return ORACLE_BAD_POINT;
-            stencil_1d(t, n[i], w, beta, phi[i], cell[i]);
         }
-        for (int64_t s = 0; s < nk; ++s) {
-            double pre = c[2 * j], pim = c[2 * j + 1];
-            for (int i = 0; i < d; ++i) {
-                int64_t k = kvec[d * s + i];
-                double are = 0.0, aim = 0.0;
-                for (int q = 0; q < w; ++q) {
-                    /* exp(-2 pi i cell k / n), with cell*k reduced mod n exactly first */
-                    int64_t r = pmod(pmod(cell[i][q], n[i]) * pmod(k, n[i]), n[i]);
-                    double ang = -2.0 * PI_D * (double)r / (double)n[i];
-                    are += phi[i][q] * cos(ang);
-                    aim += phi[i][q] * sin(ang);
-                }
-                double nre = pre * are - pim * aim;
-                double nim = pre * aim + pim * are;
-                pre = nre; pim = nim;
-            }
-            bhat[2 * s] += pre;
-            bhat[2 * s + 1] += pim;
+    int nthreads = 1;
+#ifdef _OPENMP
+    nthreads = omp_get_max_threads();
+#endif
+    /* points are split into nthreads contiguous ranges; each range's partial sums are added
+       in range order at the end */
+    double* part = (double*)calloc((size_t)nthreads * 2 * (size_t)(nk > 0 ? nk : 1), sizeof(double));
+    if (!part) return ORACLE_BAD_ARG;
+    /* twiddles exp(-2 pi i r / n_i), r = 0..n_i-1, one table per dimension */
+    double* tw[3] = {NULL, NULL, NULL};
+    for (int i = 0; i < d; ++i) {
+        tw[i] = (double*)malloc(sizeof(double) * 2 * (size_t)n[i]);
+        if (!tw[i]) { free(part); for (int q = 0; q < i; ++q) free(tw[q]); return ORACLE_BAD_ARG; }
+        for (int64_t r = 0; r < n[i]; ++r) {
+            double ang = -2.0 * PI_D * (double)r / (double)n[i];
+            tw[i][2 * r] = cos(ang);
+            tw[i][2 * r + 1] = sin(ang);
         }
     }
+#pragma omp parallel num_threads(nthreads)
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        int64_t j0 = M * tid / nthreads, j1 = M * (tid + 1) / nthreads;
+        double* acc = part + (size_t)tid * 2 * (size_t)nk;
+        double phi[3][32];
+        int64_t cell[3][32];
+        for (int64_t j = j0; j < j1; ++j) {
+            for (int i = 0; i < d; ++i) {
+                double t; int64_t l;
+                grid_coord(X[i][j], n[i], oracle_grid_scale(n[i]), &t, &l);
+                stencil_1d(t, n[i], w, beta, phi[i], cell[i]);
+            }
+            for (int64_t s = 0; s < nk; ++s) {
+                double pre = c[2 * j], pim = c[2 * j + 1];
+                for (int i = 0; i < d; ++i) {
+                    int64_t k = kvec[d * s + i];
+                    double are = 0.0, aim = 0.0;
+                    for (int q = 0; q < w; ++q) {
+                        /* exp(-2 pi i cell k / n), with cell*k reduced mod n exactly first */
+                        int64_t r = pmod(pmod(cell[i][q], n[i]) * pmod(k, n[i]), n[i]);
+                        are += phi[i][q] * tw[i][2 * r];
+                        aim += phi[i][q] * tw[i][2 * r + 1];
+                    }
+                    double nre = pre * are - pim * aim;
+                    double nim = pre * aim + pim * are;
+                    pre = nre; pim = nim;
+                }
+                acc[2 * s] += pre;
+                acc[2 * s + 1] += pim;
+            }
+        }
+    }
+    for (int t = 0; t < nthreads; ++t)
+        for (int64_t s = 0; s < 2 * nk; ++s) bhat[s] += part[(size_t)t * 2 * (size_t)nk + s];
+    free(part);
+    for (int i = 0; i < d; ++i) free(tw[i]);
     return ORACLE_OK;
 }

@@ -33,6 +33,7 @@ import subprocess
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
+import scipy.fft
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nufft_oracle.c")
@@ -47,7 +48,7 @@ def build(force: bool = True) -> str:
     os.makedirs(_LIBDIR, exist_ok=True)
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+        cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
                "-shared", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
@@ -229,12 +230,12 @@ def interp(X, b, w: int, beta: float) -> np.ndarray:
 
 def fft_forward(b: np.ndarray) -> np.ndarray:
     """Eq. (9): bhat_k = sum_l b_l exp(-2 pi i l.k/n), unnormalised (library FFT)."""
-    return np.fft.fftn(b)
+    return scipy.fft.fftn(b, workers=-1)
 
 
 def fft_backward(bhat: np.ndarray) -> np.ndarray:
     """Eq. (12): b_l = sum_k bhat_k exp(+2 pi i l.k/n), unnormalised (library FFT)."""
-    return np.fft.ifftn(bhat, norm="forward")
+    return scipy.fft.ifftn(bhat, norm="forward", workers=-1)
 
 
 def _index_grids(N, n):
