@@ -35,20 +35,58 @@ def spread_bytes(M, dim, n, real_size):
 
 
 def cpu_baseline(wl, inp, sample_M):
-    """Time the CPU oracle (serial C + numpy FFT) on the first `sample_M` points of the workload:
-    type 1 (spread, FFT, correct) then type 2 (pad, inverse FFT, interpolate)."""
-    import numpy as np
-
+    """Time the CPU oracle on the first `sample_M` points of the workload, single-threaded:
+    bin-sort, type 1 (spread, FFT, correct), then type 2 (pad, inverse FFT, interpolate)."""
     import oracle.oracle as orc
+    orc._load()
+    orc.FFT_WORKERS = 1
     X = [x[:sample_M] for x in inp["X"]]
     c = inp["c"][:sample_M]
+    prm = orc.Params(wl.N, wl.eps)
     t0 = time.perf_counter()
+    orc.binsort(X, prm.n, (16, 16, 8)[:wl.dim])
     orc.nufft_type1(X, c, wl.N, wl.eps)
     orc.nufft_type2(X, inp["f"], wl.N, wl.eps)
     dt = time.perf_counter() - t0
     return {"value": sample_M / dt, "unit": "NU points/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {sample_M} of {wl.M} points of the same workload, type 1 + type 2 "
-                      f"(serial C spread/interp, single-threaded numpy FFT), {dt:.1f} s"}
+            "sample": f"first {sample_M} of {wl.M} points of the same workload through the serial "
+                      f"oracle (bin-sort, type 1, type 2; C spread/interp, one-thread scipy FFT), "
+                      f"{dt:.1f} s"}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None when
+    the kernel's source has changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*hbm_traffic*.md")):
+        for line in open(path):
+            parts = line.split()
+            if len(parts) < 2 or parts[0] != "traffic":
+                continue
+            kv = dict(p.split("=", 1) for p in parts[1:] if "=" in p)
+            if kv.get("kernel") != kernel:
+                continue
+            src = os.path.join(ROOT, kv["source"])
+            if not os.path.exists(src):
+                return None
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("sha256"):
+                return None
+            return float(kv["bytes"])
+    return None
+
+
+def probe_copy(nbytes):
+    """A plain device-to-device copy of known size, for calibrating the HBM byte counters."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    a.fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe_copy_bytes": nbytes, "copies": 3}))
 
 
 def main():
@@ -57,10 +95,15 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="3d_n128_m16m_f32_e5")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 20,
+    ap.add_argument("--cpu-sample", type=int, default=1 << 21,
                     help="points of the workload timed on the CPU oracle (0 = skip)")
     ap.add_argument("--method", type=int, default=0)
+    ap.add_argument("--probe-copy", type=int, default=0,
+                    help="only run a plain copy of this many bytes (counter calibration)")
     args = ap.parse_args()
+    if args.probe_copy:
+        probe_copy(args.probe_copy)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -134,7 +177,8 @@ def main():
                    "fine_grid": list(info["n"]), "w": info["w"], "bins": list(info["bins"]),
                    "nsubproblems": info["nsubproblems"]},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(dom_name) if args.workload == "3d_n128_m16m_f32_e5" else None,
                      "algorithmic_bytes": bytes_alg, "avg_ms": dom_ms},
         "stages_ms": stg,
         "exec_pts_per_s": {"type1": wl.M / (exec1 * 1e-3), "type2": wl.M / (exec2 * 1e-3)},

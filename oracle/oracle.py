@@ -228,14 +228,18 @@ def interp(X, b, w: int, beta: float) -> np.ndarray:
     return c
 
 
+# Threads the library FFT may use (-1 = all host cores).  The CPU-baseline timing sets 1.
+FFT_WORKERS = -1
+
+
 def fft_forward(b: np.ndarray) -> np.ndarray:
     """Eq. (9): bhat_k = sum_l b_l exp(-2 pi i l.k/n), unnormalised (library FFT)."""
-    return scipy.fft.fftn(b, workers=-1)
+    return scipy.fft.fftn(b, workers=FFT_WORKERS)
 
 
 def fft_backward(bhat: np.ndarray) -> np.ndarray:
     """Eq. (12): b_l = sum_k bhat_k exp(+2 pi i l.k/n), unnormalised (library FFT)."""
-    return scipy.fft.ifftn(bhat, norm="forward", workers=-1)
+    return scipy.fft.ifftn(bhat, norm="forward", workers=FFT_WORKERS)
 
 
 def _index_grids(N, n):
