@@ -45,6 +45,19 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
         bidx[i] = l / a.m[i];
     }
     int key = bidx[0] + a.nb[0] * (bidx[1] + a.nb[1] * bidx[2]);
+    if (DIM == 3 && a.colw > 0) {
+        // column of the kernel support inside the bin's padded tile (see SortArgs::colw)
+        int lo[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            double t = grid_t((double)((const T*)a.x[i])[j], a.s[i]);
+            int l = 0;
+            fold_t(t, a.n[i], l);
+            lo[i] = (int)ceil(__dsub_rn(t, 0.5 * (double)a.colw)) - (bidx[i] * a.m[i] - a.colw / 2);
+            lo[i] = min(max(lo[i], 0), a.m[i]);
+        }
+        key = key * a.ncol + lo[1] * (a.m[0] + 1) + lo[0];
+    }
     if (!ok) {
         key = 0;
         atomicOr(bad, 1);
@@ -303,13 +316,13 @@ __global__ void k_iota(int32_t* __restrict__ v, int64_t M) {
     if (j < M) v[j] = (int32_t)j;
 }
 
-// offsets[b] = first sorted position whose bin is >= b (offsets[nbins] = M).
-__global__ void k_bin_offsets(const int32_t* __restrict__ skeys, int64_t M, int nbins,
+// offsets[b] = first sorted position whose bin is >= b (offsets[nbins] = M); key = bin * ncol + column.
+__global__ void k_bin_offsets(const int32_t* __restrict__ skeys, int64_t M, int nbins, int ncol,
                               int32_t* __restrict__ offsets) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i > M) return;
-    int lo = (i == 0) ? 0 : skeys[i - 1] + 1;
-    int hi = (i == M) ? nbins : skeys[i];
+    int lo = (i == 0) ? 0 : skeys[i - 1] / ncol + 1;
+    int hi = (i == M) ? nbins : skeys[i] / ncol;
     for (int b = lo; b <= hi; ++b) offsets[b] = (int32_t)i;
 }
 
@@ -453,7 +466,7 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
         if ((e = hipMemcpyAsync(perm, vi, sizeof(int32_t) * M, hipMemcpyDeviceToDevice, st)) !=
             hipSuccess)
             return e;
-        k_bin_offsets<<<dim3((unsigned)cdiv(M + 1, kBlock)), kBlock, 0, st>>>(ki, M, a.nbins, offsets);
+        k_bin_offsets<<<dim3((unsigned)cdiv(M + 1, kBlock)), kBlock, 0, st>>>(ki, M, a.nbins, a.ncol, offsets);
     } else {
         if ((e = hipMemsetAsync(offsets, 0, sizeof(int32_t) * (a.nbins + 1), st)) != hipSuccess)
             return e;

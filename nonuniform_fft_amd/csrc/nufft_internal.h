@@ -42,7 +42,8 @@ __device__ __forceinline__ bool fold_t(double& t, int n, int& l) {
 // ES kernel weights (cuFINUFFT paper eq. (5), rescaled as in eq. (8)) of a point with folded
 // scaled coordinate t along one dimension: the support is the W cells starting at
 // l0 = ceil(t - W/2); weight q has argument z = (l0 + q - t) * 2/W.  The offset l0 - t is
-// formed in fp64 and the rest in the plan precision T.
+// formed in fp64 and the rest in the plan precision T (fp32 uses the hardware exp2-based exponential,
+// whose relative error ~1e-6 at the smallest weights is far below the fp32 output tolerance).
 template <typename T, int W>
 __device__ __forceinline__ int es_weights(double t, T beta, T* phi) {
     double l0d = ceil(__dsub_rn(t, 0.5 * (double)W));
@@ -52,7 +53,10 @@ __device__ __forceinline__ int es_weights(double t, T beta, T* phi) {
     for (int q = 0; q < W; ++q) {
         T z = (delta + (T)q) * scale;
         T zz = z * z;
-        phi[q] = (zz <= (T)1) ? exp(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
+        if constexpr (sizeof(T) == 4)
+            phi[q] = (zz <= 1.0f) ? __expf(beta * (sqrtf(1.0f - zz) - 1.0f)) : 0.0f;
+        else
+            phi[q] = (zz <= (T)1) ? exp(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
     }
     return (int)l0d;
 }
@@ -87,7 +91,9 @@ struct nufft_plan_s {
     int nb[3] = {1, 1, 1};
     int64_t nbins = 0;
     int cap = 0;
-    int nbits = 0;                      // bits of the largest bin index
+    int nbits = 0;                      // bits of the largest sort key
+    int colw = 0;                       // column order inside bins (see SortArgs)
+    int ncol = 1;
 
     size_t bytes_in_use = 0;
     std::string last_error;
@@ -138,6 +144,9 @@ struct SortArgs {
     int nbins;
     int nbits;
     int cap;
+    int colw;      // > 0: order points inside a bin by the x-y column of their kernel support
+                   //       (3D; colw = kernel width), 0: by original index only
+    int ncol;      // columns per bin, (m1 + 1)(m2 + 1) when colw > 0, else 1
 };
 // Bytes of scratch the sort needs for M points and the plan's bin count.
 size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec);
@@ -170,8 +179,9 @@ struct GeomArgs {
     int64_t nsub;
 };
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// columns: the points of each bin are in column order (3D), so the column-run kernel may run.
 hipError_t launch_spread(int prec, int method, const GeomArgs& g, const void* c, void* grid,
-                         hipStream_t st);
+                         hipStream_t st, bool columns);
 hipError_t launch_interp(int prec, int method, const GeomArgs& g, const void* grid, void* c,
                          hipStream_t st);
 size_t interp_tile_bytes(int prec, int dim, int w, const int* m);
@@ -182,5 +192,9 @@ hipError_t launch_precorrect_pad(int prec, int dim, const int64_t* N, const int6
 // Largest LDS tile (bytes) the SM spreading kernel may use.
 size_t spread_lds_limit();
 size_t spread_tile_bytes(int prec, int dim, int w, const int* m);
+// LDS bytes of the 3D column-run spreading kernel for bins m (0 if it cannot run: m3 > 8).
+size_t spread_col_lds_bytes(int prec, int w, const int* m);
+// Whether 3D spreading with this kernel width uses the column-run kernel (needs the column order).
+bool spread_uses_columns(int dim, int w);
 
 }  // namespace nufft

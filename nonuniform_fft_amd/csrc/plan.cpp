@@ -185,7 +185,11 @@ void default_bins(nufft_plan p, int* m) {
     } else {
         for (auto& c : c3) {
             int mm[3] = {c[0], c[1], c[2]};
-            if (nufft::spread_tile_bytes(p->prec, 3, p->w, mm) <= nufft::spread_lds_limit()) {
+            const bool col = nufft::spread_uses_columns(3, p->w) && p->method == NUFFT_METHOD_SM;
+            const size_t need = col ? nufft::spread_col_lds_bytes(p->prec, p->w, mm)
+                                    : nufft::spread_tile_bytes(p->prec, 3, p->w, mm);
+            if (need > 0 && need <= nufft::spread_lds_limit() &&
+                nufft::spread_tile_bytes(p->prec, 3, p->w, mm) <= nufft::spread_lds_limit()) {
                 m[0] = c[0];
                 m[1] = c[1];
                 m[2] = c[2];
@@ -275,7 +279,7 @@ int run_type1(nufft_plan plan, const void* c, void* f) {
     record(plan, EV_T1 + 0);
     NUFFT_HIP(nufft::launch_fill_zero(plan->grid.p, gbytes, plan->stream));
     record(plan, EV_T1 + 1);
-    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, plan->grid.p, plan->stream));
+    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, plan->grid.p, plan->stream, plan->colw > 0));
     record(plan, EV_T1 + 2);
     if ((rc = fft_exec(plan, plan->fft_fwd, plan->grid.p)) != NUFFT_OK) return rc;
     record(plan, EV_T1 + 3);
@@ -416,7 +420,17 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
         return NUFFT_ERR_BAD_ARG;
     }
     plan->nbins = (int64_t)plan->nb[0] * plan->nb[1] * plan->nb[2];
-    plan->nbits = bit_length(plan->nbins - 1);
+    // 3D spreading by column runs needs the points of a bin ordered by support column
+    plan->colw = 0;
+    plan->ncol = 1;
+    if (plan->method == NUFFT_METHOD_SM && nufft::spread_uses_columns(dim, w) && plan->m[2] <= 8) {
+        const int64_t ncol = (int64_t)(plan->m[0] + 1) * (plan->m[1] + 1);
+        if (plan->nbins * ncol < (int64_t(1) << 31)) {
+            plan->colw = w;
+            plan->ncol = (int)ncol;
+        }
+    }
+    plan->nbits = bit_length(plan->nbins * plan->ncol - 1);
     int64_t vol = (int64_t)plan->m[0] * plan->m[1] * plan->m[2];
     plan->cap = plan->opts.subproblem_cap > 0 ? plan->opts.subproblem_cap
                                               : (int)std::max<int64_t>(1024, 2 * vol);
@@ -512,6 +526,8 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     a.nbins = (int)plan->nbins;
     a.nbits = plan->nbits;
     a.cap = plan->cap;
+    a.colw = plan->colw;
+    a.ncol = plan->ncol;
     NUFFT_HIP(nufft::launch_sort(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p,
                                  (int32_t*)plan->offsets.p, plan->xs.p, plan->sort_tmp.p,
                                  plan->sort_tmp.bytes - 256, nsub_dev, bad_dev, plan->stream));
@@ -584,7 +600,7 @@ int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d) {
         int64_t v[20] = {plan->type, plan->dim, plan->prec, plan->w, plan->n[0], plan->n[1], plan->n[2],
                          plan->N[0], plan->N[1], plan->N[2], plan->m[0], plan->m[1], plan->m[2],
                          plan->nbins, plan->M >= 0 ? plan->nsub : 0, plan->M, plan->cap, plan->method,
-                         0, 0};
+                         plan->colw, 0};
         std::memcpy(info_i, v, sizeof(v));
     }
     if (info_d) {
@@ -601,7 +617,7 @@ int nufft_spread(nufft_plan plan, const void* c, void* grid) {
     if (!grid || (plan->M > 0 && !c)) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
     nufft::GeomArgs g = geom(plan);
     NUFFT_HIP(nufft::launch_fill_zero(grid, (size_t)grid_cells(plan) * 2 * real_size(plan), plan->stream));
-    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, grid, plan->stream));
+    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, grid, plan->stream, plan->colw > 0));
     return NUFFT_OK;
 }
 

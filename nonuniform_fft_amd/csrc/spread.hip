@@ -190,6 +190,257 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// 3D column-run spreading.
+//
+// The points of a bin arrive ordered by the x-y column of their kernel support (setpts orders
+// them so).  A wavefront walks a slice of the subproblem's points; its lanes own the w x w
+// (q1, q2) slots of a support column and keep the whole z-line of that column (8 + w cells)
+// in registers.  Consecutive points of the same column -- about m3 * density of them -- are
+// accumulated in registers and the line is added to the LDS padded bin only when the column
+// changes, so the LDS atomics per point drop from 2 w^3 to about 2 w^2 (8 + w) / run length.
+// Per-point weights are staged per wavefront (no workgroup barrier inside the loop); the z
+// weights are stored already placed at the point's z offset so the register updates use
+// fixed indices.
+// ------------------------------------------------------------------------------------------
+constexpr int kColBlock = 1024;
+constexpr int kColWaves = kColBlock / 64;
+
+template <typename T, int W>
+struct ColCfg {
+    static constexpr int kZ = 8 + W;                        // register z-line: bins have m3 <= 8
+    static constexpr int kSlotWaves = (W * W + 63) / 64;    // wavefronts sharing one slice
+    static constexpr int kPiece = (sizeof(T) == 4) ? 20 : 6;  // points staged per round (3 lanes each)
+    static constexpr int kWP = (W + 3) & ~3;
+};
+
+template <typename T, int W>
+struct ColStage {
+    using C = ColCfg<T, W>;
+    T kx[C::kPiece][C::kWP];
+    T ky[C::kPiece][C::kWP];
+    T kzp[C::kPiece][C::kZ];      // z weights at their local z (zero elsewhere)
+    cplx<T> cv[C::kPiece];
+    int l0[C::kPiece][4];
+};
+
+template <typename T, int W>
+__device__ __forceinline__ void col_flush(double* tre, double* tim, const T (&are)[ColCfg<T, W>::kZ],
+                                          const T (&aim)[ColCfg<T, W>::kZ], int base, int pp, int p3) {
+#pragma unroll
+    for (int z = 0; z < ColCfg<T, W>::kZ; ++z) {
+        if (z < p3) {
+            atomicAdd(tre + base + z * pp, (double)are[z]);
+            atomicAdd(tim + base + z * pp, (double)aim[z]);
+        }
+    }
+}
+
+template <typename T, int W>
+__global__ void __launch_bounds__(kColBlock) k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
+                                                          cplx<T>* __restrict__ grid, int p1, int p2, int p3,
+                                                          int pc) {
+    using C = ColCfg<T, W>;
+    using St = ColStage<T, W>;
+    constexpr int Z = C::kZ;
+    constexpr int SW = C::kSlotWaves;
+    constexpr int SLICES = kColWaves / SW;
+    constexpr int PIECE = C::kPiece;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int pp = pc * p2;
+    const int PL = pp * p3;
+    double* tre = (double*)smem;
+    double* tim = tre + PL;
+    St* stages = (St*)(tim + PL);
+
+    const int sid = blockIdx.x;
+    const int bin = g.sub[3 * sid + 0];
+    const int start = g.sub[3 * sid + 1];
+    const int len = g.sub[3 * sid + 2];
+    int origin[3];
+    {
+        int b0 = bin % g.nb[0];
+        int b1 = (bin / g.nb[0]) % g.nb[1];
+        int b2 = bin / (g.nb[0] * g.nb[1]);
+        origin[0] = b0 * g.m[0] - W / 2;
+        origin[1] = b1 * g.m[1] - W / 2;
+        origin[2] = b2 * g.m[2] - W / 2;
+    }
+    const int pd[3] = {p1, p2, p3};
+    for (int k = threadIdx.x; k < 2 * PL; k += kColBlock) tre[k] = 0.0;
+    __syncthreads();
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int slice = wave / SW, sub_wave = wave - slice * SW;
+    St* ws = stages + wave;
+    const int slot = sub_wave * 64 + lane;
+    const bool valid = (slot < W * W) && (slice < SLICES);
+    const int q2 = valid ? slot / W : 0;
+    const int q1 = valid ? slot - q2 * W : 0;
+    const int per = (len + SLICES - 1) / SLICES;
+    const int a = (slice < SLICES) ? min(len, slice * per) : len;
+    const int b = (slice < SLICES) ? min(len, a + per) : len;
+
+    T are[Z], aim[Z];
+#pragma unroll
+    for (int z = 0; z < Z; ++z) {
+        are[z] = (T)0;
+        aim[z] = (T)0;
+    }
+    int cur_x = -1, cur_y = -1, base = 0;
+    const T beta = (T)g.beta;
+    // staging lane (point sp, dimension si); the raw coordinate and strength of the next piece
+    // are loaded into registers while the current piece is processed
+    const int sp = lane / 3, si = lane - (lane / 3) * 3;
+    T xr = (T)0;
+    cplx<T> cr;
+    cr.re = (T)0;
+    cr.im = (T)0;
+    if (lane < min(PIECE, b - a) * 3) {
+        const int64_t j = (int64_t)start + a + sp;
+        xr = ((const T*)g.xs[si])[j];
+        if (si == 0) cr = c[g.perm[j]];
+    }
+    for (int p0 = a; p0 < b; p0 += PIECE) {
+        const int np = min(PIECE, b - p0);
+        if (lane < np * 3) {
+            double tt = grid_t((double)xr, g.s[si]);
+            int l;
+            fold_t(tt, g.n[si], l);
+            T ker[W];
+            int l0 = es_weights<T, W>(tt, beta, ker) - origin[si];
+            l0 = min(max(l0, 0), pd[si] - W);
+            if (si == 0) {
+#pragma unroll
+                for (int q = 0; q < W; ++q) ws->kx[sp][q] = ker[q];
+                ws->cv[sp] = cr;
+            } else if (si == 1) {
+#pragma unroll
+                for (int q = 0; q < W; ++q) ws->ky[sp][q] = ker[q];
+            } else {
+#pragma unroll
+                for (int z = 0; z < Z; ++z) ws->kzp[sp][z] = (T)0;
+#pragma unroll
+                for (int q = 0; q < W; ++q) ws->kzp[sp][l0 + q] = ker[q];
+            }
+            ws->l0[sp][si] = l0;
+        }
+        {
+            const int pn = p0 + PIECE;
+            if (lane < min(PIECE, b - pn) * 3) {
+                const int64_t j = (int64_t)start + pn + sp;
+                xr = ((const T*)g.xs[si])[j];
+                if (si == 0) cr = c[g.perm[j]];
+            }
+        }
+        // the staged piece is written and read by this wavefront only
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int p = 0; p < np; ++p) {
+            int lxv = 0, lyv = 0;
+            if (valid) {
+                lxv = ws->l0[p][0];
+                lyv = ws->l0[p][1];
+            }
+            const int lx = __builtin_amdgcn_readfirstlane(lxv);
+            const int ly = __builtin_amdgcn_readfirstlane(lyv);
+            if (lx != cur_x || ly != cur_y) {
+                if (cur_x >= 0 && valid) col_flush<T, W>(tre, tim, are, aim, base, pp, p3);
+#pragma unroll
+                for (int z = 0; z < Z; ++z) {
+                    are[z] = (T)0;
+                    aim[z] = (T)0;
+                }
+                cur_x = lx;
+                cur_y = ly;
+                base = lx + q1 + (ly + q2) * pc;
+            }
+            if (valid) {
+                const cplx<T> cv = ws->cv[p];
+                const T wxy = ws->kx[p][q1] * ws->ky[p][q2];
+                const T vre = cv.re * wxy, vim = cv.im * wxy;
+#pragma unroll
+                for (int z = 0; z < Z; ++z) {
+                    const T kz = ws->kzp[p][z];
+                    are[z] += vre * kz;
+                    aim[z] += vim * kz;
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (cur_x >= 0 && valid) col_flush<T, W>(tre, tim, are, aim, base, pp, p3);
+    __syncthreads();
+    // add the padded bin to the fine grid with periodic wrap (eq. (15))
+    const int P = p1 * p2 * p3;
+    CellWalk cw(threadIdx.x, kColBlock, p1, p2);
+    for (int k = threadIdx.x; k < P; k += kColBlock, cw.next()) {
+        const int li = cw.s1 + cw.s2 * pc + cw.s3 * pp;
+        const double re = tre[li], im = tim[li];
+        if (re == 0.0 && im == 0.0) continue;
+        const int g1 = wrap_grid(origin[0] + cw.s1, g.n[0]);
+        const int g2 = wrap_grid(origin[1] + cw.s2, g.n[1]);
+        const int g3 = wrap_grid(origin[2] + cw.s3, g.n[2]);
+        const size_t gi = (size_t)g1 + (size_t)g.n[0] * ((size_t)g2 + (size_t)g.n[1] * (size_t)g3);
+        unsafeAtomicAdd(&grid[gi].re, (T)re);
+        unsafeAtomicAdd(&grid[gi].im, (T)im);
+    }
+}
+
+template <typename T, int W>
+size_t col_stage_bytes() { return sizeof(ColStage<T, W>) * kColWaves; }
+
+size_t col_stage_bytes_rt(int prec, int w) {
+    switch (w) {
+#define NUFFT_CASE(WW) case WW: return prec == 0 ? col_stage_bytes<float, WW>() : col_stage_bytes<double, WW>();
+        NUFFT_CASE(5) NUFFT_CASE(6) NUFFT_CASE(7) NUFFT_CASE(8) NUFFT_CASE(9) NUFFT_CASE(10)
+        NUFFT_CASE(11) NUFFT_CASE(12)
+#undef NUFFT_CASE
+        default: return 0;
+    }
+}
+
+// Row pitch of the column kernel's tile: the bank-spreading pitch when it fits, else p1.
+int col_row_pitch(int prec, int w, const int* m) {
+    const int p1 = m[0] + w, p2 = m[1] + w, p3 = m[2] + w;
+    const int pc = tile_row_pitch(p1, w);
+    if ((size_t)pc * p2 * p3 * 16 + col_stage_bytes_rt(prec, w) <= 160 * 1024) return pc;
+    return p1;
+}
+
+template <typename T, int W>
+hipError_t spread_col_w(const GeomArgs& g, const void* c, void* grid, hipStream_t st) {
+    if (g.M <= 0 || g.nsub <= 0) return hipSuccess;
+    const int p1 = g.m[0] + W, p2 = g.m[1] + W, p3 = g.m[2] + W;
+    if (g.m[2] > 8) return hipErrorInvalidConfiguration;
+    const int pc = col_row_pitch(sizeof(T) == 4 ? 0 : 1, W, g.m);
+    const size_t lds = (size_t)pc * p2 * p3 * 2 * sizeof(double) + col_stage_bytes<T, W>();
+    if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_spread_col<T, W>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    k_spread_col<T, W><<<dim3((unsigned)g.nsub), kColBlock, lds, st>>>(g, (const cplx<T>*)c, (cplx<T>*)grid,
+                                                                       p1, p2, p3, pc);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t spread_col(const GeomArgs& g, const void* c, void* grid, hipStream_t st) {
+    switch (g.w) {
+#define NUFFT_CASE(WW) case WW: return spread_col_w<T, WW>(g, c, grid, st);
+        NUFFT_CASE(5) NUFFT_CASE(6) NUFFT_CASE(7) NUFFT_CASE(8) NUFFT_CASE(9) NUFFT_CASE(10)
+        NUFFT_CASE(11) NUFFT_CASE(12)
+#undef NUFFT_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T, int DIM, int W>
 __global__ void __launch_bounds__(kGmBlock) k_spread_gm(GeomArgs g, const cplx<T>* __restrict__ c,
                                                         cplx<T>* __restrict__ grid) {
@@ -313,8 +564,18 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
     return hipGetLastError();
 }
 
+bool spread_uses_columns(int dim, int w) { return dim == 3 && w >= 5 && w <= 12; }
+
+size_t spread_col_lds_bytes(int prec, int w, const int* m) {
+    if (!spread_uses_columns(3, w) || m[2] > 8) return 0;
+    const int pc = col_row_pitch(prec, w, m);
+    return (size_t)pc * (m[1] + w) * (m[2] + w) * 2 * sizeof(double) + col_stage_bytes_rt(prec, w);
+}
+
 hipError_t launch_spread(int prec, int method, const GeomArgs& g, const void* c, void* grid,
-                         hipStream_t st) {
+                         hipStream_t st, bool columns) {
+    if (columns && method != NUFFT_METHOD_GM_SORT)
+        return prec == 0 ? spread_col<float>(g, c, grid, st) : spread_col<double>(g, c, grid, st);
     if (prec == 0) return g.dim == 2 ? spread_dim<float, 2>(method, g, c, grid, st)
                                      : spread_dim<float, 3>(method, g, c, grid, st);
     return g.dim == 2 ? spread_dim<double, 2>(method, g, c, grid, st)

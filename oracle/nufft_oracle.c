@@ -174,11 +174,15 @@ int oracle_interp(int d, const int64_t* n, int w, double beta, int64_t M,
  * The fine grid is cut into bins of m1 x m2 (x m3) cells, ordered with the x
  * index fastest.  Point j lies in the bin holding its cell l_i = floor(t_i).
  * Outputs: bin[j]; counts[b] = number of points in bin b; perm = the points
- * listed bin by bin, in increasing original index inside each bin (a stable
- * counting sort: the list is read out in bin order).
+ * listed bin by bin (a stable counting sort: the list is read out in bin
+ * order).  Inside a bin the order is the original index, or, when w_col > 0
+ * (3D only), the x-y column of the point's kernel support first: the column of
+ * a point is (l0_2 - o_2) (m1 + 1) + (l0_1 - o_1), where l0_i = ceil(t_i - w/2)
+ * starts the support and o_i = b_i m_i - floor(w/2) is its bin's padded origin,
+ * then the original index.
  */
 int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const double* const* X,
-                   int64_t* bin, int64_t* counts, int64_t* perm)
+                   int w_col, int64_t* bin, int64_t* counts, int64_t* perm)
 {
     if (d < 1 || d > 3 || M < 0) return ORACLE_BAD_ARG;
     int64_t nb[3] = {1, 1, 1};
@@ -186,24 +190,34 @@ int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const d
         if (n[i] < 1 || m[i] < 1) return ORACLE_BAD_ARG;
         nb[i] = (n[i] + m[i] - 1) / m[i];
     }
+    int use_col = (w_col > 0 && d == 3);
+    int64_t ncol = use_col ? (m[0] + 1) * (m[1] + 1) : 1;
     int64_t nbins = nb[0] * nb[1] * nb[2];
+    int64_t nkeys = nbins * ncol;
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    int64_t* next = (int64_t*)calloc((size_t)(nkeys > 0 ? nkeys : 1), sizeof(int64_t));
+    if (!key || !next) { free(key); free(next); return ORACLE_BAD_ARG; }
     for (int64_t b = 0; b < nbins; ++b) counts[b] = 0;
     for (int64_t j = 0; j < M; ++j) {
-        int64_t bi[3] = {0, 0, 0};
+        int64_t bi[3] = {0, 0, 0}, lo[3] = {0, 0, 0};
         for (int i = 0; i < d; ++i) {
             double t; int64_t l;
-            if (grid_coord(X[i][j], n[i], oracle_grid_scale(n[i]), &t, &l) != ORACLE_OK)
+            if (grid_coord(X[i][j], n[i], oracle_grid_scale(n[i]), &t, &l) != ORACLE_OK) {
+                free(key); free(next);
                 return ORACLE_BAD_POINT;
+            }
             bi[i] = l / m[i];
+            if (use_col) lo[i] = (int64_t)ceil(t - 0.5 * (double)w_col) - (bi[i] * m[i] - w_col / 2);
         }
         bin[j] = bi[0] + nb[0] * (bi[1] + nb[1] * bi[2]);
         counts[bin[j]] += 1;
+        key[j] = use_col ? bin[j] * ncol + (lo[1] * (m[0] + 1) + lo[0]) : bin[j];
+        next[key[j]] += 1;
     }
-    int64_t* next = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nbins > 0 ? nbins : 1));
-    if (!next) return ORACLE_BAD_ARG;
     int64_t run = 0;
-    for (int64_t b = 0; b < nbins; ++b) { next[b] = run; run += counts[b]; }
-    for (int64_t j = 0; j < M; ++j) perm[next[bin[j]]++] = j;
+    for (int64_t k = 0; k < nkeys; ++k) { int64_t c = next[k]; next[k] = run; run += c; }
+    for (int64_t j = 0; j < M; ++j) perm[next[key[j]]++] = j;
+    free(key);
     free(next);
     return ORACLE_OK;
 }
