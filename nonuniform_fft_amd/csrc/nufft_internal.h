@@ -42,8 +42,9 @@ __device__ __forceinline__ bool fold_t(double& t, int n, int& l) {
 // ES kernel weights (cuFINUFFT paper eq. (5), rescaled as in eq. (8)) of a point with folded
 // scaled coordinate t along one dimension: the support is the W cells starting at
 // l0 = ceil(t - W/2); weight q has argument z = (l0 + q - t) * 2/W.  The offset l0 - t is
-// formed in fp64 and the rest in the plan precision T (fp32 uses the hardware exp2-based exponential,
-// whose relative error ~1e-6 at the smallest weights is far below the fp32 output tolerance).
+// formed in fp64 and the rest in the plan precision T (fp32 uses the hardware square root and
+// exp2-based exponential, whose relative errors -- about 1e-7, and 1e-6 at the smallest weights --
+// are far below the fp32 output tolerance).
 template <typename T, int W>
 __device__ __forceinline__ int es_weights(double t, T beta, T* phi) {
     double l0d = ceil(__dsub_rn(t, 0.5 * (double)W));
@@ -54,7 +55,7 @@ __device__ __forceinline__ int es_weights(double t, T beta, T* phi) {
         T z = (delta + (T)q) * scale;
         T zz = z * z;
         if constexpr (sizeof(T) == 4)
-            phi[q] = (zz <= 1.0f) ? __expf(beta * (sqrtf(1.0f - zz) - 1.0f)) : 0.0f;
+            phi[q] = (zz <= 1.0f) ? __expf(beta * (__builtin_amdgcn_sqrtf(1.0f - zz) - 1.0f)) : 0.0f;
         else
             phi[q] = (zz <= (T)1) ? exp(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
     }

@@ -183,17 +183,20 @@ void default_bins(nufft_plan p, int* m) {
             }
         }
     } else {
-        for (auto& c : c3) {
-            int mm[3] = {c[0], c[1], c[2]};
-            const bool col = nufft::spread_uses_columns(3, p->w) && p->method == NUFFT_METHOD_SM;
-            const size_t need = col ? nufft::spread_col_lds_bytes(p->prec, p->w, mm)
-                                    : nufft::spread_tile_bytes(p->prec, 3, p->w, mm);
-            if (need > 0 && need <= nufft::spread_lds_limit() &&
-                nufft::spread_tile_bytes(p->prec, 3, p->w, mm) <= nufft::spread_lds_limit()) {
-                m[0] = c[0];
-                m[1] = c[1];
-                m[2] = c[2];
-                return;
+        // the column-run kernel first (it needs m3 = 8), then the plain SM tile
+        const bool col = nufft::spread_uses_columns(3, p->w) && p->method == NUFFT_METHOD_SM;
+        for (int pass = col ? 0 : 1; pass < 2; ++pass) {
+            for (auto& c : c3) {
+                int mm[3] = {c[0], c[1], c[2]};
+                const size_t need = (pass == 0) ? nufft::spread_col_lds_bytes(p->prec, p->w, mm)
+                                                : nufft::spread_tile_bytes(p->prec, 3, p->w, mm);
+                if (need > 0 && need <= nufft::spread_lds_limit() &&
+                    nufft::spread_tile_bytes(p->prec, 3, p->w, mm) <= nufft::spread_lds_limit()) {
+                    m[0] = c[0];
+                    m[1] = c[1];
+                    m[2] = c[2];
+                    return;
+                }
             }
         }
     }
@@ -423,7 +426,9 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
     // 3D spreading by column runs needs the points of a bin ordered by support column
     plan->colw = 0;
     plan->ncol = 1;
-    if (plan->method == NUFFT_METHOD_SM && nufft::spread_uses_columns(dim, w) && plan->m[2] <= 8) {
+    const size_t col_lds = nufft::spread_col_lds_bytes(plan->prec, w, plan->m);
+    if (plan->method == NUFFT_METHOD_SM && nufft::spread_uses_columns(dim, w) && plan->m[2] == 8 &&
+        col_lds > 0 && col_lds <= nufft::spread_lds_limit()) {
         const int64_t ncol = (int64_t)(plan->m[0] + 1) * (plan->m[1] + 1);
         if (plan->nbins * ncol < (int64_t(1) << 31)) {
             plan->colw = w;

@@ -208,7 +208,7 @@ constexpr int kColWaves = kColBlock / 64;
 
 template <typename T, int W>
 struct ColCfg {
-    static constexpr int kZ = 8 + W;                        // register z-line: bins have m3 <= 8
+    static constexpr int kZ = 8 + W;                        // register z-line: bins have m3 = 8
     static constexpr int kSlotWaves = (W * W + 63) / 64;    // wavefronts sharing one slice
     static constexpr int kPiece = (sizeof(T) == 4) ? 20 : 6;  // points staged per round (3 lanes each)
     static constexpr int kWP = (W + 3) & ~3;
@@ -224,15 +224,14 @@ struct ColStage {
     int l0[C::kPiece][4];
 };
 
+// The column kernel runs with m3 = 8, so the register z-line spans the padded tile exactly.
 template <typename T, int W>
 __device__ __forceinline__ void col_flush(double* tre, double* tim, const T (&are)[ColCfg<T, W>::kZ],
-                                          const T (&aim)[ColCfg<T, W>::kZ], int base, int pp, int p3) {
+                                          const T (&aim)[ColCfg<T, W>::kZ], int base, int pp) {
 #pragma unroll
     for (int z = 0; z < ColCfg<T, W>::kZ; ++z) {
-        if (z < p3) {
-            atomicAdd(tre + base + z * pp, (double)are[z]);
-            atomicAdd(tim + base + z * pp, (double)aim[z]);
-        }
+        atomicAdd(tre + base + z * pp, (double)are[z]);
+        atomicAdd(tim + base + z * pp, (double)aim[z]);
     }
 }
 
@@ -346,7 +345,7 @@ __global__ void __launch_bounds__(kColBlock) k_spread_col(GeomArgs g, const cplx
             const int lx = __builtin_amdgcn_readfirstlane(lxv);
             const int ly = __builtin_amdgcn_readfirstlane(lyv);
             if (lx != cur_x || ly != cur_y) {
-                if (cur_x >= 0 && valid) col_flush<T, W>(tre, tim, are, aim, base, pp, p3);
+                if (cur_x >= 0 && valid) col_flush<T, W>(tre, tim, are, aim, base, pp);
 #pragma unroll
                 for (int z = 0; z < Z; ++z) {
                     are[z] = (T)0;
@@ -371,7 +370,7 @@ __global__ void __launch_bounds__(kColBlock) k_spread_col(GeomArgs g, const cplx
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
-    if (cur_x >= 0 && valid) col_flush<T, W>(tre, tim, are, aim, base, pp, p3);
+    if (cur_x >= 0 && valid) col_flush<T, W>(tre, tim, are, aim, base, pp);
     __syncthreads();
     // add the padded bin to the fine grid with periodic wrap (eq. (15))
     const int P = p1 * p2 * p3;
@@ -414,7 +413,7 @@ template <typename T, int W>
 hipError_t spread_col_w(const GeomArgs& g, const void* c, void* grid, hipStream_t st) {
     if (g.M <= 0 || g.nsub <= 0) return hipSuccess;
     const int p1 = g.m[0] + W, p2 = g.m[1] + W, p3 = g.m[2] + W;
-    if (g.m[2] > 8) return hipErrorInvalidConfiguration;
+    if (g.m[2] != 8) return hipErrorInvalidConfiguration;
     const int pc = col_row_pitch(sizeof(T) == 4 ? 0 : 1, W, g.m);
     const size_t lds = (size_t)pc * p2 * p3 * 2 * sizeof(double) + col_stage_bytes<T, W>();
     if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
@@ -567,7 +566,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 bool spread_uses_columns(int dim, int w) { return dim == 3 && w >= 5 && w <= 12; }
 
 size_t spread_col_lds_bytes(int prec, int w, const int* m) {
-    if (!spread_uses_columns(3, w) || m[2] > 8) return 0;
+    if (!spread_uses_columns(3, w) || m[2] != 8) return 0;
     const int pc = col_row_pitch(prec, w, m);
     return (size_t)pc * (m[1] + w) * (m[2] + w) * 2 * sizeof(double) + col_stage_bytes_rt(prec, w);
 }
