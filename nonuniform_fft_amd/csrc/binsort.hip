@@ -192,9 +192,11 @@ struct Payload {
 // Stable scatter of one radix pass.  Besides (key, original index), the NP coordinate arrays
 // travel with the keys, so the last pass leaves the coordinates in sorted order without a
 // random gather (the first pass reads them in the caller's order, coalesced).
-// The tile is first ranked (ballots within a wavefront, LDS counters across wavefronts) and
-// reordered by digit in LDS; the write-out then stores each digit's run of the tile to
-// consecutive addresses, so global stores are coalesced within runs.
+//
+// Each wavefront ranks its own contiguous chunk of the tile (kItems rounds of 64 keys) with
+// ballots and wavefront-private digit counters, so ranking needs no workgroup barrier; the
+// per-digit counts of the four chunks are then combined into tile offsets, the tile is
+// reordered by digit in LDS, and each digit's run is written to consecutive addresses.
 template <typename T, int NP>
 __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restrict__ keys_in,
                                                            const int32_t* __restrict__ vals_in,
@@ -203,10 +205,12 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
                                                            int64_t M, int shift, int64_t ntiles,
                                                            const int32_t* __restrict__ offs,
                                                            Payload<T, NP> pl) {
-    __shared__ int32_t gbase[kRadix];          // global start of each digit's run of this tile
-    __shared__ int32_t tbase[kRadix];          // start of each digit's run inside the tile
-    __shared__ int32_t running[kRadix];        // items of each digit placed so far
-    __shared__ int32_t wcount[kBlock / 64][kRadix];
+    constexpr int kWaves = kBlock / 64;
+    constexpr int kChunk = kItems * 64;                  // keys per wavefront
+    __shared__ int32_t cnt[kWaves][kRadix];             // per-wavefront digit counts, then offsets
+    __shared__ int32_t gbase[kRadix];                   // global start of each digit's run of this tile
+    __shared__ int32_t tbase[kRadix];                   // start of each digit's run inside the tile
+    __shared__ int32_t wsum[kWaves];
     __shared__ int32_t sk[kTile];
     __shared__ int32_t sv[kTile];
     __shared__ T sc[NP > 0 ? NP : 1][kTile];
@@ -214,91 +218,82 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
     const int64_t base = (int64_t)blockIdx.x * kTile;
     const int count = (int)min<int64_t>(kTile, M - base);
 
-    // load the tile (coalesced) and build its digit histogram
+    // load this wavefront's chunk (coalesced per round)
     int32_t keys[kItems], vals[kItems];
     T cvs[kItems][NP > 0 ? NP : 1];
-    for (int d = tid; d < kRadix; d += kBlock) {
-        running[d] = 0;
-#pragma unroll
-        for (int i = 0; i < kBlock / 64; ++i) wcount[i][d] = 0;
-    }
-    __syncthreads();
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
-        const int li = r * kBlock + tid;
+        const int li = wv * kChunk + r * 64 + lane;
         const bool valid = li < count;
         keys[r] = valid ? keys_in[base + li] : 0;
         vals[r] = valid ? vals_in[base + li] : 0;
 #pragma unroll
         for (int d = 0; d < NP; ++d) cvs[r][d] = valid ? pl.in[d][base + li] : (T)0;
-        if (valid) atomicAdd(&running[(keys[r] >> shift) & (kRadix - 1)], 1);
     }
-    __syncthreads();
-    // exclusive scan of the tile histogram (one wavefront, 4 digits per lane)
-    if (wv == 0) {
-        int32_t c4[kRadix / 64], s = 0;
-#pragma unroll
-        for (int i = 0; i < kRadix / 64; ++i) {
-            c4[i] = running[lane * (kRadix / 64) + i];
-            s += c4[i];
-        }
-        int32_t inc = s;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            int32_t u = __shfl_up(inc, off, 64);
-            if (lane >= off) inc += u;
-        }
-        int32_t run = inc - s;
-#pragma unroll
-        for (int i = 0; i < kRadix / 64; ++i) {
-            const int d = lane * (kRadix / 64) + i;
-            tbase[d] = run;
-            gbase[d] = offs[(int64_t)d * ntiles + blockIdx.x];
-            run += c4[i];
-        }
-    }
-    __syncthreads();
-    for (int d = tid; d < kRadix; d += kBlock) running[d] = 0;
-    __syncthreads();
+    for (int d = lane; d < kRadix; d += 64) cnt[wv][d] = 0;
 
-    // stable rank: items in tile order (r major, then thread), placed into LDS by digit
+    // rank inside the wavefront's chunk: rounds in order, lanes in order
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int32_t rank[kItems];
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
-        const bool valid = r * kBlock + tid < count;
-        const int32_t key = keys[r];
-        const int digit = (key >> shift) & (kRadix - 1);
+        const bool valid = wv * kChunk + r * 64 + lane < count;
+        const int digit = (keys[r] >> shift) & (kRadix - 1);
         uint64_t peers = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
-            bool bit = (digit >> b) & 1;
-            uint64_t m = __ballot(bit);
+            const bool bit = (digit >> b) & 1;
+            const uint64_t m = __ballot(bit);
             peers &= bit ? m : ~m;
         }
-        const int rank = __popcll(peers & lt_mask);
+        const int32_t before = valid ? cnt[wv][digit] : 0;
+        rank[r] = before + __popcll(peers & lt_mask);
         const int leader = peers ? (__ffsll((unsigned long long)peers) - 1) : 64;
-        if (valid && lane == leader) wcount[wv][digit] = __popcll(peers);
+        // the counter read above and this update are ordered within the wavefront
+        if (valid && lane == leader) cnt[wv][digit] = before + __popcll(peers);
+    }
+    __syncthreads();
+
+    // tile offsets: digit-major exclusive scan of the tile counts, then per-wavefront offsets
+    {
+        const int d = tid;                                // kBlock == kRadix
+        int32_t c[kWaves], tot = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            c[i] = cnt[i][d];
+            tot += c[i];
+        }
+        int32_t inc = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t u = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += u;
+        }
+        if (lane == 63) wsum[wv] = inc;
         __syncthreads();
-        if (valid) {
-            int32_t pos = tbase[digit] + running[digit] + rank;
-            for (int i = 0; i < wv; ++i) pos += wcount[i][digit];
-            sk[pos] = key;
+        int32_t run = inc - tot;
+        for (int i = 0; i < wv; ++i) run += wsum[i];
+        tbase[d] = run;
+        gbase[d] = offs[(int64_t)d * ntiles + blockIdx.x];
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            cnt[i][d] = run;
+            run += c[i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        if (wv * kChunk + r * 64 + lane < count) {
+            const int digit = (keys[r] >> shift) & (kRadix - 1);
+            const int pos = cnt[wv][digit] + rank[r];
+            sk[pos] = keys[r];
             sv[pos] = vals[r];
 #pragma unroll
             for (int d = 0; d < NP; ++d) sc[d][pos] = cvs[r][d];
         }
-        __syncthreads();
-        for (int d = tid; d < kRadix; d += kBlock) {
-            int32_t add = 0;
-#pragma unroll
-            for (int i = 0; i < kBlock / 64; ++i) {
-                add += wcount[i][d];
-                wcount[i][d] = 0;
-            }
-            running[d] += add;
-        }
-        __syncthreads();
     }
+    __syncthreads();
     // write out: position i of the reordered tile goes to gbase[digit] + (i - tbase[digit])
     for (int i = tid; i < count; i += kBlock) {
         const int32_t key = sk[i];
