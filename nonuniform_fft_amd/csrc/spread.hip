@@ -203,11 +203,14 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
 // weights are stored already placed at the point's z offset so the register updates use
 // fixed indices.
 // ------------------------------------------------------------------------------------------
-constexpr int kColBlock = 1024;
-constexpr int kColWaves = kColBlock / 64;
+// fp64 z-lines need twice the registers: 8 wavefronts per workgroup keep them resident
+template <typename T>
+constexpr int kColBlock = (sizeof(T) == 4) ? 1024 : 512;
 
 template <typename T, int W>
 struct ColCfg {
+    static constexpr int kBlock = kColBlock<T>;
+    static constexpr int kWaves = kBlock / 64;
     static constexpr int kZ = 8 + W;                        // register z-line: bins have m3 = 8
     static constexpr int kSlotWaves = (W * W + 63) / 64;    // wavefronts sharing one slice
     static constexpr int kPiece = (sizeof(T) == 4) ? 20 : 6;  // points staged per round (3 lanes each)
@@ -236,15 +239,16 @@ __device__ __forceinline__ void col_flush(double* tre, double* tim, const T (&ar
 }
 
 template <typename T, int W>
-__global__ void __launch_bounds__(kColBlock) k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
+__global__ void __launch_bounds__(kColBlock<T>) k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
                                                           cplx<T>* __restrict__ grid, int p1, int p2, int p3,
                                                           int pc) {
     using C = ColCfg<T, W>;
     using St = ColStage<T, W>;
     constexpr int Z = C::kZ;
     constexpr int SW = C::kSlotWaves;
-    constexpr int SLICES = kColWaves / SW;
+    constexpr int SLICES = C::kWaves / SW;
     constexpr int PIECE = C::kPiece;
+    constexpr int BLOCK = C::kBlock;
     extern __shared__ __align__(16) unsigned char smem[];
     const int pp = pc * p2;
     const int PL = pp * p3;
@@ -266,7 +270,7 @@ __global__ void __launch_bounds__(kColBlock) k_spread_col(GeomArgs g, const cplx
         origin[2] = b2 * g.m[2] - W / 2;
     }
     const int pd[3] = {p1, p2, p3};
-    for (int k = threadIdx.x; k < 2 * PL; k += kColBlock) tre[k] = 0.0;
+    for (int k = threadIdx.x; k < 2 * PL; k += BLOCK) tre[k] = 0.0;
     __syncthreads();
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -374,8 +378,8 @@ __global__ void __launch_bounds__(kColBlock) k_spread_col(GeomArgs g, const cplx
     __syncthreads();
     // add the padded bin to the fine grid with periodic wrap (eq. (15))
     const int P = p1 * p2 * p3;
-    CellWalk cw(threadIdx.x, kColBlock, p1, p2);
-    for (int k = threadIdx.x; k < P; k += kColBlock, cw.next()) {
+    CellWalk cw(threadIdx.x, BLOCK, p1, p2);
+    for (int k = threadIdx.x; k < P; k += BLOCK, cw.next()) {
         const int li = cw.s1 + cw.s2 * pc + cw.s3 * pp;
         const double re = tre[li], im = tim[li];
         if (re == 0.0 && im == 0.0) continue;
@@ -389,7 +393,7 @@ __global__ void __launch_bounds__(kColBlock) k_spread_col(GeomArgs g, const cplx
 }
 
 template <typename T, int W>
-size_t col_stage_bytes() { return sizeof(ColStage<T, W>) * kColWaves; }
+size_t col_stage_bytes() { return sizeof(ColStage<T, W>) * ColCfg<T, W>::kWaves; }
 
 size_t col_stage_bytes_rt(int prec, int w) {
     switch (w) {
@@ -424,8 +428,8 @@ hipError_t spread_col_w(const GeomArgs& g, const void* c, void* grid, hipStream_
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_spread_col<T, W><<<dim3((unsigned)g.nsub), kColBlock, lds, st>>>(g, (const cplx<T>*)c, (cplx<T>*)grid,
-                                                                       p1, p2, p3, pc);
+    k_spread_col<T, W><<<dim3((unsigned)g.nsub), ColCfg<T, W>::kBlock, lds, st>>>(
+        g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2, p3, pc);
     return hipGetLastError();
 }
 
