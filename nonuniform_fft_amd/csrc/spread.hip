@@ -196,63 +196,76 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
 // The points of a bin arrive ordered by the x-y column of their kernel support (setpts orders
 // them so).  A wavefront walks a slice of the subproblem's points; its lanes own the w x w
 // (q1, q2) slots of a support column and keep the whole z-line of that column (8 + w cells)
-// in registers.  Consecutive points of the same column -- about m3 * density of them -- are
-// accumulated in registers and the line is added to the LDS padded bin only when the column
-// changes, so the LDS atomics per point drop from 2 w^3 to about 2 w^2 (8 + w) / run length.
-// Per-point weights are staged per wavefront (no workgroup barrier inside the loop); the z
-// weights are stored already placed at the point's z offset so the register updates use
-// fixed indices.
+// in fp64 registers.  Consecutive points of the same column -- about m3 * density of them --
+// are accumulated in registers and the line is added to the LDS padded bin only when the
+// column changes, so the LDS atomics per point drop from 2 w^3 to about 2 w^2 (8 + w) / run
+// length.  All lanes of a wavefront work on the same point, so the point's z offset inside
+// the line is wave-uniform: a scalar branch picks the w registers it updates, and each point
+// costs 2 w FMAs per lane.  The LDS bin is stored z-fastest in separate real and imaginary
+// planes (cell = (x + y p1) pz + z, pz odd) so a line is flushed with fixed offsets and the
+// lanes of a flush fall on distinct bank pairs.  Per-point weights are staged per
+// wavefront (no workgroup barrier inside the loop).
 // ------------------------------------------------------------------------------------------
-// fp64 z-lines need twice the registers: 8 wavefronts per workgroup keep them resident
-template <typename T>
-constexpr int kColBlock = (sizeof(T) == 4) ? 1024 : 512;
+// wide fp64 z-lines need more registers per lane: 8 wavefronts per workgroup
+template <typename T, int W>
+constexpr int kColBlock = (sizeof(T) == 4 && W <= 6) ? 1024 : (sizeof(T) == 4 && W <= 8) ? 768 : 512;
 
 template <typename T, int W>
 struct ColCfg {
-    static constexpr int kBlock = kColBlock<T>;
+    static constexpr int kZ = 8 + W;                        // z extent of the padded bin (m3 = 8)
+    static constexpr int kPZ = kZ | 1;                      // odd z pitch of the LDS bin
+    static constexpr int kBlock = kColBlock<T, W>;
     static constexpr int kWaves = kBlock / 64;
-    static constexpr int kZ = 8 + W;                        // register z-line: bins have m3 = 8
     static constexpr int kSlotWaves = (W * W + 63) / 64;    // wavefronts sharing one slice
-    static constexpr int kPiece = (sizeof(T) == 4) ? 20 : 6;  // points staged per round (3 lanes each)
-    static constexpr int kWP = (W + 3) & ~3;
+    static constexpr int kPiece = (sizeof(T) == 4) ? 21 : 6;  // points staged per round (3 lanes each)
+    static constexpr int kWZ = (W + 1) & ~1;                // z weights padded to 16-byte pairs
 };
 
 template <typename T, int W>
 struct ColStage {
     using C = ColCfg<T, W>;
-    T kx[C::kPiece][C::kWP];
-    T ky[C::kPiece][C::kWP];
-    T kzp[C::kPiece][C::kZ];      // z weights at their local z (zero elsewhere)
+    double kz[C::kPiece][C::kWZ];
     cplx<T> cv[C::kPiece];
-    int l0[C::kPiece][4];
+    T kx[C::kPiece][W];
+    T ky[C::kPiece][W];
 };
 
-// The column kernel runs with m3 = 8, so the register z-line spans the padded tile exactly.
-template <typename T, int W>
-__device__ __forceinline__ void col_flush(double* tre, double* tim, const T (&are)[ColCfg<T, W>::kZ],
-                                          const T (&aim)[ColCfg<T, W>::kZ], int base, int pp) {
+// A copy of a wave-uniform value that the optimizer cannot see through.
+__device__ __forceinline__ int uniform_copy(int v) {
+    int r;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
+    return r;
+}
+
+// Clears a register in place (a plain assignment of 0 lets the allocator rotate the whole
+// register line through copies at the loop head).
+__device__ __forceinline__ void zero_in_place(double& v) { asm volatile("v_mov_b64 %0, 0" : "+v"(v)); }
+
+// Adds the point's w z-weights times v into the register line at the wave-uniform offset Z0.
+template <int W, int Z, int Z0>
+__device__ __forceinline__ void col_acc(double (&are)[Z], double (&aim)[Z], const double (&kz)[W],
+                                        double vre, double vim) {
 #pragma unroll
-    for (int z = 0; z < ColCfg<T, W>::kZ; ++z) {
-        atomicAdd(tre + base + z * pp, (double)are[z]);
-        atomicAdd(tim + base + z * pp, (double)aim[z]);
+    for (int q = 0; q < W; ++q) {
+        are[Z0 + q] = fma(vre, kz[q], are[Z0 + q]);
+        aim[Z0 + q] = fma(vim, kz[q], aim[Z0 + q]);
     }
 }
 
 template <typename T, int W>
-__global__ void __launch_bounds__(kColBlock<T>) k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
-                                                          cplx<T>* __restrict__ grid, int p1, int p2, int p3,
-                                                          int pc) {
+__global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
+                                                                     cplx<T>* __restrict__ grid, int p1, int p2) {
     using C = ColCfg<T, W>;
     using St = ColStage<T, W>;
     constexpr int Z = C::kZ;
+    constexpr int PZ = C::kPZ;
     constexpr int SW = C::kSlotWaves;
     constexpr int SLICES = C::kWaves / SW;
     constexpr int PIECE = C::kPiece;
     constexpr int BLOCK = C::kBlock;
     extern __shared__ __align__(16) unsigned char smem[];
-    const int pp = pc * p2;
-    const int PL = pp * p3;
-    double* tre = (double*)smem;
+    const int PL = p1 * p2 * PZ;
+    double* tre = (double*)smem;             // real and imaginary planes, cell (x + y p1) pz + z
     double* tim = tre + PL;
     St* stages = (St*)(tim + PL);
 
@@ -269,14 +282,16 @@ __global__ void __launch_bounds__(kColBlock<T>) k_spread_col(GeomArgs g, const c
         origin[1] = b1 * g.m[1] - W / 2;
         origin[2] = b2 * g.m[2] - W / 2;
     }
-    const int pd[3] = {p1, p2, p3};
+    const int pd[3] = {p1, p2, Z};
     for (int k = threadIdx.x; k < 2 * PL; k += BLOCK) tre[k] = 0.0;
     __syncthreads();
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wavefront index is uniform: say so, so the slice bounds and the point loop stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int slice = wave / SW, sub_wave = wave - slice * SW;
     St* ws = stages + wave;
     const int slot = sub_wave * 64 + lane;
+    // lanes past the w x w slots run along (slot 0's weights) but never flush
     const bool valid = (slot < W * W) && (slice < SLICES);
     const int q2 = valid ? slot / W : 0;
     const int q1 = valid ? slot - q2 * W : 0;
@@ -284,13 +299,13 @@ __global__ void __launch_bounds__(kColBlock<T>) k_spread_col(GeomArgs g, const c
     const int a = (slice < SLICES) ? min(len, slice * per) : len;
     const int b = (slice < SLICES) ? min(len, a + per) : len;
 
-    T are[Z], aim[Z];
+    double are[Z], aim[Z];
 #pragma unroll
     for (int z = 0; z < Z; ++z) {
-        are[z] = (T)0;
-        aim[z] = (T)0;
+        are[z] = 0.0;
+        aim[z] = 0.0;
     }
-    int cur_x = -1, cur_y = -1, base = 0;
+    int cur = -1, cell = 0;
     const T beta = (T)g.beta;
     // staging lane (point sp, dimension si); the raw coordinate and strength of the next piece
     // are loaded into registers while the current piece is processed
@@ -306,12 +321,13 @@ __global__ void __launch_bounds__(kColBlock<T>) k_spread_col(GeomArgs g, const c
     }
     for (int p0 = a; p0 < b; p0 += PIECE) {
         const int np = min(PIECE, b - p0);
+        int l0 = 0;
         if (lane < np * 3) {
             double tt = grid_t((double)xr, g.s[si]);
             int l;
             fold_t(tt, g.n[si], l);
             T ker[W];
-            int l0 = es_weights<T, W>(tt, beta, ker) - origin[si];
+            l0 = es_weights<T, W>(tt, beta, ker) - origin[si];
             l0 = min(max(l0, 0), pd[si] - W);
             if (si == 0) {
 #pragma unroll
@@ -322,12 +338,13 @@ __global__ void __launch_bounds__(kColBlock<T>) k_spread_col(GeomArgs g, const c
                 for (int q = 0; q < W; ++q) ws->ky[sp][q] = ker[q];
             } else {
 #pragma unroll
-                for (int z = 0; z < Z; ++z) ws->kzp[sp][z] = (T)0;
-#pragma unroll
-                for (int q = 0; q < W; ++q) ws->kzp[sp][l0 + q] = ker[q];
+                for (int q = 0; q < W; ++q) ws->kz[sp][q] = (double)ker[q];
             }
-            ws->l0[sp][si] = l0;
         }
+        // lane 3 sp packs the point's local support start: x | y << 8 | z << 16
+        const int ly = __shfl(l0, lane + 1);
+        const int lz = __shfl(l0, lane + 2);
+        const int key = l0 | (ly << 8) | (lz << 16);
         {
             const int pn = p0 + PIECE;
             if (lane < min(PIECE, b - pn) * 3) {
@@ -340,47 +357,81 @@ __global__ void __launch_bounds__(kColBlock<T>) k_spread_col(GeomArgs g, const c
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int p = 0; p < np; ++p) {
-            int lxv = 0, lyv = 0;
-            if (valid) {
-                lxv = ws->l0[p][0];
-                lyv = ws->l0[p][1];
-            }
-            const int lx = __builtin_amdgcn_readfirstlane(lxv);
-            const int ly = __builtin_amdgcn_readfirstlane(lyv);
-            if (lx != cur_x || ly != cur_y) {
-                if (cur_x >= 0 && valid) col_flush<T, W>(tre, tim, are, aim, base, pp);
+        // per-point operands, double-buffered: the loads for the next point are issued before
+        // the current point's FMAs, so their LDS latency overlaps useful work
+        struct Pt {
+            cplx<T> cv;
+            T kx, ky;
+            double kz[W];
+        };
+        auto load = [&](int p, Pt& d) {
+            d.cv = ws->cv[p];
+            d.kx = ws->kx[p][q1];
+            d.ky = ws->ky[p][q2];
+#pragma unroll
+            for (int q = 0; q < W; ++q) d.kz[q] = ws->kz[p][q];
+        };
+        auto step = [&](int p, const Pt& d) {
+            const int kp = __builtin_amdgcn_readlane(key, 3 * p);
+            const int col = kp & 0xffff;
+            if (col != cur) {
+                if (cur >= 0 && valid) {
+#pragma unroll
+                    for (int z = 0; z < Z; ++z) {
+                        atomicAdd(tre + cell + z, are[z]);
+                        atomicAdd(tim + cell + z, aim[z]);
+                    }
+                }
 #pragma unroll
                 for (int z = 0; z < Z; ++z) {
-                    are[z] = (T)0;
-                    aim[z] = (T)0;
+                    zero_in_place(are[z]);
+                    zero_in_place(aim[z]);
                 }
-                cur_x = lx;
-                cur_y = ly;
-                base = lx + q1 + (ly + q2) * pc;
+                cur = col;
+                cell = ((col & 0xff) + q1 + ((col >> 8) + q2) * p1) * PZ;
             }
-            if (valid) {
-                const cplx<T> cv = ws->cv[p];
-                const T wxy = ws->kx[p][q1] * ws->ky[p][q2];
-                const T vre = cv.re * wxy, vim = cv.im * wxy;
-#pragma unroll
-                for (int z = 0; z < Z; ++z) {
-                    const T kz = ws->kzp[p][z];
-                    are[z] += vre * kz;
-                    aim[z] += vim * kz;
-                }
-            }
+            const double wxy = (double)(d.kx * d.ky);
+            const double vre = (double)d.cv.re * wxy, vim = (double)d.cv.im * wxy;
+            // nine independent uniform branches; each tests its own opaque copy of the offset
+            // so the compiler cannot fold them into one multiway branch, whose merge points
+            // copy the register line
+            const int z0 = kp >> 16;
+            if (uniform_copy(z0) == 0) col_acc<W, Z, 0>(are, aim, d.kz, vre, vim);
+            if (uniform_copy(z0) == 1) col_acc<W, Z, 1>(are, aim, d.kz, vre, vim);
+            if (uniform_copy(z0) == 2) col_acc<W, Z, 2>(are, aim, d.kz, vre, vim);
+            if (uniform_copy(z0) == 3) col_acc<W, Z, 3>(are, aim, d.kz, vre, vim);
+            if (uniform_copy(z0) == 4) col_acc<W, Z, 4>(are, aim, d.kz, vre, vim);
+            if (uniform_copy(z0) == 5) col_acc<W, Z, 5>(are, aim, d.kz, vre, vim);
+            if (uniform_copy(z0) == 6) col_acc<W, Z, 6>(are, aim, d.kz, vre, vim);
+            if (uniform_copy(z0) == 7) col_acc<W, Z, 7>(are, aim, d.kz, vre, vim);
+            if (uniform_copy(z0) == 8) col_acc<W, Z, 8>(are, aim, d.kz, vre, vim);
+        };
+        Pt da, db;
+        load(0, da);
+        int p = 0;
+        for (; p + 1 < np; p += 2) {
+            load(p + 1, db);
+            step(p, da);
+            if (p + 2 < np) load(p + 2, da);
+            step(p + 1, db);
         }
+        if (p < np) step(p, da);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
-    if (cur_x >= 0 && valid) col_flush<T, W>(tre, tim, are, aim, base, pp);
+    if (cur >= 0 && valid) {
+#pragma unroll
+        for (int z = 0; z < Z; ++z) {
+            atomicAdd(tre + cell + z, are[z]);
+            atomicAdd(tim + cell + z, aim[z]);
+        }
+    }
     __syncthreads();
     // add the padded bin to the fine grid with periodic wrap (eq. (15))
-    const int P = p1 * p2 * p3;
+    const int P = p1 * p2 * Z;
     CellWalk cw(threadIdx.x, BLOCK, p1, p2);
     for (int k = threadIdx.x; k < P; k += BLOCK, cw.next()) {
-        const int li = cw.s1 + cw.s2 * pc + cw.s3 * pp;
+        const int li = (cw.s1 + cw.s2 * p1) * PZ + cw.s3;
         const double re = tre[li], im = tim[li];
         if (re == 0.0 && im == 0.0) continue;
         const int g1 = wrap_grid(origin[0] + cw.s1, g.n[0]);
@@ -393,11 +444,14 @@ __global__ void __launch_bounds__(kColBlock<T>) k_spread_col(GeomArgs g, const c
 }
 
 template <typename T, int W>
-size_t col_stage_bytes() { return sizeof(ColStage<T, W>) * ColCfg<T, W>::kWaves; }
+size_t col_lds_bytes(const int* m) {
+    using C = ColCfg<T, W>;
+    return (size_t)(m[0] + W) * (m[1] + W) * C::kPZ * 2 * sizeof(double) + sizeof(ColStage<T, W>) * C::kWaves;
+}
 
-size_t col_stage_bytes_rt(int prec, int w) {
+size_t col_lds_bytes_rt(int prec, int w, const int* m) {
     switch (w) {
-#define NUFFT_CASE(WW) case WW: return prec == 0 ? col_stage_bytes<float, WW>() : col_stage_bytes<double, WW>();
+#define NUFFT_CASE(WW) case WW: return prec == 0 ? col_lds_bytes<float, WW>(m) : col_lds_bytes<double, WW>(m);
         NUFFT_CASE(5) NUFFT_CASE(6) NUFFT_CASE(7) NUFFT_CASE(8) NUFFT_CASE(9) NUFFT_CASE(10)
         NUFFT_CASE(11) NUFFT_CASE(12)
 #undef NUFFT_CASE
@@ -405,31 +459,22 @@ size_t col_stage_bytes_rt(int prec, int w) {
     }
 }
 
-// Row pitch of the column kernel's tile: the bank-spreading pitch when it fits, else p1.
-int col_row_pitch(int prec, int w, const int* m) {
-    const int p1 = m[0] + w, p2 = m[1] + w, p3 = m[2] + w;
-    const int pc = tile_row_pitch(p1, w);
-    if ((size_t)pc * p2 * p3 * 16 + col_stage_bytes_rt(prec, w) <= 160 * 1024) return pc;
-    return p1;
-}
-
 template <typename T, int W>
 hipError_t spread_col_w(const GeomArgs& g, const void* c, void* grid, hipStream_t st) {
     if (g.M <= 0 || g.nsub <= 0) return hipSuccess;
-    const int p1 = g.m[0] + W, p2 = g.m[1] + W, p3 = g.m[2] + W;
     if (g.m[2] != 8) return hipErrorInvalidConfiguration;
-    const int pc = col_row_pitch(sizeof(T) == 4 ? 0 : 1, W, g.m);
-    const size_t lds = (size_t)pc * p2 * p3 * 2 * sizeof(double) + col_stage_bytes<T, W>();
-    if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
+    const int p1 = g.m[0] + W, p2 = g.m[1] + W;
+    const size_t lds = col_lds_bytes<T, W>(g.m);
+    if (lds > spread_lds_limit()) return hipErrorInvalidConfiguration;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)k_spread_col<T, W>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)spread_lds_limit());
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     k_spread_col<T, W><<<dim3((unsigned)g.nsub), ColCfg<T, W>::kBlock, lds, st>>>(
-        g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2, p3, pc);
+        g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2);
     return hipGetLastError();
 }
 
@@ -571,8 +616,7 @@ bool spread_uses_columns(int dim, int w) { return dim == 3 && w >= 5 && w <= 12;
 
 size_t spread_col_lds_bytes(int prec, int w, const int* m) {
     if (!spread_uses_columns(3, w) || m[2] != 8) return 0;
-    const int pc = col_row_pitch(prec, w, m);
-    return (size_t)pc * (m[1] + w) * (m[2] + w) * 2 * sizeof(double) + col_stage_bytes_rt(prec, w);
+    return col_lds_bytes_rt(prec, w, m);
 }
 
 hipError_t launch_spread(int prec, int method, const GeomArgs& g, const void* c, void* grid,
