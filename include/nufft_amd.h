@@ -133,7 +133,8 @@ const char* nufft_last_error(nufft_plan plan);
  *                  nbins, nsubproblems (after setpts, else 0), M (after setpts, else -1),
  *                  subproblem cap, spreading method (nufft_spread_method),
  *                  column order (kernel width w when the points of a 3D bin are ordered by the
- *                  x-y column of their kernel support, see nufft_get_sort; else 0), 0
+ *                  x-y column block where their kernel support starts, see nufft_get_sort;
+ *                  else 0), column block edge s (1 when there is no column order)
  *   info_d[0..1]:  beta, eps
  * Either pointer may be NULL.
  */
@@ -175,10 +176,11 @@ int nufft_precorrect_pad(nufft_plan plan, const void* f, void* fhat);
  *   subproblems[3*S]  (bin, start, length) per subproblem, S = nsubproblems.
  * Any pointer may be NULL.  Bins are numbered b1 + nb1*(b2 + nb2*b3) with
  * b_i = floor(l_i / m_i), l_i = floor((x_i + pi) n_i / (2 pi)) folded into [0, n_i).
- * Inside a bin the order is the original index; for plans that report a column order w
- * (nufft_get_info), the points of a bin are first ordered by the column
- * (s2 (m1 + 1) + s1) of their kernel support, s_i = ceil(t_i - w/2) - (b_i m_i - floor(w/2)),
- * t_i = (x_i + pi) n_i / (2 pi) folded, and by original index within a column.
+ * Inside a bin the order is the original index; for plans that report a column order w and a
+ * column block edge s (nufft_get_info), the points of a bin are first ordered by the block
+ * (c2 / s) ceil((m1 + 1) / s) + c1 / s of the column where their kernel support starts,
+ * c_i = ceil(t_i - w/2) - (b_i m_i - floor(w/2)), t_i = (x_i + pi) n_i / (2 pi) folded, and by
+ * original index within a block.
  */
 int nufft_get_sort(nufft_plan plan, int32_t* perm, int32_t* counts, int32_t* subproblems);
 

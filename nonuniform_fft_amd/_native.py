@@ -192,6 +192,7 @@ class Plan:
         return {"type": v[0], "dim": v[1], "precision": v[2], "w": v[3], "n": tuple(v[4:4 + self.dim]),
                 "N": tuple(v[7:7 + self.dim]), "bins": tuple(v[10:10 + self.dim]), "nbins": v[13],
                 "nsubproblems": v[14], "M": v[15], "cap": v[16], "method": v[17], "colw": v[18],
+                "colstep": v[19],
                 "beta": dd[0], "eps": dd[1]}
 
     # -- API -----------------------------------------------------------------------------------

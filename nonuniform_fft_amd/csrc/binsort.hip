@@ -56,7 +56,8 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
             lo[i] = (int)ceil(__dsub_rn(t, 0.5 * (double)a.colw)) - (bidx[i] * a.m[i] - a.colw / 2);
             lo[i] = min(max(lo[i], 0), a.m[i]);
         }
-        key = key * a.ncol + lo[1] * (a.m[0] + 1) + lo[0];
+        const int ncx = (a.m[0] + a.colstep) / a.colstep;
+        key = key * a.ncol + (lo[1] / a.colstep) * ncx + lo[0] / a.colstep;
     }
     if (!ok) {
         key = 0;

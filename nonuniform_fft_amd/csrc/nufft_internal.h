@@ -94,6 +94,7 @@ struct nufft_plan_s {
     int cap = 0;
     int nbits = 0;                      // bits of the largest sort key
     int colw = 0;                       // column order inside bins (see SortArgs)
+    int colstep = 1;
     int ncol = 1;
 
     size_t bytes_in_use = 0;
@@ -145,9 +146,10 @@ struct SortArgs {
     int nbins;
     int nbits;
     int cap;
-    int colw;      // > 0: order points inside a bin by the x-y column of their kernel support
-                   //       (3D; colw = kernel width), 0: by original index only
-    int ncol;      // columns per bin, (m1 + 1)(m2 + 1) when colw > 0, else 1
+    int colw;      // > 0: order points inside a bin by the x-y column block where their kernel
+                   //       support starts (3D; colw = kernel width), 0: by original index only
+    int colstep;   // column block edge s: support starts c_i in [0, m_i] grouped as c_i / s
+    int ncol;      // column blocks per bin, ceil((m1 + 1) / s) ceil((m2 + 1) / s), else 1
 };
 // Bytes of scratch the sort needs for M points and the plan's bin count.
 size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec);
@@ -197,5 +199,6 @@ size_t spread_tile_bytes(int prec, int dim, int w, const int* m);
 size_t spread_col_lds_bytes(int prec, int w, const int* m);
 // Whether 3D spreading with this kernel width uses the column-run kernel (needs the column order).
 bool spread_uses_columns(int dim, int w);
+int spread_col_step(int w);   // column block edge the 3D column kernel groups points by
 
 }  // namespace nufft

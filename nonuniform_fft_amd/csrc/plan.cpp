@@ -425,13 +425,16 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
     plan->nbins = (int64_t)plan->nb[0] * plan->nb[1] * plan->nb[2];
     // 3D spreading by column runs needs the points of a bin ordered by support column
     plan->colw = 0;
+    plan->colstep = 1;
     plan->ncol = 1;
     const size_t col_lds = nufft::spread_col_lds_bytes(plan->prec, w, plan->m);
     if (plan->method == NUFFT_METHOD_SM && nufft::spread_uses_columns(dim, w) && plan->m[2] == 8 &&
         col_lds > 0 && col_lds <= nufft::spread_lds_limit()) {
-        const int64_t ncol = (int64_t)(plan->m[0] + 1) * (plan->m[1] + 1);
+        const int step = nufft::spread_col_step(w);
+        const int64_t ncol = (int64_t)((plan->m[0] + step) / step) * ((plan->m[1] + step) / step);
         if (plan->nbins * ncol < (int64_t(1) << 31)) {
             plan->colw = w;
+            plan->colstep = step;
             plan->ncol = (int)ncol;
         }
     }
@@ -532,6 +535,7 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     a.nbits = plan->nbits;
     a.cap = plan->cap;
     a.colw = plan->colw;
+    a.colstep = plan->colstep;
     a.ncol = plan->ncol;
     NUFFT_HIP(nufft::launch_sort(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p,
                                  (int32_t*)plan->offsets.p, plan->xs.p, plan->sort_tmp.p,
@@ -605,7 +609,7 @@ int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d) {
         int64_t v[20] = {plan->type, plan->dim, plan->prec, plan->w, plan->n[0], plan->n[1], plan->n[2],
                          plan->N[0], plan->N[1], plan->N[2], plan->m[0], plan->m[1], plan->m[2],
                          plan->nbins, plan->M >= 0 ? plan->nsub : 0, plan->M, plan->cap, plan->method,
-                         plan->colw, 0};
+                         plan->colw, plan->colstep};
         std::memcpy(info_i, v, sizeof(v));
     }
     if (info_d) {

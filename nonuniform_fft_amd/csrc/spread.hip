@@ -193,41 +193,48 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
 // ------------------------------------------------------------------------------------------
 // 3D column-run spreading.
 //
-// The points of a bin arrive ordered by the x-y column of their kernel support (setpts orders
-// them so).  A wavefront walks a slice of the subproblem's points; its lanes own the w x w
-// (q1, q2) slots of a support column and keep the whole z-line of that column (8 + w cells)
-// in fp64 registers.  Consecutive points of the same column -- about m3 * density of them --
-// are accumulated in registers and the line is added to the LDS padded bin only when the
-// column changes, so the LDS atomics per point drop from 2 w^3 to about 2 w^2 (8 + w) / run
-// length.  All lanes of a wavefront work on the same point, so the point's z offset inside
-// the line is wave-uniform: a scalar branch picks the w registers it updates, and each point
-// costs 2 w FMAs per lane.  The LDS bin is stored z-fastest in separate real and imaginary
-// planes (cell = (x + y p1) pz + z, pz odd) so a line is flushed with fixed offsets and the
-// lanes of a flush fall on distinct bank pairs.  Per-point weights are staged per
-// wavefront (no workgroup barrier inside the loop).
+// The lanes of a wavefront (or of kSlotWaves wavefronts) own a B x B block of x-y columns of
+// the padded bin and keep the whole z-line of each column (8 + w cells) in registers, in the
+// transform's precision (a run's sum is added to the fp64 LDS bin when the run ends).  A
+// point whose kernel support starts at column (c1, c2) fits in the block at origin
+// (s floor(c1 / s), s floor(c2 / s)) with s = B - w + 1, so setpts orders the points of a bin
+// by that column block and a wavefront accumulates every point of a block in registers; the
+// lines are added to the LDS padded bin only when the block changes (about s^2 m3 points per
+// run).  The point's x and y weights are staged as zero-padded B-wide windows, so each lane
+// reads its own two weights and all lanes stay live in the flush.  All lanes work on the same
+// point, so its z offset inside the line is wave-uniform: a scalar branch picks the w
+// registers it updates, and each point costs 2 w FMAs per lane.  The LDS bin is stored
+// z-fastest in separate real and imaginary planes (cell = (x + y p1) pz + z, pz odd) so a line
+// is flushed with fixed offsets and the lanes of a flush fall on distinct bank pairs.
+// Per-point weights are staged per wavefront (no workgroup barrier inside the loop).
 // ------------------------------------------------------------------------------------------
-// wide fp64 z-lines need more registers per lane: 8 wavefronts per workgroup
+// column block edge per kernel width: one wavefront for w <= 6, two up to 10, three above
+__host__ __device__ constexpr int col_block_edge(int w) { return w <= 6 ? 8 : (w <= 10 ? 11 : (w == 11 ? 12 : 13)); }
+
+// register budget: fp64 z-lines need twice the registers per lane, so half the wavefronts
 template <typename T, int W>
-constexpr int kColBlock = (sizeof(T) == 4 && W <= 6) ? 1024 : (sizeof(T) == 4 && W <= 8) ? 768 : 512;
+constexpr int kColBlock = (sizeof(T) == 4) ? 1024 : 512;
 
 template <typename T, int W>
 struct ColCfg {
     static constexpr int kZ = 8 + W;                        // z extent of the padded bin (m3 = 8)
     static constexpr int kPZ = kZ | 1;                      // odd z pitch of the LDS bin
+    static constexpr int kB = col_block_edge(W);            // column block edge
+    static constexpr int kS = kB - W + 1;                   // support starts per block edge
     static constexpr int kBlock = kColBlock<T, W>;
     static constexpr int kWaves = kBlock / 64;
-    static constexpr int kSlotWaves = (W * W + 63) / 64;    // wavefronts sharing one slice
+    static constexpr int kSlotWaves = (kB * kB + 63) / 64;  // wavefronts sharing one slice
     static constexpr int kPiece = (sizeof(T) == 4) ? 21 : 6;  // points staged per round (3 lanes each)
-    static constexpr int kWZ = (W + 1) & ~1;                // z weights padded to 16-byte pairs
+    static constexpr int kWZ = (sizeof(T) == 4) ? ((W + 3) & ~3) : ((W + 1) & ~1);  // 16-byte rows
 };
 
 template <typename T, int W>
 struct ColStage {
     using C = ColCfg<T, W>;
-    double kz[C::kPiece][C::kWZ];
+    T kz[C::kPiece][C::kWZ];
     cplx<T> cv[C::kPiece];
-    T kx[C::kPiece][W];
-    T ky[C::kPiece][W];
+    T kx[C::kPiece][C::kB];       // x weights placed in the point's block window (zero elsewhere)
+    T ky[C::kPiece][C::kB];
 };
 
 // A copy of a wave-uniform value that the optimizer cannot see through.
@@ -240,11 +247,11 @@ __device__ __forceinline__ int uniform_copy(int v) {
 // Clears a register in place (a plain assignment of 0 lets the allocator rotate the whole
 // register line through copies at the loop head).
 __device__ __forceinline__ void zero_in_place(double& v) { asm volatile("v_mov_b64 %0, 0" : "+v"(v)); }
+__device__ __forceinline__ void zero_in_place(float& v) { asm volatile("v_mov_b32 %0, 0" : "+v"(v)); }
 
 // Adds the point's w z-weights times v into the register line at the wave-uniform offset Z0.
-template <int W, int Z, int Z0>
-__device__ __forceinline__ void col_acc(double (&are)[Z], double (&aim)[Z], const double (&kz)[W],
-                                        double vre, double vim) {
+template <int W, int Z, int Z0, typename A>
+__device__ __forceinline__ void col_acc(A (&are)[Z], A (&aim)[Z], const A (&kz)[W], A vre, A vim) {
 #pragma unroll
     for (int q = 0; q < W; ++q) {
         are[Z0 + q] = fma(vre, kz[q], are[Z0 + q]);
@@ -259,6 +266,8 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
     using St = ColStage<T, W>;
     constexpr int Z = C::kZ;
     constexpr int PZ = C::kPZ;
+    constexpr int B = C::kB;
+    constexpr int S = C::kS;
     constexpr int SW = C::kSlotWaves;
     constexpr int SLICES = C::kWaves / SW;
     constexpr int PIECE = C::kPiece;
@@ -291,21 +300,22 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
     const int slice = wave / SW, sub_wave = wave - slice * SW;
     St* ws = stages + wave;
     const int slot = sub_wave * 64 + lane;
-    // lanes past the w x w slots run along (slot 0's weights) but never flush
-    const bool valid = (slot < W * W) && (slice < SLICES);
-    const int q2 = valid ? slot / W : 0;
-    const int q1 = valid ? slot - q2 * W : 0;
+    // lanes past the B x B block run along (column (0, 0)'s weights) but never flush
+    const bool valid = (slot < B * B) && (slice < SLICES);
+    const int q2 = valid ? slot / B : 0;
+    const int q1 = valid ? slot - q2 * B : 0;
     const int per = (len + SLICES - 1) / SLICES;
     const int a = (slice < SLICES) ? min(len, slice * per) : len;
     const int b = (slice < SLICES) ? min(len, a + per) : len;
 
-    double are[Z], aim[Z];
+    T are[Z], aim[Z];
 #pragma unroll
     for (int z = 0; z < Z; ++z) {
-        are[z] = 0.0;
-        aim[z] = 0.0;
+        are[z] = (T)0;
+        aim[z] = (T)0;
     }
     int cur = -1, cell = 0;
+    bool live = false;   // this lane's column lies inside the padded bin
     const T beta = (T)g.beta;
     // staging lane (point sp, dimension si); the raw coordinate and strength of the next piece
     // are loaded into registers while the current piece is processed
@@ -329,19 +339,23 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
             T ker[W];
             l0 = es_weights<T, W>(tt, beta, ker) - origin[si];
             l0 = min(max(l0, 0), pd[si] - W);
-            if (si == 0) {
+            if (si < 2) {
+                // x or y: the block index, and the weights placed in the block's window
+                const int blk = l0 / S;
+                const int off = l0 - blk * S;
+                T* win = (si == 0) ? ws->kx[sp] : ws->ky[sp];
 #pragma unroll
-                for (int q = 0; q < W; ++q) ws->kx[sp][q] = ker[q];
-                ws->cv[sp] = cr;
-            } else if (si == 1) {
+                for (int q = 0; q < B; ++q) win[q] = (T)0;
 #pragma unroll
-                for (int q = 0; q < W; ++q) ws->ky[sp][q] = ker[q];
+                for (int q = 0; q < W; ++q) win[off + q] = ker[q];
+                if (si == 0) ws->cv[sp] = cr;
+                l0 = blk;
             } else {
 #pragma unroll
-                for (int q = 0; q < W; ++q) ws->kz[sp][q] = (double)ker[q];
+                for (int q = 0; q < W; ++q) ws->kz[sp][q] = ker[q];
             }
         }
-        // lane 3 sp packs the point's local support start: x | y << 8 | z << 16
+        // lane 3 sp packs the point's x block | y block << 8 | z start << 16
         const int ly = __shfl(l0, lane + 1);
         const int lz = __shfl(l0, lane + 2);
         const int key = l0 | (ly << 8) | (lz << 16);
@@ -362,7 +376,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
         struct Pt {
             cplx<T> cv;
             T kx, ky;
-            double kz[W];
+            T kz[W];
         };
         auto load = [&](int p, Pt& d) {
             d.cv = ws->cv[p];
@@ -375,11 +389,11 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
             const int kp = __builtin_amdgcn_readlane(key, 3 * p);
             const int col = kp & 0xffff;
             if (col != cur) {
-                if (cur >= 0 && valid) {
+                if (cur >= 0 && live) {
 #pragma unroll
                     for (int z = 0; z < Z; ++z) {
-                        atomicAdd(tre + cell + z, are[z]);
-                        atomicAdd(tim + cell + z, aim[z]);
+                        atomicAdd(tre + cell + z, (double)are[z]);
+                        atomicAdd(tim + cell + z, (double)aim[z]);
                     }
                 }
 #pragma unroll
@@ -388,10 +402,12 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
                     zero_in_place(aim[z]);
                 }
                 cur = col;
-                cell = ((col & 0xff) + q1 + ((col >> 8) + q2) * p1) * PZ;
+                const int cx = (col & 0xff) * S + q1, cy = (col >> 8) * S + q2;
+                live = valid && cx < p1 && cy < p2;
+                cell = (cx + cy * p1) * PZ;
             }
-            const double wxy = (double)(d.kx * d.ky);
-            const double vre = (double)d.cv.re * wxy, vim = (double)d.cv.im * wxy;
+            const T wxy = d.kx * d.ky;
+            const T vre = d.cv.re * wxy, vim = d.cv.im * wxy;
             // nine independent uniform branches; each tests its own opaque copy of the offset
             // so the compiler cannot fold them into one multiway branch, whose merge points
             // copy the register line
@@ -419,11 +435,11 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
-    if (cur >= 0 && valid) {
+    if (cur >= 0 && live) {
 #pragma unroll
         for (int z = 0; z < Z; ++z) {
-            atomicAdd(tre + cell + z, are[z]);
-            atomicAdd(tim + cell + z, aim[z]);
+            atomicAdd(tre + cell + z, (double)are[z]);
+            atomicAdd(tim + cell + z, (double)aim[z]);
         }
     }
     __syncthreads();
@@ -613,6 +629,8 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 }
 
 bool spread_uses_columns(int dim, int w) { return dim == 3 && w >= 5 && w <= 12; }
+
+int spread_col_step(int w) { return col_block_edge(w) - w + 1; }
 
 size_t spread_col_lds_bytes(int prec, int w, const int* m) {
     if (!spread_uses_columns(3, w) || m[2] != 8) return 0;

@@ -176,22 +176,27 @@ int oracle_interp(int d, const int64_t* n, int w, double beta, int64_t M,
  * Outputs: bin[j]; counts[b] = number of points in bin b; perm = the points
  * listed bin by bin (a stable counting sort: the list is read out in bin
  * order).  Inside a bin the order is the original index, or, when w_col > 0
- * (3D only), the x-y column of the point's kernel support first: the column of
- * a point is (l0_2 - o_2) (m1 + 1) + (l0_1 - o_1), where l0_i = ceil(t_i - w/2)
- * starts the support and o_i = b_i m_i - floor(w/2) is its bin's padded origin,
- * then the original index.
+ * (3D only), the x-y column block of the point's kernel support first, then
+ * the original index.  The support of a point starts at l0_i = ceil(t_i - w/2);
+ * relative to its bin's padded origin o_i = b_i m_i - floor(w/2) that start is
+ * c_i = l0_i - o_i in [0, m_i].  Starts are grouped in blocks of s x s
+ * (s = col_step >= 1): the block is (c_1 / s, c_2 / s), numbered
+ * (c_2 / s) ceil((m1 + 1) / s) + c_1 / s.  This ordering is not from the
+ * pages: it is the order the 3D spreading kernel consumes, stated here so the
+ * permutation can be checked exactly.
  */
 int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const double* const* X,
-                   int w_col, int64_t* bin, int64_t* counts, int64_t* perm)
+                   int w_col, int col_step, int64_t* bin, int64_t* counts, int64_t* perm)
 {
-    if (d < 1 || d > 3 || M < 0) return ORACLE_BAD_ARG;
+    if (d < 1 || d > 3 || M < 0 || col_step < 1) return ORACLE_BAD_ARG;
     int64_t nb[3] = {1, 1, 1};
     for (int i = 0; i < d; ++i) {
         if (n[i] < 1 || m[i] < 1) return ORACLE_BAD_ARG;
         nb[i] = (n[i] + m[i] - 1) / m[i];
     }
     int use_col = (w_col > 0 && d == 3);
-    int64_t ncol = use_col ? (m[0] + 1) * (m[1] + 1) : 1;
+    int64_t ncx = (m[0] + col_step) / col_step, ncy = (m[1] + col_step) / col_step;
+    int64_t ncol = use_col ? ncx * ncy : 1;
     int64_t nbins = nb[0] * nb[1] * nb[2];
     int64_t nkeys = nbins * ncol;
     int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
@@ -211,7 +216,7 @@ int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const d
         }
         bin[j] = bi[0] + nb[0] * (bi[1] + nb[1] * bi[2]);
         counts[bin[j]] += 1;
-        key[j] = use_col ? bin[j] * ncol + (lo[1] * (m[0] + 1) + lo[0]) : bin[j];
+        key[j] = use_col ? bin[j] * ncol + ((lo[1] / col_step) * ncx + lo[0] / col_step) : bin[j];
         next[key[j]] += 1;
     }
     int64_t run = 0;

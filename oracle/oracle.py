@@ -73,7 +73,7 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = [I, P, I, D, L, P, P, P]
             fn.restype = I
-        lib.oracle_binsort.argtypes = [I, P, P, L, P, I, P, P, P]
+        lib.oracle_binsort.argtypes = [I, P, P, L, P, I, I, P, P, P]
         lib.oracle_binsort.restype = I
         lib.oracle_subproblems.argtypes = [L, P, L, P]
         lib.oracle_subproblems.restype = L
@@ -371,9 +371,10 @@ def direct_type2(X, f, N: Sequence[int], sel: Optional[Sequence[int]] = None) ->
 # Bin-sort and subproblems (Sec. III-A)
 # ----------------------------------------------------------------------------------------------
 
-def binsort(X, n: Sequence[int], m: Sequence[int], w_col: int = 0):
+def binsort(X, n: Sequence[int], m: Sequence[int], w_col: int = 0, col_step: int = 1):
     """Returns (bin_of_point, counts, perm) as int64 arrays; see the C routine.  With w_col > 0
-    (3D) the points of a bin are ordered by the x-y column of their kernel support."""
+    (3D) the points of a bin are ordered by the col_step x col_step block of the x-y column where
+    their kernel support starts."""
     lib = _load()
     d = len(n)
     xs, xa = _coords(X)
@@ -384,7 +385,7 @@ def binsort(X, n: Sequence[int], m: Sequence[int], w_col: int = 0):
     counts = np.zeros(nbins, dtype=np.int64)
     perm = np.zeros(M, dtype=np.int64)
     nn, mm = _i64(n), _i64(m)
-    _check(lib.oracle_binsort(d, _ptr(nn), _ptr(mm), M, xa, int(w_col), _ptr(binv), _ptr(counts),
+    _check(lib.oracle_binsort(d, _ptr(nn), _ptr(mm), M, xa, int(w_col), int(col_step), _ptr(binv), _ptr(counts),
                               _ptr(perm)), "binsort")
     return binv, counts, perm
 

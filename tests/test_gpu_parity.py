@@ -63,7 +63,8 @@ def test_binsort_bit_exact(nf, orc, name, wl, cap):
     p.setpts(*[to_dev(x) for x in X])
     info = p.info()
     perm, counts, sub = [t.cpu().numpy().astype(np.int64) for t in p.get_sort()]
-    _, ocounts, operm = orc.binsort(X, info["n"], info["bins"], w_col=info["colw"])
+    _, ocounts, operm = orc.binsort(X, info["n"], info["bins"], w_col=info["colw"],
+                                    col_step=info["colstep"])
     np.testing.assert_array_equal(counts, ocounts)
     np.testing.assert_array_equal(perm, operm)
     if cap > 0:
@@ -85,7 +86,8 @@ def test_binsort_boundary_points(nf, orc):
         p.setpts(*[to_dev(x) for x in X])
         info = p.info()
         perm, counts, _ = [t.cpu().numpy().astype(np.int64) for t in p.get_sort()]
-        _, ocounts, operm = orc.binsort(X, info["n"], info["bins"], w_col=info["colw"])
+        _, ocounts, operm = orc.binsort(X, info["n"], info["bins"], w_col=info["colw"],
+                                        col_step=info["colstep"])
         np.testing.assert_array_equal(counts, ocounts)
         np.testing.assert_array_equal(perm, operm)
         p.destroy()

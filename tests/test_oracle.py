@@ -403,16 +403,17 @@ def test_points_out_of_range_rejected(oracle_mod):
         oracle_mod.spread([np.array([np.nan]), np.array([0.0])], np.array([1 + 0j]), (16, 16), 4, 9.2)
 
 
-def test_bins_column_order_within_bins(oracle_mod):
-    """3D column order: perm is numpy's stable lexsort by (bin, support column), the column of a
-    point being (l0_2 - o_2)(m1 + 1) + (l0_1 - o_1) with l0 the kernel-support start (computed here
-    in extended precision) and o the bin's padded origin."""
+@pytest.mark.parametrize("step", [1, 2, 3, 4])
+def test_bins_column_order_within_bins(oracle_mod, step):
+    """3D column order: perm is numpy's stable lexsort by (bin, support-column block), the block of
+    a point being (c_2 // s) ceil((m1 + 1) / s) + c_1 // s with c = l0 - o, l0 the kernel-support
+    start (computed here in extended precision), o the bin's padded origin and s the step."""
     n = (32, 24, 20)
     m = (8, 8, 4)
     w = 6
     rng = _rng(12)
     X = [rng.uniform(-math.pi, math.pi, 4000) for _ in range(3)]
-    binv, counts, perm = oracle_mod.binsort(X, n, m, w_col=w)
+    binv, counts, perm = oracle_mod.binsort(X, n, m, w_col=w, col_step=step)
     binv0, counts0, perm0 = oracle_mod.binsort(X, n, m)
     np.testing.assert_array_equal(binv, binv0)
     np.testing.assert_array_equal(counts, counts0)
@@ -424,7 +425,8 @@ def test_bins_column_order_within_bins(oracle_mod):
         l0 = np.ceil(t - w / 2).astype(np.int64)
         lo.append(l0 - (bidx[i] * m[i] - w // 2))
     assert lo[0].min() >= 0 and lo[0].max() <= m[0] and lo[1].min() >= 0 and lo[1].max() <= m[1]
-    col = lo[1] * (m[0] + 1) + lo[0]
+    ncx = -(-(m[0] + 1) // step)
+    col = (lo[1] // step) * ncx + lo[0] // step
     expect = np.lexsort((np.arange(4000), col, binv))
     np.testing.assert_array_equal(perm, expect)
     # 2D ignores the column order
