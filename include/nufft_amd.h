@@ -178,9 +178,9 @@ int nufft_precorrect_pad(nufft_plan plan, const void* f, void* fhat);
  * b_i = floor(l_i / m_i), l_i = floor((x_i + pi) n_i / (2 pi)) folded into [0, n_i).
  * Inside a bin the order is the original index; for plans that report a column order w and a
  * column block edge s (nufft_get_info), the points of a bin are first ordered by the block
- * (c2 / s) ceil((m1 + 1) / s) + c1 / s of the column where their kernel support starts,
- * c_i = ceil(t_i - w/2) - (b_i m_i - floor(w/2)), t_i = (x_i + pi) n_i / (2 pi) folded, and by
- * original index within a block.
+ * (c2 / s) ceil((m1 + 1) / s) + c1 / s of the column where their kernel support starts, then by
+ * the z start c3, with c_i = ceil(t_i - w/2) - (b_i m_i - floor(w/2)) and
+ * t_i = (x_i + pi) n_i / (2 pi) folded, and by original index last.
  */
 int nufft_get_sort(nufft_plan plan, int32_t* perm, int32_t* counts, int32_t* subproblems);
 

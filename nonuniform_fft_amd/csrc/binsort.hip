@@ -47,9 +47,9 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
     int key = bidx[0] + a.nb[0] * (bidx[1] + a.nb[1] * bidx[2]);
     if (DIM == 3 && a.colw > 0) {
         // column of the kernel support inside the bin's padded tile (see SortArgs::colw)
-        int lo[2];
+        int lo[3];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 3; ++i) {
             double t = grid_t((double)((const T*)a.x[i])[j], a.s[i]);
             int l = 0;
             fold_t(t, a.n[i], l);
@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
             lo[i] = min(max(lo[i], 0), a.m[i]);
         }
         const int ncx = (a.m[0] + a.colstep) / a.colstep;
-        key = key * a.ncol + (lo[1] / a.colstep) * ncx + lo[0] / a.colstep;
+        key = key * a.ncol + ((lo[1] / a.colstep) * ncx + lo[0] / a.colstep) * (a.m[2] + 1) + lo[2];
     }
     if (!ok) {
         key = 0;

@@ -147,9 +147,10 @@ struct SortArgs {
     int nbits;
     int cap;
     int colw;      // > 0: order points inside a bin by the x-y column block where their kernel
-                   //       support starts (3D; colw = kernel width), 0: by original index only
+                   //       support starts, then by its z start (3D; colw = kernel width),
+                   //       0: by original index only
     int colstep;   // column block edge s: support starts c_i in [0, m_i] grouped as c_i / s
-    int ncol;      // column blocks per bin, ceil((m1 + 1) / s) ceil((m2 + 1) / s), else 1
+    int ncol;      // keys per bin, ceil((m1 + 1) / s) ceil((m2 + 1) / s) (m3 + 1), else 1
 };
 // Bytes of scratch the sort needs for M points and the plan's bin count.
 size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec);

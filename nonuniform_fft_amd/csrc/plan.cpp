@@ -170,7 +170,7 @@ int64_t mode_count(const nufft_plan p) { return p->N[0] * p->N[1] * p->N[2]; }
 // tile plus point staging fits the LDS limit.
 void default_bins(nufft_plan p, int* m) {
     static const int c2[][2] = {{32, 32}, {32, 16}, {16, 16}, {16, 8}, {8, 8}, {4, 4}, {2, 2}, {1, 1}};
-    static const int c3[][3] = {{16, 16, 8}, {16, 8, 8}, {8, 8, 8}, {8, 8, 4}, {8, 4, 4},
+    static const int c3[][3] = {{32, 16, 8}, {16, 16, 8}, {16, 8, 8}, {8, 8, 8}, {8, 8, 4}, {8, 4, 4},
                                 {4, 4, 4}, {4, 4, 2}, {2, 2, 2}, {1, 1, 1}};
     if (p->dim == 2) {
         for (auto& c : c2) {
@@ -187,6 +187,7 @@ void default_bins(nufft_plan p, int* m) {
         const bool col = nufft::spread_uses_columns(3, p->w) && p->method == NUFFT_METHOD_SM;
         for (int pass = col ? 0 : 1; pass < 2; ++pass) {
             for (auto& c : c3) {
+                if (pass == 1 && c[0] > 16) continue;   // the point-patch kernel keeps 16 x 16 x 8
                 int mm[3] = {c[0], c[1], c[2]};
                 const size_t need = (pass == 0) ? nufft::spread_col_lds_bytes(p->prec, p->w, mm)
                                                 : nufft::spread_tile_bytes(p->prec, 3, p->w, mm);
@@ -431,7 +432,8 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
     if (plan->method == NUFFT_METHOD_SM && nufft::spread_uses_columns(dim, w) && plan->m[2] == 8 &&
         col_lds > 0 && col_lds <= nufft::spread_lds_limit()) {
         const int step = nufft::spread_col_step(w);
-        const int64_t ncol = (int64_t)((plan->m[0] + step) / step) * ((plan->m[1] + step) / step);
+        const int64_t ncol = (int64_t)((plan->m[0] + step) / step) * ((plan->m[1] + step) / step) *
+                             (plan->m[2] + 1);
         if (plan->nbins * ncol < (int64_t(1) << 31)) {
             plan->colw = w;
             plan->colstep = step;

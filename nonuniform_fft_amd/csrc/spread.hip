@@ -628,6 +628,8 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
     return hipGetLastError();
 }
 
+// below w = 5 the per-point overhead of a column run outweighs its savings: the point-patch
+// kernel is faster there
 bool spread_uses_columns(int dim, int w) { return dim == 3 && w >= 5 && w <= 12; }
 
 int spread_col_step(int w) { return col_block_edge(w) - w + 1; }

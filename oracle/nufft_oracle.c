@@ -177,13 +177,14 @@ int oracle_interp(int d, const int64_t* n, int w, double beta, int64_t M,
  * listed bin by bin (a stable counting sort: the list is read out in bin
  * order).  Inside a bin the order is the original index, or, when w_col > 0
  * (3D only), the x-y column block of the point's kernel support first, then
- * the original index.  The support of a point starts at l0_i = ceil(t_i - w/2);
- * relative to its bin's padded origin o_i = b_i m_i - floor(w/2) that start is
- * c_i = l0_i - o_i in [0, m_i].  Starts are grouped in blocks of s x s
- * (s = col_step >= 1): the block is (c_1 / s, c_2 / s), numbered
- * (c_2 / s) ceil((m1 + 1) / s) + c_1 / s.  This ordering is not from the
- * pages: it is the order the 3D spreading kernel consumes, stated here so the
- * permutation can be checked exactly.
+ * the z start of the support, then the original index.  The support of a point
+ * starts at l0_i = ceil(t_i - w/2); relative to its bin's padded origin
+ * o_i = b_i m_i - floor(w/2) that start is c_i = l0_i - o_i in [0, m_i].
+ * Starts are grouped in blocks of s x s (s = col_step >= 1): the block is
+ * (c_1 / s, c_2 / s), numbered (c_2 / s) ceil((m1 + 1) / s) + c_1 / s, and the
+ * in-bin key is block (m3 + 1) + c_3.  This ordering is not from the pages:
+ * it is the order the 3D kernels consume, stated here so the permutation can
+ * be checked exactly.
  */
 int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const double* const* X,
                    int w_col, int col_step, int64_t* bin, int64_t* counts, int64_t* perm)
@@ -196,7 +197,7 @@ int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const d
     }
     int use_col = (w_col > 0 && d == 3);
     int64_t ncx = (m[0] + col_step) / col_step, ncy = (m[1] + col_step) / col_step;
-    int64_t ncol = use_col ? ncx * ncy : 1;
+    int64_t ncol = use_col ? ncx * ncy * (m[2] + 1) : 1;
     int64_t nbins = nb[0] * nb[1] * nb[2];
     int64_t nkeys = nbins * ncol;
     int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
@@ -216,7 +217,8 @@ int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const d
         }
         bin[j] = bi[0] + nb[0] * (bi[1] + nb[1] * bi[2]);
         counts[bin[j]] += 1;
-        key[j] = use_col ? bin[j] * ncol + ((lo[1] / col_step) * ncx + lo[0] / col_step) : bin[j];
+        key[j] = use_col ? bin[j] * ncol + ((lo[1] / col_step) * ncx + lo[0] / col_step) * (m[2] + 1) + lo[2]
+                         : bin[j];
         next[key[j]] += 1;
     }
     int64_t run = 0;

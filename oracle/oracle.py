@@ -58,8 +58,8 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I = ctypes.c_int
@@ -374,7 +374,7 @@ def direct_type2(X, f, N: Sequence[int], sel: Optional[Sequence[int]] = None) ->
 def binsort(X, n: Sequence[int], m: Sequence[int], w_col: int = 0, col_step: int = 1):
     """Returns (bin_of_point, counts, perm) as int64 arrays; see the C routine.  With w_col > 0
     (3D) the points of a bin are ordered by the col_step x col_step block of the x-y column where
-    their kernel support starts."""
+    their kernel support starts, then by the z start of the support."""
     lib = _load()
     d = len(n)
     xs, xa = _coords(X)

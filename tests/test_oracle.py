@@ -405,9 +405,10 @@ def test_points_out_of_range_rejected(oracle_mod):
 
 @pytest.mark.parametrize("step", [1, 2, 3, 4])
 def test_bins_column_order_within_bins(oracle_mod, step):
-    """3D column order: perm is numpy's stable lexsort by (bin, support-column block), the block of
-    a point being (c_2 // s) ceil((m1 + 1) / s) + c_1 // s with c = l0 - o, l0 the kernel-support
-    start (computed here in extended precision), o the bin's padded origin and s the step."""
+    """3D column order: perm is numpy's stable lexsort by (bin, support-column block, z start), the
+    block of a point being (c_2 // s) ceil((m1 + 1) / s) + c_1 // s with c = l0 - o, l0 the
+    kernel-support start (computed here in extended precision), o the bin's padded origin and s
+    the step."""
     n = (32, 24, 20)
     m = (8, 8, 4)
     w = 6
@@ -418,16 +419,17 @@ def test_bins_column_order_within_bins(oracle_mod, step):
     np.testing.assert_array_equal(binv, binv0)
     np.testing.assert_array_equal(counts, counts0)
     nb0, nb1 = (n[0] + m[0] - 1) // m[0], (n[1] + m[1] - 1) // m[1]
-    bidx = [binv % nb0, (binv // nb0) % nb1]
+    bidx = [binv % nb0, (binv // nb0) % nb1, binv // (nb0 * nb1)]
     lo = []
-    for i in range(2):
+    for i in range(3):
         t = (np.longdouble(X[i]) + np.longdouble(math.pi)) * n[i] / (2 * np.longdouble(math.pi))
         l0 = np.ceil(t - w / 2).astype(np.int64)
         lo.append(l0 - (bidx[i] * m[i] - w // 2))
-    assert lo[0].min() >= 0 and lo[0].max() <= m[0] and lo[1].min() >= 0 and lo[1].max() <= m[1]
+    for i in range(3):
+        assert lo[i].min() >= 0 and lo[i].max() <= m[i]
     ncx = -(-(m[0] + 1) // step)
     col = (lo[1] // step) * ncx + lo[0] // step
-    expect = np.lexsort((np.arange(4000), col, binv))
+    expect = np.lexsort((np.arange(4000), lo[2], col, binv))
     np.testing.assert_array_equal(perm, expect)
     # 2D ignores the column order
     _, _, p2 = oracle_mod.binsort(X[:2], n[:2], m[:2], w_col=w)
