@@ -237,6 +237,11 @@ struct ColStage {
     T ky[C::kPiece][C::kB];
 };
 
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
 // A copy of a wave-uniform value that the optimizer cannot see through.
 __device__ __forceinline__ int uniform_copy(int v) {
     int r;
@@ -371,21 +376,23 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // per-point operands, double-buffered: the loads for the next point are issued before
-        // the current point's FMAs, so their LDS latency overlaps useful work
-        struct Pt {
-            cplx<T> cv;
-            T kx, ky;
-            T kz[W];
-        };
-        auto load = [&](int p, Pt& d) {
-            d.cv = ws->cv[p];
-            d.kx = ws->kx[p][q1];
-            d.ky = ws->ky[p][q2];
+        // The points arrive grouped by (column block, z start).  One scalar dispatch on the z
+        // start covers a whole group, whose points then cost only their loads and 2 w FMAs.
+        auto group = [&](auto z0c, int p, int kp) -> int {
+            constexpr int Z0 = decltype(z0c)::value;
+            do {
+                const cplx<T> cv = ws->cv[p];
+                const T wxy = ws->kx[p][q1] * ws->ky[p][q2];
+                T kz[W];
 #pragma unroll
-            for (int q = 0; q < W; ++q) d.kz[q] = ws->kz[p][q];
+                for (int q = 0; q < W; ++q) kz[q] = ws->kz[p][q];
+                col_acc<W, Z, Z0>(are, aim, kz, cv.re * wxy, cv.im * wxy);
+                ++p;
+            } while (p < np && __builtin_amdgcn_readlane(key, 3 * p) == kp);
+            return p;
         };
-        auto step = [&](int p, const Pt& d) {
+        int p = 0;
+        while (p < np) {
             const int kp = __builtin_amdgcn_readlane(key, 3 * p);
             const int col = kp & 0xffff;
             if (col != cur) {
@@ -406,32 +413,20 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
                 live = valid && cx < p1 && cy < p2;
                 cell = (cx + cy * p1) * PZ;
             }
-            const T wxy = d.kx * d.ky;
-            const T vre = d.cv.re * wxy, vim = d.cv.im * wxy;
             // nine independent uniform branches; each tests its own opaque copy of the offset
             // so the compiler cannot fold them into one multiway branch, whose merge points
             // copy the register line
             const int z0 = kp >> 16;
-            if (uniform_copy(z0) == 0) col_acc<W, Z, 0>(are, aim, d.kz, vre, vim);
-            if (uniform_copy(z0) == 1) col_acc<W, Z, 1>(are, aim, d.kz, vre, vim);
-            if (uniform_copy(z0) == 2) col_acc<W, Z, 2>(are, aim, d.kz, vre, vim);
-            if (uniform_copy(z0) == 3) col_acc<W, Z, 3>(are, aim, d.kz, vre, vim);
-            if (uniform_copy(z0) == 4) col_acc<W, Z, 4>(are, aim, d.kz, vre, vim);
-            if (uniform_copy(z0) == 5) col_acc<W, Z, 5>(are, aim, d.kz, vre, vim);
-            if (uniform_copy(z0) == 6) col_acc<W, Z, 6>(are, aim, d.kz, vre, vim);
-            if (uniform_copy(z0) == 7) col_acc<W, Z, 7>(are, aim, d.kz, vre, vim);
-            if (uniform_copy(z0) == 8) col_acc<W, Z, 8>(are, aim, d.kz, vre, vim);
-        };
-        Pt da, db;
-        load(0, da);
-        int p = 0;
-        for (; p + 1 < np; p += 2) {
-            load(p + 1, db);
-            step(p, da);
-            if (p + 2 < np) load(p + 2, da);
-            step(p + 1, db);
+            if (uniform_copy(z0) == 0) p = group(IntC<0>{}, p, kp);
+            if (uniform_copy(z0) == 1) p = group(IntC<1>{}, p, kp);
+            if (uniform_copy(z0) == 2) p = group(IntC<2>{}, p, kp);
+            if (uniform_copy(z0) == 3) p = group(IntC<3>{}, p, kp);
+            if (uniform_copy(z0) == 4) p = group(IntC<4>{}, p, kp);
+            if (uniform_copy(z0) == 5) p = group(IntC<5>{}, p, kp);
+            if (uniform_copy(z0) == 6) p = group(IntC<6>{}, p, kp);
+            if (uniform_copy(z0) == 7) p = group(IntC<7>{}, p, kp);
+            if (uniform_copy(z0) == 8) p = group(IntC<8>{}, p, kp);
         }
-        if (p < np) step(p, da);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
