@@ -95,7 +95,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="3d_n128_m16m_f32_e5")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 21,
+    ap.add_argument("--cpu-sample", type=int, default=1 << 22,
                     help="points of the workload timed on the CPU oracle (0 = skip)")
     ap.add_argument("--method", type=int, default=0)
     ap.add_argument("--probe-copy", type=int, default=0,
