@@ -4,8 +4,9 @@
 // by the subproblem split of SM spreading (Sec. III-A "Step 1", chunks of at most `cap`
 // consecutive sorted points of one bin).
 //
-// gfx950 design: the permutation is a least-significant-digit radix sort on the bin key,
-// 8 bits per pass.  Each pass is (1) a per-workgroup digit histogram in LDS (integer LDS
+// gfx950 design: the permutation is a least-significant-digit radix sort on the bin key, at
+// most 8 bits per pass, the key's bits spread evenly over the passes (fewer digits per pass
+// give longer runs per digit in the scatter, so fuller memory transactions).  Each pass is (1) a per-workgroup digit histogram in LDS (integer LDS
 // atomics), (2) an exclusive scan over digit-major histograms, (3) a stable scatter that ranks
 // equal digits inside a wavefront with 64-bit ballots and across the four wavefronts of a
 // workgroup through LDS counters.  Every pass is stable, so points keep their original order
@@ -169,8 +170,9 @@ hipError_t exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* s
 // Radix sort passes
 // ------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(kBlock) k_radix_hist(const int32_t* __restrict__ keys, int64_t M,
-                                                        int shift, int64_t ntiles,
+                                                        int shift, int bits, int64_t ntiles,
                                                         int32_t* __restrict__ hist) {
+    const int mask = (1 << bits) - 1;
     __shared__ int32_t h[kRadix];
     for (int i = threadIdx.x; i < kRadix; i += kBlock) h[i] = 0;
     __syncthreads();
@@ -178,10 +180,10 @@ __global__ void __launch_bounds__(kBlock) k_radix_hist(const int32_t* __restrict
 #pragma unroll 4
     for (int r = 0; r < kItems; ++r) {
         int64_t idx = base + (int64_t)r * kBlock + threadIdx.x;
-        if (idx < M) atomicAdd(&h[(keys[idx] >> shift) & (kRadix - 1)], 1);
+        if (idx < M) atomicAdd(&h[(keys[idx] >> shift) & mask], 1);
     }
     __syncthreads();
-    for (int d = threadIdx.x; d < kRadix; d += kBlock) hist[(int64_t)d * ntiles + blockIdx.x] = h[d];
+    for (int d = threadIdx.x; d <= mask; d += kBlock) hist[(int64_t)d * ntiles + blockIdx.x] = h[d];
 }
 
 template <typename T, int NP>
@@ -203,9 +205,10 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
                                                            const int32_t* __restrict__ vals_in,
                                                            int32_t* __restrict__ keys_out,
                                                            int32_t* __restrict__ vals_out,
-                                                           int64_t M, int shift, int64_t ntiles,
+                                                           int64_t M, int shift, int bits, int64_t ntiles,
                                                            const int32_t* __restrict__ offs,
                                                            Payload<T, NP> pl) {
+    const int mask = (1 << bits) - 1;
     constexpr int kWaves = kBlock / 64;
     constexpr int kChunk = kItems * 64;                  // keys per wavefront
     __shared__ int32_t cnt[kWaves][kRadix];             // per-wavefront digit counts, then offsets
@@ -239,10 +242,11 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
         const bool valid = wv * kChunk + r * 64 + lane < count;
-        const int digit = (keys[r] >> shift) & (kRadix - 1);
+        const int digit = (keys[r] >> shift) & mask;
         uint64_t peers = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
+            if (b >= bits) break;
             const bool bit = (digit >> b) & 1;
             const uint64_t m = __ballot(bit);
             peers &= bit ? m : ~m;
@@ -275,7 +279,7 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
         int32_t run = inc - tot;
         for (int i = 0; i < wv; ++i) run += wsum[i];
         tbase[d] = run;
-        gbase[d] = offs[(int64_t)d * ntiles + blockIdx.x];
+        gbase[d] = (d <= mask) ? offs[(int64_t)d * ntiles + blockIdx.x] : 0;
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) {
             cnt[i][d] = run;
@@ -286,7 +290,7 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
         if (wv * kChunk + r * 64 + lane < count) {
-            const int digit = (keys[r] >> shift) & (kRadix - 1);
+            const int digit = (keys[r] >> shift) & mask;
             const int pos = cnt[wv][digit] + rank[r];
             sk[pos] = keys[r];
             sv[pos] = vals[r];
@@ -298,7 +302,7 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
     // write out: position i of the reordered tile goes to gbase[digit] + (i - tbase[digit])
     for (int i = tid; i < count; i += kBlock) {
         const int32_t key = sk[i];
-        const int digit = (key >> shift) & (kRadix - 1);
+        const int digit = (key >> shift) & mask;
         const int64_t pos = (int64_t)gbase[digit] + (i - tbase[digit]);
         keys_out[pos] = key;
         vals_out[pos] = sv[i];
@@ -406,15 +410,17 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
             else k_bin_keys<double, 3><<<g, kBlock, 0, st>>>(a, keysA, valsA, bad_dev);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        int passes = (a.nbits + kRadixBits - 1) / kRadixBits;
+        const int passes = (a.nbits + kRadixBits - 1) / kRadixBits;
+        int shift = 0;
         int32_t *ki = keysA, *vi = valsA, *ko = keysB, *vo = valsB;
         const size_t rs = a.prec == 0 ? 4 : 8;
         char* ctmp = base + L.coords;
         for (int p = 0; p < passes; ++p) {
-            int shift = p * kRadixBits;
+            // the remaining bits spread evenly over the remaining passes
+            const int bits = (a.nbits - shift + (passes - p) - 1) / (passes - p);
             dim3 gt((unsigned)L.ntiles);
-            k_radix_hist<<<gt, kBlock, 0, st>>>(ki, M, shift, L.ntiles, hist);
-            if ((e = exclusive_scan(hist, hscan, (int64_t)kRadix * L.ntiles, stmp, st)) != hipSuccess)
+            k_radix_hist<<<gt, kBlock, 0, st>>>(ki, M, shift, bits, L.ntiles, hist);
+            if ((e = exclusive_scan(hist, hscan, ((int64_t)1 << bits) * L.ntiles, stmp, st)) != hipSuccess)
                 return e;
             // coordinates: caller's arrays -> ... -> sorted output; the last pass writes xs_out
             const bool last = (p == passes - 1);
@@ -433,9 +439,9 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
                 if (a.dim == 2) {
                     Payload<float, 2> p2{};
                     for (int d = 0; d < 2; ++d) { p2.in[d] = pl.in[d]; p2.out[d] = pl.out[d]; }
-                    k_radix_scatter<float, 2><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan, p2);
+                    k_radix_scatter<float, 2><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
                 } else {
-                    k_radix_scatter<float, 3><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan, pl);
+                    k_radix_scatter<float, 3><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
                 }
             } else {
                 Payload<double, 3> pl{};
@@ -443,14 +449,15 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
                 if (a.dim == 2) {
                     Payload<double, 2> p2{};
                     for (int d = 0; d < 2; ++d) { p2.in[d] = pl.in[d]; p2.out[d] = pl.out[d]; }
-                    k_radix_scatter<double, 2><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan, p2);
+                    k_radix_scatter<double, 2><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
                 } else {
-                    k_radix_scatter<double, 3><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, L.ntiles, hscan, pl);
+                    k_radix_scatter<double, 3><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
                 }
             }
             if ((e = hipGetLastError()) != hipSuccess) return e;
             std::swap(ki, ko);
             std::swap(vi, vo);
+            shift += bits;
         }
         if (passes == 0) {
             // a single bin: the order is unchanged
