@@ -233,8 +233,10 @@ struct ColStage {
     using C = ColCfg<T, W>;
     T kz[C::kPiece][C::kWZ];
     cplx<T> cv[C::kPiece];
-    T kx[C::kPiece][C::kB];       // x weights placed in the point's block window (zero elsewhere)
-    T ky[C::kPiece][C::kB];
+    // x and y weights placed in the point's block window (zero elsewhere); the odd row pitch puts
+    // the staging lanes' stores on distinct banks
+    T kx[C::kPiece][C::kB | 1];
+    T ky[C::kPiece][C::kB | 1];
 };
 
 template <int V>
