@@ -189,10 +189,10 @@ void default_bins(nufft_plan p, int* m) {
             for (auto& c : c3) {
                 if (pass == 1 && c[0] > 16) continue;   // the point-patch kernel keeps 16 x 16 x 8
                 int mm[3] = {c[0], c[1], c[2]};
+                // the column kernel's fp64 bin (z pitch >= depth) also covers the interpolation tile
                 const size_t need = (pass == 0) ? nufft::spread_col_lds_bytes(p->prec, p->w, mm)
                                                 : nufft::spread_tile_bytes(p->prec, 3, p->w, mm);
-                if (need > 0 && need <= nufft::spread_lds_limit() &&
-                    nufft::spread_tile_bytes(p->prec, 3, p->w, mm) <= nufft::spread_lds_limit()) {
+                if (need > 0 && need <= nufft::spread_lds_limit()) {
                     m[0] = c[0];
                     m[1] = c[1];
                     m[2] = c[2];
@@ -418,27 +418,30 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
         plan->m[i] = i < dim ? (int)std::min<int64_t>(m[i], plan->n[i]) : 1;
         plan->nb[i] = (int)((plan->n[i] + plan->m[i] - 1) / plan->m[i]);
     }
-    if (nufft::spread_tile_bytes(plan->prec, dim, w, plan->m) > nufft::spread_lds_limit()) {
-        plan->last_error = "bin size too large for LDS";
-        nufft_destroy(plan);
-        return NUFFT_ERR_BAD_ARG;
-    }
     plan->nbins = (int64_t)plan->nb[0] * plan->nb[1] * plan->nb[2];
     // 3D spreading by column runs needs the points of a bin ordered by support column
     plan->colw = 0;
     plan->colstep = 1;
     plan->ncol = 1;
     const size_t col_lds = nufft::spread_col_lds_bytes(plan->prec, w, plan->m);
-    if (plan->method == NUFFT_METHOD_SM && nufft::spread_uses_columns(dim, w) && plan->m[2] == 8 &&
-        col_lds > 0 && col_lds <= nufft::spread_lds_limit()) {
-        const int step = nufft::spread_col_step(w);
-        const int64_t ncol = (int64_t)((plan->m[0] + step) / step) * ((plan->m[1] + step) / step) *
-                             (plan->m[2] + 1);
-        if (plan->nbins * ncol < (int64_t(1) << 31)) {
-            plan->colw = w;
-            plan->colstep = step;
-            plan->ncol = (int)ncol;
-        }
+    const int step = nufft::spread_col_step(w);
+    const int64_t ncol = (int64_t)((plan->m[0] + step) / step) * ((plan->m[1] + step) / step) *
+                         (plan->m[2] + 1);
+    const bool col_fits = plan->method == NUFFT_METHOD_SM && nufft::spread_uses_columns(dim, w) &&
+                          plan->m[2] == 8 && col_lds > 0 && col_lds <= nufft::spread_lds_limit() &&
+                          plan->nbins * ncol < (int64_t(1) << 31);
+    // the bins must fit the spreader this plan will run, and the interpolation tile
+    if ((!col_fits && plan->method == NUFFT_METHOD_SM &&
+         nufft::spread_tile_bytes(plan->prec, dim, w, plan->m) > nufft::spread_lds_limit()) ||
+        nufft::interp_tile_bytes(plan->prec, dim, w, plan->m) > nufft::spread_lds_limit()) {
+        plan->last_error = "bin size too large for LDS";
+        nufft_destroy(plan);
+        return NUFFT_ERR_BAD_ARG;
+    }
+    if (col_fits) {
+        plan->colw = w;
+        plan->colstep = step;
+        plan->ncol = (int)ncol;
     }
     plan->nbits = bit_length(plan->nbins * plan->ncol - 1);
     int64_t vol = (int64_t)plan->m[0] * plan->m[1] * plan->m[2];

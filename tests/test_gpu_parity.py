@@ -349,3 +349,35 @@ def test_execute_adjoint_matches_oracle(nf, orc, wl):
         st = p.stage_times()
         assert st["sort"] > 0 and st["spread"] > 0 and st["interp"] > 0 and st["fft1"] > 0 and st["fft2"] > 0
         p.destroy()
+
+
+# ---------------------------------------------------------------------------------------------
+# The 3D column-run spreader at every kernel width it serves
+# ---------------------------------------------------------------------------------------------
+
+COLUMN_CASES = [("f32", 1e-4), ("f32", 1e-6), ("f32", 1e-7)] + \
+               [("f64", e) for e in (1e-4, 1e-5, 1e-6, 1e-7, 1e-8, 1e-10, 1e-11)]
+
+
+@pytest.mark.parametrize("prec,eps", COLUMN_CASES, ids=[f"{p}_{e:g}" for p, e in COLUMN_CASES])
+def test_column_kernel_widths(nf, orc, prec, eps):
+    """3D plans whose kernel width selects the column-run spreader (w = 5..12): the plan reports the
+    column order, and type 1 plus the adjoint type 2 on the same sorted points match the oracle."""
+    N = (20, 18, 16)
+    wl = Workload("col", 3, N, 12_000, eps, prec, seed=81)
+    _announce(f"column widths {prec} eps={eps}")
+    inp = make_inputs(wl)
+    cd = cdtype(prec)
+    p = nf.Plan(1, N, eps, prec)
+    info = p.info()
+    assert info["colw"] == info["w"] and info["colstep"] >= 1, info
+    p.setpts(*[to_dev(x) for x in inp["X"]])
+    f = torch.empty(tuple(reversed(N)), dtype=cd, device=dev())
+    c = torch.empty(wl.M, dtype=cd, device=dev())
+    p.execute(to_dev(inp["c"]), f)
+    p.execute_adjoint(c, to_dev(inp["f"]))
+    torch.cuda.synchronize()
+    p.destroy()
+    e1 = orc.rel_l2(f.cpu().numpy(), orc.nufft_type1(inp["X"], inp["c"], N, eps))
+    e2 = orc.rel_l2(c.cpu().numpy(), orc.nufft_type2(inp["X"], inp["f"], N, eps))
+    assert e1 <= tol_for(prec) and e2 <= tol_for(prec), (info["w"], e1, e2)
