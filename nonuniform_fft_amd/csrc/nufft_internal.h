@@ -179,13 +179,16 @@ struct GeomArgs {
     int64_t M;
     const void* xs[3];     // sorted coordinates
     const int32_t* perm;
+    const int32_t* cperm;  // spreading reads strength cperm[j] for sorted point j; null: c is sorted
     const int32_t* sub;    // (bin, start, len)
     int64_t nsub;
 };
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // columns: the points of each bin are in column order (3D), so the column-run kernel may run.
+// c_scratch: device scratch of at least M complex values (fp64 plans gather c into it in sorted
+// order before spreading).
 hipError_t launch_spread(int prec, int method, const GeomArgs& g, const void* c, void* grid,
-                         hipStream_t st, bool columns);
+                         hipStream_t st, bool columns, void* c_scratch);
 hipError_t launch_interp(int prec, int method, const GeomArgs& g, const void* grid, void* c,
                          hipStream_t st);
 size_t interp_tile_bytes(int prec, int dim, int w, const int* m);

@@ -220,6 +220,7 @@ nufft::GeomArgs geom(const nufft_plan p) {
     for (int i = 0; i < p->dim; ++i)
         g.xs[i] = (const char*)p->xs.p + (size_t)i * (size_t)std::max<int64_t>(p->M, 0) * real_size(p);
     g.perm = (const int32_t*)p->perm.p;
+    g.cperm = g.perm;
     g.sub = (const int32_t*)p->sub.p;
     g.nsub = p->nsub;
     return g;
@@ -283,7 +284,8 @@ int run_type1(nufft_plan plan, const void* c, void* f) {
     record(plan, EV_T1 + 0);
     NUFFT_HIP(nufft::launch_fill_zero(plan->grid.p, gbytes, plan->stream));
     record(plan, EV_T1 + 1);
-    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, plan->grid.p, plan->stream, plan->colw > 0));
+    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, plan->grid.p, plan->stream, plan->colw > 0,
+                                   plan->sort_tmp.p));
     record(plan, EV_T1 + 2);
     if ((rc = fft_exec(plan, plan->fft_fwd, plan->grid.p)) != NUFFT_OK) return rc;
     record(plan, EV_T1 + 3);
@@ -631,7 +633,8 @@ int nufft_spread(nufft_plan plan, const void* c, void* grid) {
     if (!grid || (plan->M > 0 && !c)) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
     nufft::GeomArgs g = geom(plan);
     NUFFT_HIP(nufft::launch_fill_zero(grid, (size_t)grid_cells(plan) * 2 * real_size(plan), plan->stream));
-    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, grid, plan->stream, plan->colw > 0));
+    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, grid, plan->stream, plan->colw > 0,
+                                   plan->sort_tmp.p));
     return NUFFT_OK;
 }
 

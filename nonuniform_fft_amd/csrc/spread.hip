@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
             }
             if (i == 0) {
                 st->l0[p].x = l0;
-                st->cv[p] = c[g.perm[j]];
+                st->cv[p] = c[g.cperm ? g.cperm[j] : j];
             } else if (i == 1) {
                 st->l0[p].y = l0;
             } else {
@@ -266,6 +266,28 @@ __device__ __forceinline__ void col_acc(A (&are)[Z], A (&aim)[Z], const A (&kz)[
     }
 }
 
+// One point's operands for a lane of a column block: its x and y window weights, the z weights
+// and the strength, read from a stage.
+template <typename T, int W>
+struct ColPt {
+    cplx<T> cv;
+    T kx, ky;
+    T kz[W];
+    template <typename Stage>
+    __device__ __forceinline__ void load(const Stage& st, int p, int q1, int q2) {
+        cv = st.cv[p];
+        kx = st.kx[p][q1];
+        ky = st.ky[p][q2];
+#pragma unroll
+        for (int q = 0; q < W; ++q) kz[q] = st.kz[p][q];
+    }
+    template <int Z, int Z0>
+    __device__ __forceinline__ void add(T (&are)[Z], T (&aim)[Z]) const {
+        const T wxy = kx * ky;
+        col_acc<W, Z, Z0>(are, aim, kz, cv.re * wxy, cv.im * wxy);
+    }
+};
+
 template <typename T, int W>
 __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
                                                                      cplx<T>* __restrict__ grid, int p1, int p2) {
@@ -334,7 +356,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
     if (lane < min(PIECE, b - a) * 3) {
         const int64_t j = (int64_t)start + a + sp;
         xr = ((const T*)g.xs[si])[j];
-        if (si == 0) cr = c[g.perm[j]];
+        if (si == 0) cr = c[g.cperm ? g.cperm[j] : j];
     }
     for (int p0 = a; p0 < b; p0 += PIECE) {
         const int np = min(PIECE, b - p0);
@@ -371,7 +393,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
             if (lane < min(PIECE, b - pn) * 3) {
                 const int64_t j = (int64_t)start + pn + sp;
                 xr = ((const T*)g.xs[si])[j];
-                if (si == 0) cr = c[g.perm[j]];
+                if (si == 0) cr = c[g.cperm ? g.cperm[j] : j];
             }
         }
         // the staged piece is written and read by this wavefront only
@@ -382,13 +404,10 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
         // start covers a whole group, whose points then cost only their loads and 2 w FMAs.
         auto group = [&](auto z0c, int p, int kp) -> int {
             constexpr int Z0 = decltype(z0c)::value;
+            ColPt<T, W> A;
             do {
-                const cplx<T> cv = ws->cv[p];
-                const T wxy = ws->kx[p][q1] * ws->ky[p][q2];
-                T kz[W];
-#pragma unroll
-                for (int q = 0; q < W; ++q) kz[q] = ws->kz[p][q];
-                col_acc<W, Z, Z0>(are, aim, kz, cv.re * wxy, cv.im * wxy);
+                A.load(*ws, p, q1, q2);
+                A.template add<Z, Z0>(are, aim);
                 ++p;
             } while (p < np && __builtin_amdgcn_readlane(key, 3 * p) == kp);
             return p;
@@ -456,10 +475,257 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// Column runs with workgroup staging (fp64 plans).
+//
+// The same register-line accumulation, but the per-point weights are computed once per
+// workgroup with one lane per weight: a piece holds the next kWgPiece points of every slice,
+// every thread evaluates one (slice, point, dimension, q) weight, and a workgroup barrier hands
+// the piece to the slices' wavefronts.  fp64 exp and sqrt are long instruction sequences, so
+// evaluating each weight once, on full wavefronts, matters more than the barrier: with
+// per-wavefront staging only 3 lanes per point work, and the wavefronts of a slice (two or
+// three at these widths) repeat each other's work.  The stage is double-buffered (one barrier
+// per piece) and the raw coordinates and strengths of the piece after next are loaded into
+// registers while the current one is consumed.  The strengths must arrive in sorted order.
+// ------------------------------------------------------------------------------------------
+template <typename T, int W>
+struct WgStage {
+    using C = ColCfg<T, W>;
+    static constexpr int kPiece = 8;
+    T kz[kPiece][C::kWZ];
+    cplx<T> cv[kPiece];
+    T kx[kPiece][C::kB | 1];
+    T ky[kPiece][C::kB | 1];
+    int kp[kPiece][4];           // x block, y block, z start
+};
+
+template <typename T, int W>
+__global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g, const cplx<T>* __restrict__ c,
+                                                                        cplx<T>* __restrict__ grid, int p1, int p2) {
+    using C = ColCfg<T, W>;
+    using St = WgStage<T, W>;
+    constexpr int Z = C::kZ;
+    constexpr int PZ = C::kPZ;
+    constexpr int B = C::kB;
+    constexpr int S = C::kS;
+    constexpr int SW = C::kSlotWaves;
+    constexpr int SLICES = C::kWaves / SW;
+    constexpr int PIECE = St::kPiece;
+    constexpr int BLOCK = C::kBlock;
+    constexpr int ITEMS = SLICES * PIECE * 3 * W;              // weights per piece
+    constexpr int IT = (ITEMS + BLOCK - 1) / BLOCK;            // weights per thread per piece
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int PL = p1 * p2 * PZ;
+    double* tre = (double*)smem;             // real and imaginary planes, cell (x + y p1) pz + z
+    double* tim = tre + PL;
+    St* stages = (St*)(tim + PL);            // [2][SLICES]
+
+    const int sid = blockIdx.x;
+    const int bin = g.sub[3 * sid + 0];
+    const int start = g.sub[3 * sid + 1];
+    const int len = g.sub[3 * sid + 2];
+    int origin[3];
+    {
+        int b0 = bin % g.nb[0];
+        int b1 = (bin / g.nb[0]) % g.nb[1];
+        int b2 = bin / (g.nb[0] * g.nb[1]);
+        origin[0] = b0 * g.m[0] - W / 2;
+        origin[1] = b1 * g.m[1] - W / 2;
+        origin[2] = b2 * g.m[2] - W / 2;
+    }
+    const int pd[3] = {p1, p2, Z};
+    for (int k = threadIdx.x; k < 2 * PL; k += BLOCK) tre[k] = 0.0;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int slice = wave / SW, sub_wave = wave - slice * SW;
+    const int slot = sub_wave * 64 + lane;
+    const bool valid = (slot < B * B) && (slice < SLICES);
+    const int q2 = valid ? slot / B : 0;
+    const int q1 = valid ? slot - q2 * B : 0;
+    const int per = (len + SLICES - 1) / SLICES;      // points per slice (the last may have fewer)
+    const int npieces = (per + PIECE - 1) / PIECE;    // the same for every wavefront
+    const T beta = (T)g.beta;
+
+    // this thread's staging items: (slice, point, dimension, q), and their raw inputs (the
+    // strengths arrive in sorted order)
+    T xr[IT];
+    cplx<T> cr[IT];
+    auto item_point = [&](int it, int k, int& s_, int& p_, int& d_, int& q_) -> int64_t {
+        const int i = threadIdx.x + it * BLOCK;
+        if (i >= ITEMS) return -1;
+        q_ = i % W;
+        int r = i / W;
+        d_ = r % 3;
+        r /= 3;
+        p_ = r % PIECE;
+        s_ = r / PIECE;
+        const int ps = s_ * per + k * PIECE + p_;              // point index in the subproblem
+        if (k * PIECE + p_ >= per || ps >= len) return -1;
+        return (int64_t)start + ps;
+    };
+    auto fetch = [&](int k) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            int s_, p_, d_, q_;
+            const int64_t j = item_point(it, k, s_, p_, d_, q_);
+            if (j >= 0) {
+                xr[it] = ((const T*)g.xs[d_])[j];
+                if (d_ == 0 && q_ == 0) cr[it] = c[j];
+            }
+        }
+    };
+    auto stage = [&](int k, St* buf) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            int s_, p_, d_, q_;
+            const int64_t j = item_point(it, k, s_, p_, d_, q_);
+            if (j < 0) continue;
+            St& st = buf[s_];
+            double tt = grid_t((double)xr[it], g.s[d_]);
+            int l;
+            fold_t(tt, g.n[d_], l);
+            // the weight for offset q of eq. (8), as in es_weights
+            const double l0d = ceil(__dsub_rn(tt, 0.5 * (double)W));
+            const T delta = (T)__dsub_rn(l0d, tt);
+            const T zq = (delta + (T)q_) * ((T)2 / (T)W);
+            const T zz = zq * zq;
+            T phi;
+            if constexpr (sizeof(T) == 4)
+                phi = (zz <= 1.0f) ? __expf(beta * (__builtin_amdgcn_sqrtf(1.0f - zz) - 1.0f)) : 0.0f;
+            else
+                phi = (zz <= (T)1) ? exp(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
+            int l0 = (int)l0d - origin[d_];
+            l0 = min(max(l0, 0), pd[d_] - W);
+            if (d_ < 2) {
+                const int blk = l0 / S;
+                const int off = l0 - blk * S;
+                T* win = (d_ == 0) ? st.kx[p_] : st.ky[p_];
+                win[off + q_] = phi;
+                if (q_ < B - W) win[q_ < off ? q_ : q_ + W] = (T)0;
+                if (q_ == 0) st.kp[p_][d_] = blk;
+                if (d_ == 0 && q_ == 0) st.cv[p_] = cr[it];
+            } else {
+                st.kz[p_][q_] = phi;
+                if (q_ == 0) st.kp[p_][2] = l0;
+            }
+        }
+    };
+
+    T are[Z], aim[Z];
+#pragma unroll
+    for (int z = 0; z < Z; ++z) {
+        are[z] = (T)0;
+        aim[z] = (T)0;
+    }
+    int cur = -1, cell = 0;
+    bool live = false;
+
+    fetch(0);
+    stage(0, stages);
+    fetch(1);
+    __syncthreads();
+    for (int k = 0; k < npieces; ++k) {
+        St* now = stages + (k & 1) * SLICES;
+        if (k + 1 < npieces) {
+            stage(k + 1, stages + ((k + 1) & 1) * SLICES);
+            fetch(k + 2);
+        }
+        const int p0 = slice * per + k * PIECE;
+        const int np = (slice < SLICES) ? max(0, min(PIECE, min(len, slice * per + per) - p0)) : 0;
+        if (np > 0) {
+            const St& ws = now[slice];
+            int key = 0;
+            if (lane < np) key = ws.kp[lane][0] | (ws.kp[lane][1] << 8) | (ws.kp[lane][2] << 16);
+            auto group = [&](auto z0c, int p, int kp) -> int {
+                constexpr int Z0 = decltype(z0c)::value;
+                ColPt<T, W> A, Bp;
+                A.load(ws, p, q1, q2);
+                while (true) {
+                    const bool m1 = p + 1 < np && __builtin_amdgcn_readlane(key, p + 1) == kp;
+                    if (m1) Bp.load(ws, p + 1, q1, q2);
+                    A.template add<Z, Z0>(are, aim);
+                    ++p;
+                    if (!m1) break;
+                    const bool m2 = p + 1 < np && __builtin_amdgcn_readlane(key, p + 1) == kp;
+                    if (m2) A.load(ws, p + 1, q1, q2);
+                    Bp.template add<Z, Z0>(are, aim);
+                    ++p;
+                    if (!m2) break;
+                }
+                return p;
+            };
+            int p = 0;
+            while (p < np) {
+                const int kp = __builtin_amdgcn_readlane(key, p);
+                const int col = kp & 0xffff;
+                if (col != cur) {
+                    if (cur >= 0 && live) {
+#pragma unroll
+                        for (int z = 0; z < Z; ++z) {
+                            atomicAdd(tre + cell + z, (double)are[z]);
+                            atomicAdd(tim + cell + z, (double)aim[z]);
+                        }
+                    }
+#pragma unroll
+                    for (int z = 0; z < Z; ++z) {
+                        zero_in_place(are[z]);
+                        zero_in_place(aim[z]);
+                    }
+                    cur = col;
+                    const int cx = (col & 0xff) * S + q1, cy = (col >> 8) * S + q2;
+                    live = valid && cx < p1 && cy < p2;
+                    cell = (cx + cy * p1) * PZ;
+                }
+                const int z0 = kp >> 16;
+                if (uniform_copy(z0) == 0) p = group(IntC<0>{}, p, kp);
+                if (uniform_copy(z0) == 1) p = group(IntC<1>{}, p, kp);
+                if (uniform_copy(z0) == 2) p = group(IntC<2>{}, p, kp);
+                if (uniform_copy(z0) == 3) p = group(IntC<3>{}, p, kp);
+                if (uniform_copy(z0) == 4) p = group(IntC<4>{}, p, kp);
+                if (uniform_copy(z0) == 5) p = group(IntC<5>{}, p, kp);
+                if (uniform_copy(z0) == 6) p = group(IntC<6>{}, p, kp);
+                if (uniform_copy(z0) == 7) p = group(IntC<7>{}, p, kp);
+                if (uniform_copy(z0) == 8) p = group(IntC<8>{}, p, kp);
+            }
+        }
+        // piece k + 1 is staged and piece k consumed before either buffer is reused
+        __syncthreads();
+    }
+    if (cur >= 0 && live) {
+#pragma unroll
+        for (int z = 0; z < Z; ++z) {
+            atomicAdd(tre + cell + z, (double)are[z]);
+            atomicAdd(tim + cell + z, (double)aim[z]);
+        }
+    }
+    __syncthreads();
+    // add the padded bin to the fine grid with periodic wrap (eq. (15))
+    const int P = p1 * p2 * Z;
+    CellWalk cw(threadIdx.x, BLOCK, p1, p2);
+    for (int k = threadIdx.x; k < P; k += BLOCK, cw.next()) {
+        const int li = (cw.s1 + cw.s2 * p1) * PZ + cw.s3;
+        const double re = tre[li], im = tim[li];
+        if (re == 0.0 && im == 0.0) continue;
+        const int g1 = wrap_grid(origin[0] + cw.s1, g.n[0]);
+        const int g2 = wrap_grid(origin[1] + cw.s2, g.n[1]);
+        const int g3 = wrap_grid(origin[2] + cw.s3, g.n[2]);
+        const size_t gi = (size_t)g1 + (size_t)g.n[0] * ((size_t)g2 + (size_t)g.n[1] * (size_t)g3);
+        unsafeAtomicAdd(&grid[gi].re, (T)re);
+        unsafeAtomicAdd(&grid[gi].im, (T)im);
+    }
+}
+
+// fp64 plans stage per workgroup; fp32 plans per wavefront
+template <typename T>
+constexpr bool kWgStaging = sizeof(T) == 8;
+
 template <typename T, int W>
 size_t col_lds_bytes(const int* m) {
     using C = ColCfg<T, W>;
-    return (size_t)(m[0] + W) * (m[1] + W) * C::kPZ * 2 * sizeof(double) + sizeof(ColStage<T, W>) * C::kWaves;
+    const size_t tile = (size_t)(m[0] + W) * (m[1] + W) * C::kPZ * 2 * sizeof(double);
+    if constexpr (kWgStaging<T>)
+        return tile + sizeof(WgStage<T, W>) * 2 * (C::kWaves / C::kSlotWaves);
+    return tile + sizeof(ColStage<T, W>) * C::kWaves;
 }
 
 size_t col_lds_bytes_rt(int prec, int w, const int* m) {
@@ -479,15 +745,19 @@ hipError_t spread_col_w(const GeomArgs& g, const void* c, void* grid, hipStream_
     const int p1 = g.m[0] + W, p2 = g.m[1] + W;
     const size_t lds = col_lds_bytes<T, W>(g.m);
     if (lds > spread_lds_limit()) return hipErrorInvalidConfiguration;
+    const void* fn = kWgStaging<T> ? (const void*)k_spread_col_wg<T, W> : (const void*)k_spread_col<T, W>;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_spread_col<T, W>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)spread_lds_limit());
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)spread_lds_limit());
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_spread_col<T, W><<<dim3((unsigned)g.nsub), ColCfg<T, W>::kBlock, lds, st>>>(
-        g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2);
+    if constexpr (kWgStaging<T>)
+        k_spread_col_wg<T, W><<<dim3((unsigned)g.nsub), ColCfg<T, W>::kBlock, lds, st>>>(
+            g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2);
+    else
+        k_spread_col<T, W><<<dim3((unsigned)g.nsub), ColCfg<T, W>::kBlock, lds, st>>>(
+            g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2);
     return hipGetLastError();
 }
 
@@ -523,7 +793,7 @@ __global__ void __launch_bounds__(kGmBlock) k_spread_gm(GeomArgs g, const cplx<T
             idx[d][q] = v;
         }
     }
-    const cplx<T> v = c[g.perm[i]];
+    const cplx<T> v = c[g.cperm ? g.cperm[i] : i];
     const int n1 = g.n[0], n2 = g.n[1];
 #pragma unroll
     for (int q3 = 0; q3 < (DIM == 3 ? W : 1); ++q3) {
@@ -543,6 +813,13 @@ __global__ void __launch_bounds__(kGmBlock) k_spread_gm(GeomArgs g, const cplx<T
             }
         }
     }
+}
+
+// cs[i] = c[perm[i]]: the strengths in the bin-sorted order the spreading kernels walk.
+__global__ void __launch_bounds__(256) k_gather_c(const int32_t* __restrict__ perm, const cplx<double>* __restrict__ c,
+                                                  cplx<double>* __restrict__ cs, int64_t M) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < M) cs[i] = c[perm[i]];
 }
 
 __global__ void k_fill_zero(uint4* __restrict__ p, size_t n16) {
@@ -636,8 +913,21 @@ size_t spread_col_lds_bytes(int prec, int w, const int* m) {
     return col_lds_bytes_rt(prec, w, m);
 }
 
-hipError_t launch_spread(int prec, int method, const GeomArgs& g, const void* c, void* grid,
-                         hipStream_t st, bool columns) {
+hipError_t launch_spread(int prec, int method, const GeomArgs& g_in, const void* c_in, void* grid,
+                         hipStream_t st, bool columns, void* c_scratch) {
+    // fp64 plans put the strengths in sorted order first, with a streaming gather: their
+    // spreading kernels run two wavefronts per SIMD and cannot hide the dependent perm -> c
+    // loads of large point sets (fp32 plans hide them, and the extra pass would cost more)
+    GeomArgs g = g_in;
+    const void* c = c_in;
+    if (prec == 1 && g.M > 0) {
+        k_gather_c<<<(unsigned)((g.M + 255) / 256), 256, 0, st>>>(g.perm, (const cplx<double>*)c_in,
+                                                                   (cplx<double>*)c_scratch, g.M);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g.cperm = nullptr;
+        c = c_scratch;
+    }
     if (columns && method != NUFFT_METHOD_GM_SORT)
         return prec == 0 ? spread_col<float>(g, c, grid, st) : spread_col<double>(g, c, grid, st);
     if (prec == 0) return g.dim == 2 ? spread_dim<float, 2>(method, g, c, grid, st)
