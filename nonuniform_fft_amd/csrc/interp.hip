@@ -89,6 +89,15 @@ __global__ void __launch_bounds__(kInterpSmBlock) k_interp_sm(GeomArgs g, const 
         origin[1] = b1 * g.m[1] - W / 2;
         if (DIM == 3) origin[2] = b2 * g.m[2] - W / 2;
     }
+    // the coordinates of this thread's first point are requested before the tile copy, and
+    // each later point's one iteration ahead, so their latency overlaps other work
+    T xn[DIM];
+    int32_t on = 0;   // output index (original order) of the next point
+    if ((int)threadIdx.x < len) {
+#pragma unroll
+        for (int d = 0; d < DIM; ++d) xn[d] = ((const T*)g.xs[d])[(int64_t)start + threadIdx.x];
+        on = g.perm[(int64_t)start + threadIdx.x];
+    }
     // copy the padded bin (with periodic wrap) into LDS; consecutive lanes read consecutive x
     const int P = p1 * p2 * p3;
     for (int k = threadIdx.x; k < P; k += kInterpSmBlock) {
@@ -112,11 +121,20 @@ __global__ void __launch_bounds__(kInterpSmBlock) k_interp_sm(GeomArgs g, const 
     const int pd[3] = {p1, p2, p3};
     for (int i = threadIdx.x; i < len; i += kInterpSmBlock) {
         const int64_t j = (int64_t)start + i;
+        T xc[DIM];
+#pragma unroll
+        for (int d = 0; d < DIM; ++d) xc[d] = xn[d];
+        const int32_t oc = on;
+        if (i + kInterpSmBlock < len) {
+#pragma unroll
+            for (int d = 0; d < DIM; ++d) xn[d] = ((const T*)g.xs[d])[j + kInterpSmBlock];
+            on = g.perm[j + kInterpSmBlock];
+        }
         T ker[DIM][W];
         int l0[3] = {0, 0, 0};
 #pragma unroll
         for (int d = 0; d < DIM; ++d) {
-            double t = grid_t((double)((const T*)g.xs[d])[j], g.s[d]);
+            double t = grid_t((double)xc[d], g.s[d]);
             int l;
             fold_t(t, g.n[d], l);
             int v = es_weights<T, W>(t, beta, ker[d]) - origin[d];
@@ -146,7 +164,7 @@ __global__ void __launch_bounds__(kInterpSmBlock) k_interp_sm(GeomArgs g, const 
         cplx<T> out;
         out.re = are;
         out.im = aim;
-        c[g.perm[j]] = out;
+        c[oc] = out;
     }
 }
 

@@ -570,7 +570,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
             const int64_t j = item_point(it, k, s_, p_, d_, q_);
             if (j >= 0) {
                 xr[it] = ((const T*)g.xs[d_])[j];
-                if (d_ == 0 && q_ == 0) cr[it] = c[j];
+                if (d_ == 0 && q_ == 0) cr[it] = c[g.cperm ? g.cperm[j] : j];
             }
         }
     };
