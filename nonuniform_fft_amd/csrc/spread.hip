@@ -114,15 +114,29 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
     const bool active = p_first < PPP;
 
     const T beta = (T)g.beta;
+    // staging thread (point sp, dimension si): its raw coordinate and strength for the next
+    // chunk are requested while the current chunk is accumulated
+    const int sp = threadIdx.x / DIM, si = threadIdx.x - (threadIdx.x / DIM) * DIM;
+    T xr = (T)0;
+    cplx<T> cr;
+    cr.re = (T)0;
+    cr.im = (T)0;
+    auto fetch = [&](int c0) {
+        if (threadIdx.x < min(CH, len - c0) * DIM) {
+            const int64_t j = (int64_t)start + c0 + sp;
+            xr = ((const T*)g.xs[si])[j];
+            if (si == 0) cr = c[g.cperm ? g.cperm[j] : j];
+        }
+    };
+    fetch(0);
     for (int c0 = 0; c0 < len; c0 += CH) {
         const int np = min(CH, len - c0);
         __syncthreads();   // previous chunk consumed (and tile zeroed on the first round)
         // stage kernel weights: one thread per (point, dimension)
         if (threadIdx.x < np * DIM) {
-            const int p = threadIdx.x / DIM;
-            const int i = threadIdx.x - p * DIM;
-            const int64_t j = (int64_t)start + c0 + p;
-            double tt = grid_t((double)((const T*)g.xs[i])[j], g.s[i]);
+            const int p = sp;
+            const int i = si;
+            double tt = grid_t((double)xr, g.s[i]);
             int l;
             fold_t(tt, g.n[i], l);
             T ker[W];
@@ -137,13 +151,14 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
             }
             if (i == 0) {
                 st->l0[p].x = l0;
-                st->cv[p] = c[g.cperm ? g.cperm[j] : j];
+                st->cv[p] = cr;
             } else if (i == 1) {
                 st->l0[p].y = l0;
             } else {
                 st->l0[p].z = l0;
             }
         }
+        if (c0 + CH < len) fetch(c0 + CH);
         __syncthreads();
         if (active) {
             for (int p = p_first; p < np; p += PPP) {
@@ -745,7 +760,11 @@ hipError_t spread_col_w(const GeomArgs& g, const void* c, void* grid, hipStream_
     const int p1 = g.m[0] + W, p2 = g.m[1] + W;
     const size_t lds = col_lds_bytes<T, W>(g.m);
     if (lds > spread_lds_limit()) return hipErrorInvalidConfiguration;
-    const void* fn = kWgStaging<T> ? (const void*)k_spread_col_wg<T, W> : (const void*)k_spread_col<T, W>;
+    const void* fn;
+    if constexpr (kWgStaging<T>)
+        fn = (const void*)k_spread_col_wg<T, W>;
+    else
+        fn = (const void*)k_spread_col<T, W>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)spread_lds_limit());
