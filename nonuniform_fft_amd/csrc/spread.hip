@@ -363,16 +363,20 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
     const T beta = (T)g.beta;
     // staging lane (point sp, dimension si); the raw coordinate and strength of the next piece
     // are loaded into registers while the current piece is processed
+    // (the permutation entry that selects a strength is requested one piece earlier still)
     const int sp = lane / 3, si = lane - (lane / 3) * 3;
     T xr = (T)0;
     cplx<T> cr;
     cr.re = (T)0;
     cr.im = (T)0;
+    int32_t pr = 0;
+    auto perm_of = [&](int64_t j) -> int32_t { return g.cperm ? g.cperm[j] : (int32_t)j; };
     if (lane < min(PIECE, b - a) * 3) {
         const int64_t j = (int64_t)start + a + sp;
         xr = ((const T*)g.xs[si])[j];
-        if (si == 0) cr = c[g.cperm ? g.cperm[j] : j];
+        if (si == 0) cr = c[perm_of(j)];
     }
+    if (si == 0 && lane < min(PIECE, b - a - PIECE) * 3) pr = perm_of((int64_t)start + a + PIECE + sp);
     for (int p0 = a; p0 < b; p0 += PIECE) {
         const int np = min(PIECE, b - p0);
         int l0 = 0;
@@ -408,8 +412,9 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
             if (lane < min(PIECE, b - pn) * 3) {
                 const int64_t j = (int64_t)start + pn + sp;
                 xr = ((const T*)g.xs[si])[j];
-                if (si == 0) cr = c[g.cperm ? g.cperm[j] : j];
+                if (si == 0) cr = c[pr];
             }
+            if (si == 0 && lane < min(PIECE, b - pn - PIECE) * 3) pr = perm_of((int64_t)start + pn + PIECE + sp);
         }
         // the staged piece is written and read by this wavefront only
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
