@@ -17,7 +17,7 @@ namespace nufft {
 namespace {
 
 constexpr int kBlock = 256;                 // threads per workgroup (4 wavefronts)
-constexpr int kItems = 8;                   // keys per thread per sort tile
+constexpr int kItems = 16;                  // keys per thread per sort tile
 constexpr int kTile = kBlock * kItems;      // keys per sort tile
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
