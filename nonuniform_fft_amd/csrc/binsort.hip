@@ -31,7 +31,6 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ------------------------------------------------------------------------------------------
 template <typename T, int DIM>
 __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __restrict__ keys,
-                                                      int32_t* __restrict__ vals,
                                                       int* __restrict__ bad) {
     int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (j >= a.M) return;
@@ -65,7 +64,6 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
         atomicOr(bad, 1);
     }
     keys[j] = key;
-    vals[j] = (int32_t)j;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -117,7 +115,10 @@ __global__ void __launch_bounds__(kBlock) k_scan_tiles(const int32_t* __restrict
         if (base + i < n) out[base + i] = run;
         run += v[i];
     }
-    if (threadIdx.x == 0) tile_sums[blockIdx.x] = tot;
+    if (threadIdx.x == 0) {
+        tile_sums[blockIdx.x] = tot;
+        if (gridDim.x == 1) out[n] = tot;   // a one-tile scan writes its total here
+    }
 }
 
 __global__ void __launch_bounds__(kBlock) k_scan_add(int32_t* __restrict__ out, int64_t n,
@@ -127,6 +128,8 @@ __global__ void __launch_bounds__(kBlock) k_scan_add(int32_t* __restrict__ out, 
     for (int i = threadIdx.x; i < kScanTile; i += kBlock) {
         if (base + i < n) out[base + i] += add;
     }
+    // the scan of the tile sums ends with their total
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) out[n] = tile_pref[gridDim.x];
 }
 
 // Writes total of a scanned array: out[n] = out[n-1] + in[n-1] (or 0 for n == 0).
@@ -161,8 +164,9 @@ hipError_t exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* s
             if (e != hipSuccess) return e;
             k_scan_add<<<dim3((unsigned)tiles), dim3(kBlock), 0, st>>>(out, n, pref);
         }
+    } else {
+        k_scan_total<<<1, 64, 0, st>>>(in, out, n);
     }
-    k_scan_total<<<1, 64, 0, st>>>(in, out, n);
     return hipGetLastError();
 }
 
@@ -200,7 +204,8 @@ struct Payload {
 // ballots and wavefront-private digit counters, so ranking needs no workgroup barrier; the
 // per-digit counts of the four chunks are then combined into tile offsets, the tile is
 // reordered by digit in LDS, and each digit's run is written to consecutive addresses.
-template <typename T, int NP>
+// IDV: the values are the keys' positions (the first pass), so none are read.
+template <typename T, int NP, bool IDV>
 __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restrict__ keys_in,
                                                            const int32_t* __restrict__ vals_in,
                                                            int32_t* __restrict__ keys_out,
@@ -230,7 +235,10 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
         const int li = wv * kChunk + r * 64 + lane;
         const bool valid = li < count;
         keys[r] = valid ? keys_in[base + li] : 0;
-        vals[r] = valid ? vals_in[base + li] : 0;
+        if constexpr (IDV)
+            vals[r] = (int32_t)(base + li);
+        else
+            vals[r] = valid ? vals_in[base + li] : 0;
 #pragma unroll
         for (int d = 0; d < NP; ++d) cvs[r][d] = valid ? pl.in[d][base + li] : (T)0;
     }
@@ -403,16 +411,19 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
     if (M > 0) {
         dim3 g((unsigned)cdiv(M, kBlock));
         if (a.prec == 0) {
-            if (a.dim == 2) k_bin_keys<float, 2><<<g, kBlock, 0, st>>>(a, keysA, valsA, bad_dev);
-            else k_bin_keys<float, 3><<<g, kBlock, 0, st>>>(a, keysA, valsA, bad_dev);
+            if (a.dim == 2) k_bin_keys<float, 2><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
+            else k_bin_keys<float, 3><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
         } else {
-            if (a.dim == 2) k_bin_keys<double, 2><<<g, kBlock, 0, st>>>(a, keysA, valsA, bad_dev);
-            else k_bin_keys<double, 3><<<g, kBlock, 0, st>>>(a, keysA, valsA, bad_dev);
+            if (a.dim == 2) k_bin_keys<double, 2><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
+            else k_bin_keys<double, 3><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int passes = (a.nbits + kRadixBits - 1) / kRadixBits;
         int shift = 0;
-        int32_t *ki = keysA, *vi = valsA, *ko = keysB, *vo = valsB;
+        // values: the first pass generates the identity, the last writes the caller's perm, and
+        // the passes between alternate valsA / valsB
+        int32_t *ki = keysA, *ko = keysB;
+        int32_t* vbuf[2] = {valsA, valsB};
         const size_t rs = a.prec == 0 ? 4 : 8;
         char* ctmp = base + L.coords;
         for (int p = 0; p < passes; ++p) {
@@ -424,6 +435,8 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
                 return e;
             // coordinates: caller's arrays -> ... -> sorted output; the last pass writes xs_out
             const bool last = (p == passes - 1);
+            const int32_t* vi = (p == 0) ? nullptr : vbuf[(p - 1) & 1];
+            int32_t* vo = last ? perm : vbuf[p & 1];
             const bool to_tmp = ((passes - 1 - p) % 2) == 1;
             const void* cin[3];
             void* cout[3];
@@ -439,9 +452,11 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
                 if (a.dim == 2) {
                     Payload<float, 2> p2{};
                     for (int d = 0; d < 2; ++d) { p2.in[d] = pl.in[d]; p2.out[d] = pl.out[d]; }
-                    k_radix_scatter<float, 2><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
+                    if (vi) k_radix_scatter<float, 2, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
+                    else k_radix_scatter<float, 2, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
                 } else {
-                    k_radix_scatter<float, 3><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
+                    if (vi) k_radix_scatter<float, 3, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
+                    else k_radix_scatter<float, 3, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
                 }
             } else {
                 Payload<double, 3> pl{};
@@ -449,14 +464,15 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
                 if (a.dim == 2) {
                     Payload<double, 2> p2{};
                     for (int d = 0; d < 2; ++d) { p2.in[d] = pl.in[d]; p2.out[d] = pl.out[d]; }
-                    k_radix_scatter<double, 2><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
+                    if (vi) k_radix_scatter<double, 2, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
+                    else k_radix_scatter<double, 2, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
                 } else {
-                    k_radix_scatter<double, 3><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
+                    if (vi) k_radix_scatter<double, 3, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
+                    else k_radix_scatter<double, 3, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
                 }
             }
             if ((e = hipGetLastError()) != hipSuccess) return e;
             std::swap(ki, ko);
-            std::swap(vi, vo);
             shift += bits;
         }
         if (passes == 0) {
@@ -465,10 +481,9 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
                 if ((e = hipMemcpyAsync((char*)xs_out + (size_t)d * M * rs, a.x[d], M * rs, hipMemcpyDeviceToDevice,
                                         st)) != hipSuccess)
                     return e;
+            k_iota<<<dim3((unsigned)cdiv(M, kBlock)), kBlock, 0, st>>>(perm, M);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        if ((e = hipMemcpyAsync(perm, vi, sizeof(int32_t) * M, hipMemcpyDeviceToDevice, st)) !=
-            hipSuccess)
-            return e;
         k_bin_offsets<<<dim3((unsigned)cdiv(M + 1, kBlock)), kBlock, 0, st>>>(ki, M, a.nbins, a.ncol, offsets);
     } else {
         if ((e = hipMemsetAsync(offsets, 0, sizeof(int32_t) * (a.nbins + 1), st)) != hipSuccess)
