@@ -35,6 +35,7 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
     int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (j >= a.M) return;
     int bidx[3] = {0, 0, 0};
+    double tf[DIM];
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < DIM; ++i) {
@@ -42,6 +43,7 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
         double t = grid_t(x, a.s[i]);
         int l = 0;
         if (!fold_t(t, a.n[i], l)) { ok = false; l = 0; }
+        tf[i] = t;   // folded
         bidx[i] = l / a.m[i];
     }
     int key = bidx[0] + a.nb[0] * (bidx[1] + a.nb[1] * bidx[2]);
@@ -50,10 +52,7 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
         int lo[3];
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
-            double t = grid_t((double)((const T*)a.x[i])[j], a.s[i]);
-            int l = 0;
-            fold_t(t, a.n[i], l);
-            lo[i] = (int)ceil(__dsub_rn(t, 0.5 * (double)a.colw)) - (bidx[i] * a.m[i] - a.colw / 2);
+            lo[i] = (int)ceil(__dsub_rn(tf[i], 0.5 * (double)a.colw)) - (bidx[i] * a.m[i] - a.colw / 2);
             lo[i] = min(max(lo[i], 0), a.m[i]);
         }
         const int ncx = (a.m[0] + a.colstep) / a.colstep;
