@@ -228,7 +228,7 @@ __host__ __device__ constexpr int col_block_edge(int w) { return w <= 6 ? 8 : (w
 
 // register budget: fp64 z-lines need twice the registers per lane, so half the wavefronts
 template <typename T, int W>
-constexpr int kColBlock = (sizeof(T) == 4) ? 1024 : 512;
+constexpr int kColBlock = (sizeof(T) == 4) ? 1024 : 768;
 
 template <typename T, int W>
 struct ColCfg {
@@ -511,7 +511,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
 template <typename T, int W>
 struct WgStage {
     using C = ColCfg<T, W>;
-    static constexpr int kPiece = 8;
+    static constexpr int kPiece = 6;
     T kz[kPiece][C::kWZ];
     cplx<T> cv[kPiece];
     T kx[kPiece][C::kB | 1];
@@ -568,8 +568,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
 
     // this thread's staging items: (slice, point, dimension, q), and their raw inputs (the
     // strengths arrive in sorted order)
-    T xr[IT];
-    cplx<T> cr[IT];
+    T xr[IT], crr[IT], cri[IT];
     auto item_point = [&](int it, int k, int& s_, int& p_, int& d_, int& q_) -> int64_t {
         const int i = threadIdx.x + it * BLOCK;
         if (i >= ITEMS) return -1;
@@ -590,7 +589,11 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
             const int64_t j = item_point(it, k, s_, p_, d_, q_);
             if (j >= 0) {
                 xr[it] = ((const T*)g.xs[d_])[j];
-                if (d_ == 0 && q_ == 0) cr[it] = c[g.cperm ? g.cperm[j] : j];
+                if (d_ == 0 && q_ == 0) {
+                    const cplx<T> cv = c[g.cperm ? g.cperm[j] : j];
+                    crr[it] = cv.re;
+                    cri[it] = cv.im;
+                }
             }
         }
     };
@@ -623,7 +626,10 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
                 win[off + q_] = phi;
                 if (q_ < B - W) win[q_ < off ? q_ : q_ + W] = (T)0;
                 if (q_ == 0) st.kp[p_][d_] = blk;
-                if (d_ == 0 && q_ == 0) st.cv[p_] = cr[it];
+                if (d_ == 0 && q_ == 0) {
+                    st.cv[p_].re = crr[it];
+                    st.cv[p_].im = cri[it];
+                }
             } else {
                 st.kz[p_][q_] = phi;
                 if (q_ == 0) st.kp[p_][2] = l0;
@@ -658,20 +664,12 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
             if (lane < np) key = ws.kp[lane][0] | (ws.kp[lane][1] << 8) | (ws.kp[lane][2] << 16);
             auto group = [&](auto z0c, int p, int kp) -> int {
                 constexpr int Z0 = decltype(z0c)::value;
-                ColPt<T, W> A, Bp;
-                A.load(ws, p, q1, q2);
-                while (true) {
-                    const bool m1 = p + 1 < np && __builtin_amdgcn_readlane(key, p + 1) == kp;
-                    if (m1) Bp.load(ws, p + 1, q1, q2);
+                ColPt<T, W> A;
+                do {
+                    A.load(ws, p, q1, q2);
                     A.template add<Z, Z0>(are, aim);
                     ++p;
-                    if (!m1) break;
-                    const bool m2 = p + 1 < np && __builtin_amdgcn_readlane(key, p + 1) == kp;
-                    if (m2) A.load(ws, p + 1, q1, q2);
-                    Bp.template add<Z, Z0>(are, aim);
-                    ++p;
-                    if (!m2) break;
-                }
+                } while (p < np && __builtin_amdgcn_readlane(key, p) == kp);
                 return p;
             };
             int p = 0;
