@@ -65,12 +65,14 @@ __global__ void __launch_bounds__(kInterpBlock) k_interp_gm(GeomArgs g, const cp
     c[g.perm[i]] = out;
 }
 
-constexpr int kInterpSmBlock = 512;
+// 3D fp64 tiles leave room for one workgroup per CU: 768 lanes keep three wavefronts per SIMD
+template <typename T, int DIM>
+constexpr int kInterpSmBlock = (sizeof(T) == 8 && DIM == 3) ? 768 : 512;
 
 __host__ __device__ inline int interp_row_pitch(int p1) { return p1; }
 
 template <typename T, int DIM, int W>
-__global__ void __launch_bounds__(kInterpSmBlock) k_interp_sm(GeomArgs g, const cplx<T>* __restrict__ grid,
+__global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs g, const cplx<T>* __restrict__ grid,
                                                               cplx<T>* __restrict__ c, int p1, int p2,
                                                               int p3) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -100,7 +102,7 @@ __global__ void __launch_bounds__(kInterpSmBlock) k_interp_sm(GeomArgs g, const 
     }
     // copy the padded bin (with periodic wrap) into LDS; consecutive lanes read consecutive x
     const int P = p1 * p2 * p3;
-    for (int k = threadIdx.x; k < P; k += kInterpSmBlock) {
+    for (int k = threadIdx.x; k < P; k += (kInterpSmBlock<T, DIM>)) {
         const int s1 = k % p1;
         const int rest = k / p1;
         const int s2 = rest % p2;
@@ -119,16 +121,16 @@ __global__ void __launch_bounds__(kInterpSmBlock) k_interp_sm(GeomArgs g, const 
     __syncthreads();
     const T beta = (T)g.beta;
     const int pd[3] = {p1, p2, p3};
-    for (int i = threadIdx.x; i < len; i += kInterpSmBlock) {
+    for (int i = threadIdx.x; i < len; i += (kInterpSmBlock<T, DIM>)) {
         const int64_t j = (int64_t)start + i;
         T xc[DIM];
 #pragma unroll
         for (int d = 0; d < DIM; ++d) xc[d] = xn[d];
         const int32_t oc = on;
-        if (i + kInterpSmBlock < len) {
+        if (i + (kInterpSmBlock<T, DIM>) < len) {
 #pragma unroll
-            for (int d = 0; d < DIM; ++d) xn[d] = ((const T*)g.xs[d])[j + kInterpSmBlock];
-            on = g.perm[j + kInterpSmBlock];
+            for (int d = 0; d < DIM; ++d) xn[d] = ((const T*)g.xs[d])[j + (kInterpSmBlock<T, DIM>)];
+            on = g.perm[j + (kInterpSmBlock<T, DIM>)];
         }
         T ker[DIM][W];
         int l0[3] = {0, 0, 0};
@@ -188,7 +190,7 @@ hipError_t interp_w(int method, const GeomArgs& g, const void* grid, void* c, hi
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_interp_sm<T, DIM, W><<<dim3((unsigned)g.nsub), kInterpSmBlock, lds, st>>>(
+    k_interp_sm<T, DIM, W><<<dim3((unsigned)g.nsub), (kInterpSmBlock<T, DIM>), lds, st>>>(
         g, (const cplx<T>*)grid, (cplx<T>*)c, p1, p2, p3);
     return hipGetLastError();
 }
