@@ -56,7 +56,10 @@ enum nufft_status {
 enum nufft_spread_method {
     NUFFT_METHOD_AUTO = 0,
     NUFFT_METHOD_GM_SORT = 1,     /* one thread per sorted point, global atomics (Sec. III-A "GM-sort") */
-    NUFFT_METHOD_SM = 2           /* subproblems spread into LDS tiles, then flushed (Sec. III-A "SM") */
+    NUFFT_METHOD_SM = 2,          /* subproblems spread into LDS tiles, then flushed (Sec. III-A "SM") */
+    NUFFT_METHOD_GM = 3           /* one thread per point in the caller's order, global atomics
+                                     (Sec. III-A "GM"); setpts only checks and copies the points:
+                                     the permutation is the identity and there are no subproblems */
 };
 
 typedef struct {

@@ -173,7 +173,7 @@ __global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs
 template <typename T, int DIM, int W>
 hipError_t interp_w(int method, const GeomArgs& g, const void* grid, void* c, hipStream_t st) {
     if (g.M <= 0) return hipSuccess;
-    if (method == NUFFT_METHOD_GM_SORT) {
+    if (method == NUFFT_METHOD_GM_SORT || method == NUFFT_METHOD_GM) {
         dim3 grd((unsigned)((g.M + kInterpBlock - 1) / kInterpBlock));
         k_interp_gm<T, DIM, W><<<grd, kInterpBlock, 0, st>>>(g, (const cplx<T>*)grid, (cplx<T>*)c);
         return hipGetLastError();

@@ -409,7 +409,9 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
     }
 
     // method, bins and subproblem cap
-    plan->method = (plan->opts.method == NUFFT_METHOD_GM_SORT) ? NUFFT_METHOD_GM_SORT : NUFFT_METHOD_SM;
+    plan->method = (plan->opts.method == NUFFT_METHOD_GM_SORT || plan->opts.method == NUFFT_METHOD_GM)
+                       ? plan->opts.method
+                       : NUFFT_METHOD_SM;
     int m[3] = {1, 1, 1};
     if (plan->opts.bin[0] > 0) {
         for (int i = 0; i < dim; ++i) m[i] = std::max(1, plan->opts.bin[i]);
@@ -544,6 +546,25 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     a.colw = plan->colw;
     a.colstep = plan->colstep;
     a.ncol = plan->ncol;
+    if (plan->method == NUFFT_METHOD_GM) {
+        // no sort: the points stay in the caller's order
+        NUFFT_HIP(nufft::launch_fill_zero(plan->counts.p, (size_t)plan->nbins * sizeof(int32_t), plan->stream));
+        NUFFT_HIP(nufft::launch_identity_order(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p, plan->xs.p,
+                                               bad_dev, plan->stream));
+        int host_bad = 0;
+        NUFFT_HIP(hipMemcpyAsync(&host_bad, bad_dev, sizeof(int), hipMemcpyDeviceToHost, plan->stream));
+        NUFFT_HIP(hipStreamSynchronize(plan->stream));
+        if (host_bad) return fail(plan, NUFFT_ERR_POINTS, "a coordinate is not finite or outside [-3pi, 3pi)");
+        record(plan, EV_SORT1);
+        plan->M = M;
+        plan->nsub = 0;
+        if (plan->opts.timing && plan->ev_ok) {
+            NUFFT_HIP(hipEventSynchronize(plan->ev[EV_SORT1]));
+            float ms = 0;
+            if (hipEventElapsedTime(&ms, plan->ev[EV_SORT0], plan->ev[EV_SORT1]) == hipSuccess) plan->stage_ms[0] = ms;
+        }
+        return NUFFT_OK;
+    }
     NUFFT_HIP(nufft::launch_sort(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p,
                                  (int32_t*)plan->offsets.p, plan->xs.p, plan->sort_tmp.p,
                                  plan->sort_tmp.bytes - 256, nsub_dev, bad_dev, plan->stream));

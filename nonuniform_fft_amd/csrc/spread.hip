@@ -856,7 +856,7 @@ size_t stage_bytes() { return sizeof(Stage<T, DIM, W>); }
 template <typename T, int DIM, int W>
 hipError_t spread_w(int method, const GeomArgs& g, const void* c, void* grid, hipStream_t st) {
     if (g.M <= 0) return hipSuccess;
-    if (method == NUFFT_METHOD_GM_SORT) {
+    if (method == NUFFT_METHOD_GM_SORT || method == NUFFT_METHOD_GM) {
         dim3 grd((unsigned)((g.M + kGmBlock - 1) / kGmBlock));
         k_spread_gm<T, DIM, W><<<grd, kGmBlock, 0, st>>>(g, (const cplx<T>*)c, (cplx<T>*)grid);
         return hipGetLastError();
@@ -942,7 +942,9 @@ hipError_t launch_spread(int prec, int method, const GeomArgs& g_in, const void*
     // loads of large point sets (fp32 plans hide them, and the extra pass would cost more)
     GeomArgs g = g_in;
     const void* c = c_in;
-    if (prec == 1 && g.M > 0) {
+    if (method == NUFFT_METHOD_GM) {
+        g.cperm = nullptr;   // the points are in the caller's order
+    } else if (prec == 1 && g.M > 0) {
         k_gather_c<<<(unsigned)((g.M + 255) / 256), 256, 0, st>>>(g.perm, (const cplx<double>*)c_in,
                                                                    (cplx<double>*)c_scratch, g.M);
         hipError_t e = hipGetLastError();
@@ -950,7 +952,7 @@ hipError_t launch_spread(int prec, int method, const GeomArgs& g_in, const void*
         g.cperm = nullptr;
         c = c_scratch;
     }
-    if (columns && method != NUFFT_METHOD_GM_SORT)
+    if (columns && method == NUFFT_METHOD_SM)
         return prec == 0 ? spread_col<float>(g, c, grid, st) : spread_col<double>(g, c, grid, st);
     if (prec == 0) return g.dim == 2 ? spread_dim<float, 2>(method, g, c, grid, st)
                                      : spread_dim<float, 3>(method, g, c, grid, st);

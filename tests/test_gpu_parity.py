@@ -145,7 +145,7 @@ def _step_tol(prec, fp32_atomics=False):
 
 
 @pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: f"{w.dim}d_{w.N}_{w.precision}_{w.eps:g}_{w.dist}")
-@pytest.mark.parametrize("method", [2, 1], ids=["SM", "GMsort"])
+@pytest.mark.parametrize("method", [2, 1, 3], ids=["SM", "GMsort", "GM"])
 def test_spread_step(nf, orc, wl, method):
     _announce(f"spread {wl.N} {wl.precision} eps={wl.eps} {wl.dist} method={method}")
     inp = make_inputs(wl, want_f=False)
@@ -156,12 +156,12 @@ def test_spread_step(nf, orc, wl, method):
     torch.cuda.synchronize()
     ref = orc.spread(inp["X"], inp["c"], p.n, p.w, p.beta)
     err = orc.rel_l2(grid.cpu().numpy(), ref.ravel())
-    assert err <= _step_tol(wl.precision, fp32_atomics=(method == 1)), err
+    assert err <= _step_tol(wl.precision, fp32_atomics=(method in (1, 3))), err
     p.destroy()
 
 
 @pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: f"{w.dim}d_{w.N}_{w.precision}_{w.eps:g}_{w.dist}")
-@pytest.mark.parametrize("method", [2, 1], ids=["SM", "GMsort"])
+@pytest.mark.parametrize("method", [2, 1, 3], ids=["SM", "GMsort", "GM"])
 def test_interp_step(nf, orc, wl, method):
     _announce(f"interp {wl.N} {wl.precision} eps={wl.eps} {wl.dist} method={method}")
     inp = make_inputs(wl, want_f=False)
@@ -268,11 +268,11 @@ def test_adjointness_on_gpu(nf, N, prec, eps):
 
 
 def test_methods_agree_and_caps(nf, orc):
-    """GM-sort and SM with several subproblem caps all match the oracle."""
+    """GM, GM-sort and SM with several subproblem caps all match the oracle."""
     wl = Workload("m", 3, (24, 20, 18), 40_000, 1e-5, "f32", seed=52)
     inp = make_inputs(wl, want_f=False)
     ref = orc.nufft_type1(inp["X"], inp["c"], wl.N, wl.eps)
-    for kw in ({"method": 1}, {"method": 2, "subproblem_cap": 1}, {"method": 2, "subproblem_cap": 100},
+    for kw in ({"method": 1}, {"method": 3}, {"method": 2, "subproblem_cap": 1}, {"method": 2, "subproblem_cap": 100},
                {"method": 2, "bins": (8, 8, 8)}, {"method": 2, "bins": (4, 8, 16)}):
         f = gpu_type1(nf, inp["X"], inp["c"], wl.N, wl.eps, wl.precision, **kw)
         assert orc.rel_l2(f, ref) <= 1e-5, kw
@@ -381,3 +381,35 @@ def test_column_kernel_widths(nf, orc, prec, eps):
     e1 = orc.rel_l2(f.cpu().numpy(), orc.nufft_type1(inp["X"], inp["c"], N, eps))
     e2 = orc.rel_l2(c.cpu().numpy(), orc.nufft_type2(inp["X"], inp["f"], N, eps))
     assert e1 <= tol_for(prec) and e2 <= tol_for(prec), (info["w"], e1, e2)
+
+
+@pytest.mark.parametrize("wl", [Workload("gm", 3, (24, 20, 18), 30_000, 1e-5, "f32", seed=91),
+                                Workload("gm", 2, (48, 40), 20_000, 1e-12, "f64", seed=92),
+                                Workload("gm", 3, (20, 16, 12), 10_000, 1e-9, "f64", dist="cluster", seed=93)],
+                         ids=["3d_f32", "2d_f64", "3d_f64_cluster"])
+def test_gm_method(nf, orc, wl):
+    """GM (Sec. III-A): setpts keeps the caller's order (identity permutation, no subproblems, bin
+    counts as the oracle's); type 1 and the adjoint type 2 match the oracle NUFFT."""
+    _announce(f"GM {wl.N} {wl.precision} eps={wl.eps} {wl.dist}")
+    inp = make_inputs(wl)
+    X = [to_dev(x) for x in inp["X"]]
+    p = nf.Plan(1, wl.N, wl.eps, wl.precision, method=3)
+    p.setpts(*X)
+    info = p.info()
+    assert info["method"] == 3 and info["nsubproblems"] == 0 and info["colw"] == 0
+    perm, counts, sub = p.get_sort()
+    assert sub.numel() == 0
+    np.testing.assert_array_equal(perm.cpu().numpy(), np.arange(wl.M))
+    _, ocounts, _ = orc.binsort(inp["X"], info["n"], info["bins"])
+    np.testing.assert_array_equal(counts.cpu().numpy(), ocounts)
+    cd = cdtype(wl.precision)
+    f = torch.empty(tuple(reversed(wl.N)), dtype=cd, device=dev())
+    c = torch.empty(wl.M, dtype=cd, device=dev())
+    p.execute(to_dev(inp["c"]), f)
+    p.execute_adjoint(c, to_dev(inp["f"]))
+    torch.cuda.synchronize()
+    p.destroy()
+    # GM adds every contribution with a global atomic in the plan precision (fp32: 1e-5, as for
+    # GM-sort spreading)
+    assert orc.rel_l2(f.cpu().numpy(), orc.nufft_type1(inp["X"], inp["c"], wl.N, wl.eps)) <= tol_for(wl.precision)
+    assert orc.rel_l2(c.cpu().numpy(), orc.nufft_type2(inp["X"], inp["f"], wl.N, wl.eps)) <= tol_for(wl.precision)
