@@ -89,6 +89,76 @@ def probe_copy(nbytes):
     print(json.dumps({"probe_copy_bytes": nbytes, "copies": 3}))
 
 
+def compare_methods(steps, workloads):
+    """Method comparison (GM vs GM-sort vs SM, uniform vs clustered points): one JSON line per
+    (workload, method, type) with NU points/s for exec (execute only, points already set), total
+    (setpts + execute) and total+mem (host-to-device copies of the inputs from pinned memory,
+    setpts, execute, and the copy of the output back)."""
+    import numpy as np
+    import torch
+
+    import nonuniform_fft_amd as nf
+    from nonuniform_fft_amd.workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    for name in workloads:
+        wl = WORKLOADS[name]
+        inp = make_inputs(wl)
+        cdt = torch.complex64 if wl.precision == "f32" else torch.complex128
+        hX = [torch.from_numpy(x).pin_memory() for x in inp["X"]]
+        hc = torch.from_numpy(inp["c"]).pin_memory()
+        hf = torch.from_numpy(inp["f"]).pin_memory()
+        X = [x.to(dev) for x in hX]
+        c_in = hc.to(dev)
+        f_in = hf.to(dev)
+        f_out = torch.empty(tuple(reversed(wl.N)), dtype=cdt, device=dev)
+        c_out = torch.empty(wl.M, dtype=cdt, device=dev)
+        hf_out = torch.empty(f_out.shape, dtype=cdt).pin_memory()
+        hc_out = torch.empty(wl.M, dtype=cdt).pin_memory()
+        for method, mname in ((2, "SM"), (1, "GM-sort"), (3, "GM")):
+            for typ in (1, 2):
+                plan = nf.Plan(typ, wl.N, wl.eps, wl.precision, stream=stream, method=method)
+
+                def run_exec():
+                    if typ == 1:
+                        plan.execute(c_in, f_out)
+                    else:
+                        plan.execute(c_out, f_in)
+
+                def run_total():
+                    plan.setpts(*X)
+                    run_exec()
+
+                def run_mem():
+                    for d, h in zip(X, hX):
+                        d.copy_(h, non_blocking=True)
+                    if typ == 1:
+                        c_in.copy_(hc, non_blocking=True)
+                    else:
+                        f_in.copy_(hf, non_blocking=True)
+                    run_total()
+                    if typ == 1:
+                        hf_out.copy_(f_out, non_blocking=True)
+                    else:
+                        hc_out.copy_(c_out, non_blocking=True)
+
+                plan.setpts(*X)
+                run_exec()
+                res = {}
+                for key, fn in (("exec", run_exec), ("total", run_total), ("total+mem", run_mem)):
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    for _ in range(steps):
+                        fn()
+                    torch.cuda.synchronize()
+                    ms = (time.perf_counter() - t0) * 1e3 / steps
+                    res[key] = {"ms": ms, "pts_per_s": wl.M / (ms * 1e-3)}
+                plan.destroy()
+                print(json.dumps({"workload": name, "method": mname, "type": typ, **res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,9 +170,15 @@ def main():
     ap.add_argument("--method", type=int, default=0)
     ap.add_argument("--probe-copy", type=int, default=0,
                     help="only run a plain copy of this many bytes (counter calibration)")
+    ap.add_argument("--compare", action="store_true",
+                    help="only compare the GM, GM-sort and SM methods (JSON line per method and type)")
     args = ap.parse_args()
     if args.probe_copy:
         probe_copy(args.probe_copy)
+        return
+    if args.compare:
+        compare_methods(args.steps, ["3d_n128_m16m_f32_e5", "3d_n128_m16m_f32_e5_cluster",
+                                     "2d_n1024_m4m_f32_e5"])
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))

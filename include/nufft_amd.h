@@ -59,7 +59,8 @@ enum nufft_spread_method {
     NUFFT_METHOD_SM = 2,          /* subproblems spread into LDS tiles, then flushed (Sec. III-A "SM") */
     NUFFT_METHOD_GM = 3           /* one thread per point in the caller's order, global atomics
                                      (Sec. III-A "GM"); setpts only checks and copies the points:
-                                     the permutation is the identity and there are no subproblems */
+                                     the permutation is the identity, there are no subproblems and
+                                     the bin counts read zero (no binning) */
 };
 
 typedef struct {
@@ -184,6 +185,7 @@ int nufft_precorrect_pad(nufft_plan plan, const void* f, void* fhat);
  * (c2 / s) ceil((m1 + 1) / s) + c1 / s of the column where their kernel support starts, then by
  * the z start c3, with c_i = ceil(t_i - w/2) - (b_i m_i - floor(w/2)) and
  * t_i = (x_i + pi) n_i / (2 pi) folded, and by original index last.
+ * With the GM method there is no sort: perm is the identity and counts are all zero.
  */
 int nufft_get_sort(nufft_plan plan, int32_t* perm, int32_t* counts, int32_t* subproblems);
 

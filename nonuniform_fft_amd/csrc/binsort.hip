@@ -69,11 +69,9 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
 // check as the keys above, a copy of the coordinates, the identity permutation and bin counts.
 template <typename T, int DIM>
 __global__ void __launch_bounds__(kBlock) k_identity_order(SortArgs a, int32_t* __restrict__ perm,
-                                                            int32_t* __restrict__ counts, T* __restrict__ xs_out,
-                                                            int* __restrict__ bad) {
+                                                            T* __restrict__ xs_out, int* __restrict__ bad) {
     const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (j >= a.M) return;
-    int bidx[3] = {0, 0, 0};
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < DIM; ++i) {
@@ -81,14 +79,10 @@ __global__ void __launch_bounds__(kBlock) k_identity_order(SortArgs a, int32_t* 
         xs_out[(int64_t)i * a.M + j] = xv;
         double t = grid_t((double)xv, a.s[i]);
         int l = 0;
-        if (!fold_t(t, a.n[i], l)) { ok = false; l = 0; }
-        bidx[i] = l / a.m[i];
+        if (!fold_t(t, a.n[i], l)) ok = false;
     }
     perm[j] = (int32_t)j;
-    if (ok)
-        atomicAdd(&counts[bidx[0] + a.nb[0] * (bidx[1] + a.nb[1] * bidx[2])], 1);
-    else
-        atomicOr(bad, 1);
+    if (!ok) atomicOr(bad, 1);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -526,16 +520,15 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
 }
 
 // Subproblem list from the scratch of the last launch_sort (bins, cap, counts, offsets as there).
-hipError_t launch_identity_order(const SortArgs& a, int32_t* perm, int32_t* counts, void* xs_out, int* bad_dev,
-                                 hipStream_t st) {
+hipError_t launch_identity_order(const SortArgs& a, int32_t* perm, void* xs_out, int* bad_dev, hipStream_t st) {
     if (a.M <= 0) return hipSuccess;
     dim3 g((unsigned)cdiv(a.M, kBlock));
     if (a.prec == 0) {
-        if (a.dim == 2) k_identity_order<float, 2><<<g, kBlock, 0, st>>>(a, perm, counts, (float*)xs_out, bad_dev);
-        else k_identity_order<float, 3><<<g, kBlock, 0, st>>>(a, perm, counts, (float*)xs_out, bad_dev);
+        if (a.dim == 2) k_identity_order<float, 2><<<g, kBlock, 0, st>>>(a, perm, (float*)xs_out, bad_dev);
+        else k_identity_order<float, 3><<<g, kBlock, 0, st>>>(a, perm, (float*)xs_out, bad_dev);
     } else {
-        if (a.dim == 2) k_identity_order<double, 2><<<g, kBlock, 0, st>>>(a, perm, counts, (double*)xs_out, bad_dev);
-        else k_identity_order<double, 3><<<g, kBlock, 0, st>>>(a, perm, counts, (double*)xs_out, bad_dev);
+        if (a.dim == 2) k_identity_order<double, 2><<<g, kBlock, 0, st>>>(a, perm, (double*)xs_out, bad_dev);
+        else k_identity_order<double, 3><<<g, kBlock, 0, st>>>(a, perm, (double*)xs_out, bad_dev);
     }
     return hipGetLastError();
 }

@@ -547,10 +547,9 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     a.colstep = plan->colstep;
     a.ncol = plan->ncol;
     if (plan->method == NUFFT_METHOD_GM) {
-        // no sort: the points stay in the caller's order
+        // no sort and no binning: the points stay in the caller's order and the bin counts read zero
         NUFFT_HIP(nufft::launch_fill_zero(plan->counts.p, (size_t)plan->nbins * sizeof(int32_t), plan->stream));
-        NUFFT_HIP(nufft::launch_identity_order(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p, plan->xs.p,
-                                               bad_dev, plan->stream));
+        NUFFT_HIP(nufft::launch_identity_order(a, (int32_t*)plan->perm.p, plan->xs.p, bad_dev, plan->stream));
         int host_bad = 0;
         NUFFT_HIP(hipMemcpyAsync(&host_bad, bad_dev, sizeof(int), hipMemcpyDeviceToHost, plan->stream));
         NUFFT_HIP(hipStreamSynchronize(plan->stream));

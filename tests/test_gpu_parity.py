@@ -388,8 +388,8 @@ def test_column_kernel_widths(nf, orc, prec, eps):
                                 Workload("gm", 3, (20, 16, 12), 10_000, 1e-9, "f64", dist="cluster", seed=93)],
                          ids=["3d_f32", "2d_f64", "3d_f64_cluster"])
 def test_gm_method(nf, orc, wl):
-    """GM (Sec. III-A): setpts keeps the caller's order (identity permutation, no subproblems, bin
-    counts as the oracle's); type 1 and the adjoint type 2 match the oracle NUFFT."""
+    """GM (Sec. III-A): setpts keeps the caller's order (identity permutation, no subproblems, no
+    binning: the bin counts read zero); type 1 and the adjoint type 2 match the oracle NUFFT."""
     _announce(f"GM {wl.N} {wl.precision} eps={wl.eps} {wl.dist}")
     inp = make_inputs(wl)
     X = [to_dev(x) for x in inp["X"]]
@@ -400,8 +400,7 @@ def test_gm_method(nf, orc, wl):
     perm, counts, sub = p.get_sort()
     assert sub.numel() == 0
     np.testing.assert_array_equal(perm.cpu().numpy(), np.arange(wl.M))
-    _, ocounts, _ = orc.binsort(inp["X"], info["n"], info["bins"])
-    np.testing.assert_array_equal(counts.cpu().numpy(), ocounts)
+    assert not counts.cpu().numpy().any()
     cd = cdtype(wl.precision)
     f = torch.empty(tuple(reversed(wl.N)), dtype=cd, device=dev())
     c = torch.empty(wl.M, dtype=cd, device=dev())
