@@ -111,7 +111,7 @@ def test_phihat_adaptive_quadrature(oracle_mod, w):
 # Exact sums (eqs. (1), (3))
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("N", [(8, 6), (5, 7), (4, 6, 5)])
+@pytest.mark.parametrize("N", [(16,), (9,), (8, 6), (5, 7), (4, 6, 5)])
 def test_direct_type1_on_uniform_grid_is_fft(oracle_mod, N):
     """Points on the equispaced grid 2 pi j / N - pi: eq. (1) is (-1)^(sum k) times numpy's FFT."""
     rng = _rng(1)
@@ -129,7 +129,7 @@ def test_direct_type1_on_uniform_grid_is_fft(oracle_mod, N):
     np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-12 * np.abs(expect).max())
 
 
-@pytest.mark.parametrize("N", [(6, 9), (4, 5, 3)])
+@pytest.mark.parametrize("N", [(11,), (6, 9), (4, 5, 3)])
 def test_direct_type2_all_ones_is_dirichlet_product(oracle_mod, N):
     """f = 1 on I_N: c_j = prod_i sum_{k in I_Ni} exp(i k x_ij) (geometric series)."""
     rng = _rng(2)
@@ -143,7 +143,7 @@ def test_direct_type2_all_ones_is_dirichlet_product(oracle_mod, N):
     np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("N", [(7, 8), (4, 6, 5)])
+@pytest.mark.parametrize("N", [(13,), (7, 8), (4, 6, 5)])
 def test_direct_sums_are_adjoint(oracle_mod, N):
     rng = _rng(3)
     M = 37
@@ -197,7 +197,8 @@ def _brute_psi_per(X, n, w, beta):
     return out
 
 
-@pytest.mark.parametrize("n,w", [((16, 12), 6), ((12, 10), 3), ((10, 8, 12), 4), ((9, 8, 10), 5)])
+@pytest.mark.parametrize("n,w", [((40,), 6), ((30,), 13), ((16, 12), 6), ((12, 10), 3), ((10, 8, 12), 4),
+                                 ((9, 8, 10), 5)])
 def test_spread_and_interp_match_bruteforce(oracle_mod, n, w):
     rng = _rng(5)
     beta = 2.30 * w
@@ -222,6 +223,9 @@ def test_spread_and_interp_match_bruteforce(oracle_mod, n, w):
 # ---------------------------------------------------------------------------------------------
 
 CASES = [
+    ((256,), 5000, 1e-5, "f32"),           # 1D
+    ((100,), 1000, 1e-12, "f64"),
+    ((63,), 300, 1e-2, "f32"),
     ((64, 64), 10_000, 1e-5, "f32"),       # the 2D 64x64 configuration at full size
     ((32, 32), 1000, 1e-2, "f32"),
     ((32, 32), 1000, 1e-9, "f64"),
@@ -254,7 +258,7 @@ def test_nufft_clustered_vs_direct(oracle_mod):
     assert oracle_mod.rel_l2(f1, oracle_mod.direct_type1(inp["X"], inp["c"], wl.N)) <= 10 * wl.eps
 
 
-@pytest.mark.parametrize("N,eps", [((20, 24), 1e-6), ((10, 12, 8), 1e-3)])
+@pytest.mark.parametrize("N,eps", [((50,), 1e-6), ((20, 24), 1e-6), ((10, 12, 8), 1e-3)])
 def test_nufft_type1_type2_adjoint(oracle_mod, N, eps):
     """Steps (7),(9),(10) and (11),(12),interp are exact transposes: adjoint to rounding."""
     rng = _rng(6)
@@ -277,6 +281,16 @@ def test_single_point_closed_form(oracle_mod):
         expect = np.exp(-1j * (ks[2][:, None, None] * x0[2][0] + ks[1][None, :, None] * x0[1][0]
                                + ks[0][None, None, :] * x0[0][0]))
         assert oracle_mod.rel_l2(f, expect) <= 10 * eps
+
+
+def test_single_point_closed_form_1d(oracle_mod):
+    """M = 1, c = 1 in 1D: eq. (1) is exp(-i k x0), also for odd N."""
+    for N in (32, 33):
+        for x0 in (-math.pi, 0.7, math.pi - 1e-9):
+            for eps in (1e-2, 1e-5, 1e-12):
+                f = oracle_mod.nufft_type1([np.array([x0])], np.array([1.0 + 0j]), (N,), eps)
+                expect = np.exp(-1j * oracle_mod.mode_range(N) * x0)
+                assert oracle_mod.rel_l2(f, expect) <= 10 * eps
 
 
 def test_delta_coefficients_closed_form(oracle_mod):
@@ -363,6 +377,22 @@ def test_bins_random_points_cell_interval_and_stable_perm(oracle_mod):
         ok = (u >= lo - 1e-9) & (u < hi + 1e-9)
         assert ok.all()
     np.testing.assert_array_equal(counts, np.bincount(binv, minlength=counts.size))
+    np.testing.assert_array_equal(perm, np.argsort(binv, kind="stable"))
+
+
+def test_bins_1d_cell_interval_and_stable_perm(oracle_mod):
+    """1D: the bin of a point is floor(l / m) with l h <= x + pi < (l + 1) h, and perm is the
+    stable argsort of the bins (a ragged last bin: n not a multiple of m)."""
+    n, m = (200,), (32,)
+    rng = _rng(12)
+    x = rng.uniform(-math.pi, math.pi, 3000).astype(np.float32).astype(np.float64)
+    binv, counts, perm = oracle_mod.binsort([x], n, m)
+    u = (np.longdouble(x) + np.longdouble(math.pi)) * n[0] / (2 * np.longdouble(math.pi))
+    lo = binv * m[0]
+    hi = np.minimum(lo + m[0], n[0])
+    assert ((u >= lo - 1e-9) & (u < hi + 1e-9)).all()
+    assert counts.size == 7
+    np.testing.assert_array_equal(counts, np.bincount(binv, minlength=7))
     np.testing.assert_array_equal(perm, np.argsort(binv, kind="stable"))
 
 
