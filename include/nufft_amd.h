@@ -1,11 +1,14 @@
 /*
- * nufft_amd.h -- C ABI of the MI355X (gfx950) 2D/3D type 1 / type 2 NUFFT library.
+ * nufft_amd.h -- C ABI of the MI355X (gfx950) 1D/2D/3D type 1 / type 2 NUFFT library.
  *
  * The transforms (cuFINUFFT paper, "cuFINUFFT: a load-balanced GPU library for
  * general-purpose nonuniform FFTs", Sec. I):
  *   type 1, eq. (1):  f_k = sum_{j=1..M} c_j exp(-i k.x_j),  k in I_N1 x I_N2 (x I_N3),
  *   type 2, eq. (3):  c_j = sum_k f_k exp(+i k.x_j),          j = 1..M,
- * with I_N = {k integer : -N/2 <= k < N/2} (eq. (2)) and points x_j in [-pi, pi)^d.
+ * with I_N = {k integer : -N/2 <= k < N/2} (eq. (2)) and points x_j in [-pi, pi)^d, d = 1, 2, 3.
+ * (The paper's library lists 1D as not yet provided, Sec. I-B item (4); the scheme of Sec. II
+ * applies unchanged with d = 1, as in the FINUFFT discussion page "CUFINUFFT binsize and
+ * performance", which reports 1D throughputs.)
  * Both are approximated to a requested tolerance eps by the three-step scheme of
  * Sec. II (ES-kernel spreading / interpolation on a 2x upsampled grid, a plain
  * FFT, and a diagonal correction).  The library follows the paper's "plan,
@@ -77,8 +80,8 @@ int nufft_default_opts(nufft_opts* opts);
 /*
  * Create a plan.
  *   type      1 (nonuniform -> uniform, eq. (1)) or 2 (uniform -> nonuniform, eq. (3)).
- *   dim       2 or 3.
- *   N         host array of dim mode counts (N1, N2[, N3]), each >= 1.
+ *   dim       1, 2 or 3.
+ *   N         host array of dim mode counts (N1[, N2[, N3]]), each >= 1.
  *   eps       requested relative tolerance > 0.  Kernel width w = ceil(log10(1/eps)) + 1
  *             and shape beta = 2.30 w (eq. (6)); w is clamped to [2, 16] with
  *             NUFFT_WARN_EPS_CLAMPED.
@@ -95,7 +98,7 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
 /*
  * Set the nonuniform points (Sec. III-A bin-sort and subproblems).
  *   M        number of points, 0 <= M <= 2^31 - 1.
- *   x, y, z  device arrays of M coordinates (z is NULL for dim 2).  Values must be
+ *   x, y, z  device arrays of M coordinates (z is NULL for dim 2; y and z for dim 1).  Values must be
  *            finite and in [-3pi, 3pi) (one periodic fold is applied), else
  *            NUFFT_ERR_POINTS and the plan keeps no points.
  * The library copies what it needs (sorted coordinates, permutation); the caller

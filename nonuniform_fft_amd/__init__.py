@@ -1,4 +1,4 @@
-"""MI355X (gfx950) 2D/3D type 1 / type 2 nonuniform FFT.
+"""MI355X (gfx950) 1D/2D/3D type 1 / type 2 nonuniform FFT.
 
 The transform runs in the HIP library libnufft_amd.so behind the C ABI of
 include/nufft_amd.h; `Plan` is a thin ctypes binding over it that takes torch

@@ -196,10 +196,12 @@ class Plan:
                 "beta": dd[0], "eps": dd[1]}
 
     # -- API -----------------------------------------------------------------------------------
-    def setpts(self, x, y, z=None):
-        coords = [x, y] + ([z] if self.dim == 3 else [])
-        if self.dim == 2 and z is not None:
-            raise ValueError("2D plan takes x and y only")
+    def setpts(self, x, y=None, z=None):
+        coords = [x, y, z][:self.dim]
+        if any(t is not None for t in [x, y, z][self.dim:]):
+            raise ValueError(f"{self.dim}D plan takes {self.dim} coordinate array(s)")
+        if any(t is None for t in coords):
+            raise ValueError(f"{self.dim}D plan needs {self.dim} coordinate arrays")
         M = coords[0].numel()
         rd = _real_dtype(self.prec)
         ptrs = [self._dev_tensor(t, rd, M, name) for t, name in zip(coords, "xyz")]

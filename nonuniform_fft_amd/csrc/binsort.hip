@@ -406,6 +406,38 @@ SortLayout layout(int64_t M, int nbins, int dim, int prec) {
     return L;
 }
 
+// fn(T{}, std::integral_constant<int, DIM>{}) for the plan's precision (0 = fp32) and dimension.
+template <typename F>
+void with_type_dim(int prec, int dim, F&& fn) {
+    auto by_dim = [&](auto tag) {
+        if (dim == 1) fn(tag, std::integral_constant<int, 1>{});
+        else if (dim == 2) fn(tag, std::integral_constant<int, 2>{});
+        else fn(tag, std::integral_constant<int, 3>{});
+    };
+    if (prec == 0) by_dim(float{});
+    else by_dim(double{});
+}
+
+// One radix scatter pass with the dim coordinate arrays cin[] -> cout[] as payload; vi == null
+// marks the first pass (values = identity).
+template <typename T>
+hipError_t scatter_dim(int dim, const int32_t* ki, const int32_t* vi, int32_t* ko, int32_t* vo, int64_t M,
+                       int shift, int bits, int ntiles, const int32_t* hscan, const void* const* cin,
+                       void* const* cout, hipStream_t st) {
+    auto go = [&](auto dtag) {
+        constexpr int D = decltype(dtag)::value;
+        Payload<T, D> pl{};
+        for (int d = 0; d < D; ++d) { pl.in[d] = (const T*)cin[d]; pl.out[d] = (T*)cout[d]; }
+        const dim3 gt((unsigned)ntiles);
+        if (vi) k_radix_scatter<T, D, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, pl);
+        else k_radix_scatter<T, D, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, pl);
+    };
+    if (dim == 1) go(std::integral_constant<int, 1>{});
+    else if (dim == 2) go(std::integral_constant<int, 2>{});
+    else go(std::integral_constant<int, 3>{});
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec) { return layout(M, nbins, dim, prec).end; }
@@ -429,13 +461,11 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
     const int64_t M = a.M;
     if (M > 0) {
         dim3 g((unsigned)cdiv(M, kBlock));
-        if (a.prec == 0) {
-            if (a.dim == 2) k_bin_keys<float, 2><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
-            else k_bin_keys<float, 3><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
-        } else {
-            if (a.dim == 2) k_bin_keys<double, 2><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
-            else k_bin_keys<double, 3><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
-        }
+        auto keys_kernel = [&](auto tag, auto dtag) {
+            using T = decltype(tag);
+            k_bin_keys<T, decltype(dtag)::value><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
+        };
+        with_type_dim(a.prec, a.dim, keys_kernel);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int passes = (a.nbits + kRadixBits - 1) / kRadixBits;
         int shift = 0;
@@ -464,33 +494,9 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
                                                                      : (const void*)((char*)xs_out + (size_t)d * M * rs));
                 cout[d] = to_tmp ? (void*)(ctmp + (size_t)d * M * rs) : (void*)((char*)xs_out + (size_t)d * M * rs);
             }
-            (void)last;
-            if (a.prec == 0) {
-                Payload<float, 3> pl{};
-                for (int d = 0; d < a.dim; ++d) { pl.in[d] = (const float*)cin[d]; pl.out[d] = (float*)cout[d]; }
-                if (a.dim == 2) {
-                    Payload<float, 2> p2{};
-                    for (int d = 0; d < 2; ++d) { p2.in[d] = pl.in[d]; p2.out[d] = pl.out[d]; }
-                    if (vi) k_radix_scatter<float, 2, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
-                    else k_radix_scatter<float, 2, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
-                } else {
-                    if (vi) k_radix_scatter<float, 3, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
-                    else k_radix_scatter<float, 3, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
-                }
-            } else {
-                Payload<double, 3> pl{};
-                for (int d = 0; d < a.dim; ++d) { pl.in[d] = (const double*)cin[d]; pl.out[d] = (double*)cout[d]; }
-                if (a.dim == 2) {
-                    Payload<double, 2> p2{};
-                    for (int d = 0; d < 2; ++d) { p2.in[d] = pl.in[d]; p2.out[d] = pl.out[d]; }
-                    if (vi) k_radix_scatter<double, 2, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
-                    else k_radix_scatter<double, 2, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, p2);
-                } else {
-                    if (vi) k_radix_scatter<double, 3, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
-                    else k_radix_scatter<double, 3, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, pl);
-                }
-            }
-            if ((e = hipGetLastError()) != hipSuccess) return e;
+            e = a.prec == 0 ? scatter_dim<float>(a.dim, ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, cin, cout, st)
+                            : scatter_dim<double>(a.dim, ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, cin, cout, st);
+            if (e != hipSuccess) return e;
             std::swap(ki, ko);
             shift += bits;
         }
@@ -523,13 +529,10 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
 hipError_t launch_identity_order(const SortArgs& a, int32_t* perm, void* xs_out, int* bad_dev, hipStream_t st) {
     if (a.M <= 0) return hipSuccess;
     dim3 g((unsigned)cdiv(a.M, kBlock));
-    if (a.prec == 0) {
-        if (a.dim == 2) k_identity_order<float, 2><<<g, kBlock, 0, st>>>(a, perm, (float*)xs_out, bad_dev);
-        else k_identity_order<float, 3><<<g, kBlock, 0, st>>>(a, perm, (float*)xs_out, bad_dev);
-    } else {
-        if (a.dim == 2) k_identity_order<double, 2><<<g, kBlock, 0, st>>>(a, perm, (double*)xs_out, bad_dev);
-        else k_identity_order<double, 3><<<g, kBlock, 0, st>>>(a, perm, (double*)xs_out, bad_dev);
-    }
+    with_type_dim(a.prec, a.dim, [&](auto tag, auto dtag) {
+        using T = decltype(tag);
+        k_identity_order<T, decltype(dtag)::value><<<g, kBlock, 0, st>>>(a, perm, (T*)xs_out, bad_dev);
+    });
     return hipGetLastError();
 }
 

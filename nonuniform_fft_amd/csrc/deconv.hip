@@ -1,7 +1,8 @@
 // Correction steps (cuFINUFFT paper, Sec. II): type 1 step 3, truncation to I_N and scaling by
 // p_k (eq. (10)); type 2 step 1, pre-correction and zero padding onto the fine grid (eq. (11)).
 // p_k = p_1(k1) p_2(k2) [p_3(k3)] is separable; the per-dimension vectors are computed on the
-// host once per plan (one thread per mode or cell, coalesced along the fastest dimension).
+// host once per plan (one thread per mode or cell, coalesced along the fastest dimension).  1D
+// plans run the 2D kernels: their second dimension has N2 = n2 = 1 and p_2 = 1.
 #include "nufft_internal.h"
 
 namespace nufft {
@@ -78,10 +79,10 @@ hipError_t launch_deconvolve(int prec, int dim, const int64_t* N, const int64_t*
     if (total == 0) return hipSuccess;
     dim3 g((unsigned)((total + kBlock - 1) / kBlock));
     if (prec == 0) {
-        if (dim == 2) k_deconvolve<float, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const float*)pcorr, (const cplx<float>*)fhat, (cplx<float>*)f);
+        if (dim <= 2) k_deconvolve<float, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const float*)pcorr, (const cplx<float>*)fhat, (cplx<float>*)f);
         else k_deconvolve<float, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, (const float*)pcorr, (const cplx<float>*)fhat, (cplx<float>*)f);
     } else {
-        if (dim == 2) k_deconvolve<double, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const double*)pcorr, (const cplx<double>*)fhat, (cplx<double>*)f);
+        if (dim <= 2) k_deconvolve<double, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const double*)pcorr, (const cplx<double>*)fhat, (cplx<double>*)f);
         else k_deconvolve<double, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, (const double*)pcorr, (const cplx<double>*)fhat, (cplx<double>*)f);
     }
     return hipGetLastError();
@@ -93,10 +94,10 @@ hipError_t launch_precorrect_pad(int prec, int dim, const int64_t* N, const int6
     int64_t total = n[0] * n[1] * (int64_t)n3;
     dim3 g((unsigned)((total + kBlock - 1) / kBlock));
     if (prec == 0) {
-        if (dim == 2) k_precorrect_pad<float, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const float*)pcorr, (const cplx<float>*)f, (cplx<float>*)fhat);
+        if (dim <= 2) k_precorrect_pad<float, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const float*)pcorr, (const cplx<float>*)f, (cplx<float>*)fhat);
         else k_precorrect_pad<float, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, (const float*)pcorr, (const cplx<float>*)f, (cplx<float>*)fhat);
     } else {
-        if (dim == 2) k_precorrect_pad<double, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const double*)pcorr, (const cplx<double>*)f, (cplx<double>*)fhat);
+        if (dim <= 2) k_precorrect_pad<double, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const double*)pcorr, (const cplx<double>*)f, (cplx<double>*)fhat);
         else k_precorrect_pad<double, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, (const double*)pcorr, (const cplx<double>*)f, (cplx<double>*)fhat);
     }
     return hipGetLastError();

@@ -38,6 +38,14 @@ __global__ void __launch_bounds__(kInterpBlock) k_interp_gm(GeomArgs g, const cp
     }
     const int n1 = g.n[0], n2 = g.n[1];
     T are = 0, aim = 0;
+    if constexpr (DIM == 1) {
+#pragma unroll
+        for (int q1 = 0; q1 < W; ++q1) {
+            const cplx<T> v = grid[idx[0][q1]];
+            are += v.re * ker[0][q1];
+            aim += v.im * ker[0][q1];
+        }
+    } else {
 #pragma unroll
     for (int q3 = 0; q3 < (DIM == 3 ? W : 1); ++q3) {
         for (int q2 = 0; q2 < W; ++q2) {
@@ -58,6 +66,7 @@ __global__ void __launch_bounds__(kInterpBlock) k_interp_gm(GeomArgs g, const cp
             are += rre * wr;
             aim += rim * wr;
         }
+    }
     }
     cplx<T> out;
     out.re = are;
@@ -88,7 +97,7 @@ __global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs
         int b1 = (bin / g.nb[0]) % g.nb[1];
         int b2 = bin / (g.nb[0] * g.nb[1]);
         origin[0] = b0 * g.m[0] - W / 2;
-        origin[1] = b1 * g.m[1] - W / 2;
+        if (DIM >= 2) origin[1] = b1 * g.m[1] - W / 2;
         if (DIM == 3) origin[2] = b2 * g.m[2] - W / 2;
     }
     // the coordinates of this thread's first point are requested before the tile copy, and
@@ -143,6 +152,15 @@ __global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs
             l0[d] = min(max(v, 0), pd[d] - W);
         }
         T are = 0, aim = 0;
+        if constexpr (DIM == 1) {
+            const cplx<T>* row = tile + l0[0];
+#pragma unroll
+            for (int q1 = 0; q1 < W; ++q1) {
+                const cplx<T> v = row[q1];
+                are += v.re * ker[0][q1];
+                aim += v.im * ker[0][q1];
+            }
+        } else {
 #pragma unroll
         for (int q3 = 0; q3 < (DIM == 3 ? W : 1); ++q3) {
             T pre = 0, pim = 0;
@@ -163,6 +181,7 @@ __global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs
             are += pre * kz;
             aim += pim * kz;
         }
+        }
         cplx<T> out;
         out.re = are;
         out.im = aim;
@@ -179,7 +198,7 @@ hipError_t interp_w(int method, const GeomArgs& g, const void* grid, void* c, hi
         return hipGetLastError();
     }
     if (g.nsub <= 0) return hipSuccess;
-    const int p1 = g.m[0] + W, p2 = g.m[1] + W, p3 = (DIM == 3) ? g.m[2] + W : 1;
+    const int p1 = g.m[0] + W, p2 = (DIM >= 2) ? g.m[1] + W : 1, p3 = (DIM == 3) ? g.m[2] + W : 1;
     const size_t lds = (size_t)p1 * p2 * p3 * sizeof(cplx<T>);
     if (lds > spread_lds_limit()) return hipErrorInvalidConfiguration;
     static bool attr_set = false;
@@ -212,8 +231,12 @@ hipError_t interp_dim(int method, const GeomArgs& g, const void* grid, void* c, 
 hipError_t launch_interp(int prec, int method, const GeomArgs& g, const void* grid, void* c,
                          hipStream_t st) {
     if (prec == 0)
-        return g.dim == 2 ? interp_dim<float, 2>(method, g, grid, c, st) : interp_dim<float, 3>(method, g, grid, c, st);
-    return g.dim == 2 ? interp_dim<double, 2>(method, g, grid, c, st) : interp_dim<double, 3>(method, g, grid, c, st);
+        return g.dim == 1   ? interp_dim<float, 1>(method, g, grid, c, st)
+               : g.dim == 2 ? interp_dim<float, 2>(method, g, grid, c, st)
+                            : interp_dim<float, 3>(method, g, grid, c, st);
+    return g.dim == 1   ? interp_dim<double, 1>(method, g, grid, c, st)
+           : g.dim == 2 ? interp_dim<double, 2>(method, g, grid, c, st)
+                        : interp_dim<double, 3>(method, g, grid, c, st);
 }
 
 size_t interp_tile_bytes(int prec, int dim, int w, const int* m) {

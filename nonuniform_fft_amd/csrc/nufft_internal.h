@@ -6,6 +6,7 @@
 #include <rocfft/rocfft.h>
 
 #include <cstdint>
+#include <type_traits>
 #include <string>
 
 #include "../../include/nufft_amd.h"

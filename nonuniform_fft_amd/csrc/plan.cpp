@@ -172,7 +172,18 @@ void default_bins(nufft_plan p, int* m) {
     static const int c2[][2] = {{32, 32}, {32, 16}, {16, 16}, {16, 8}, {8, 8}, {4, 4}, {2, 2}, {1, 1}};
     static const int c3[][3] = {{32, 16, 8}, {16, 16, 8}, {16, 8, 8}, {8, 8, 8}, {8, 8, 4}, {8, 4, 4},
                                 {4, 4, 4}, {4, 4, 2}, {2, 2, 2}, {1, 1, 1}};
-    if (p->dim == 2) {
+    if (p->dim == 1) {
+        // 1D: 256 cells (a sweep over 128..8192 cells at N = 2^20, M = 2^24 changed the spread
+        // and interpolation times by under 15 %, smallest at 128..256)
+        for (int c : {256, 128, 64, 32, 16, 8, 4, 2, 1}) {
+            int mm[3] = {c, 1, 1};
+            if (nufft::spread_tile_bytes(p->prec, 1, p->w, mm) <= nufft::spread_lds_limit()) {
+                m[0] = c;
+                m[1] = m[2] = 1;
+                return;
+            }
+        }
+    } else if (p->dim == 2) {
         for (auto& c : c2) {
             int mm[3] = {c[0], c[1], 1};
             if (nufft::spread_tile_bytes(p->prec, 2, p->w, mm) <= nufft::spread_lds_limit()) {
@@ -369,7 +380,7 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
                       const nufft_opts* opts, nufft_plan* out) {
     if (!out) return NUFFT_ERR_BAD_ARG;
     *out = nullptr;
-    if ((type != 1 && type != 2) || (dim != 2 && dim != 3) || !N || (precision != 0 && precision != 1))
+    if ((type != 1 && type != 2) || dim < 1 || dim > 3 || !N || (precision != 0 && precision != 1))
         return NUFFT_ERR_BAD_ARG;
     if (!(eps > 0.0) || !std::isfinite(eps)) return NUFFT_ERR_BAD_ARG;
     for (int i = 0; i < dim; ++i)

@@ -794,6 +794,65 @@ hipError_t spread_col(const GeomArgs& g, const void* c, void* grid, hipStream_t 
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// 1D SM spreading: one workgroup per subproblem and one lane per point.  A lane evaluates its
+// w weights and adds its w complex contributions into the fp64 LDS copy of the padded bin
+// (m + w cells, real and imaginary planes); the bin is then added into the fine grid with
+// periodic wrap (eq. (15)).  The next point's coordinate and strength are requested one
+// iteration ahead.
+// ------------------------------------------------------------------------------------------
+constexpr int kSpread1Block = 512;
+
+template <typename T, int W>
+__global__ void __launch_bounds__(kSpread1Block) k_spread_sm1(GeomArgs g, const cplx<T>* __restrict__ c,
+                                                              cplx<T>* __restrict__ grid, int p1) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    double* tre = (double*)smem;
+    double* tim = tre + p1;
+    const int sid = blockIdx.x;
+    const int bin = g.sub[3 * sid + 0];
+    const int start = g.sub[3 * sid + 1];
+    const int len = g.sub[3 * sid + 2];
+    const int origin = bin * g.m[0] - W / 2;
+    T xn = (T)0;
+    cplx<T> cn;
+    cn.re = (T)0;
+    cn.im = (T)0;
+    auto fetch = [&](int i) {
+        const int64_t j = (int64_t)start + i;
+        xn = ((const T*)g.xs[0])[j];
+        cn = c[g.cperm ? g.cperm[j] : j];
+    };
+    if ((int)threadIdx.x < len) fetch(threadIdx.x);
+    for (int k = threadIdx.x; k < 2 * p1; k += kSpread1Block) tre[k] = 0.0;
+    __syncthreads();
+    const T beta = (T)g.beta;
+    for (int i = threadIdx.x; i < len; i += kSpread1Block) {
+        const T xc = xn;
+        const cplx<T> cv = cn;
+        if (i + kSpread1Block < len) fetch(i + kSpread1Block);
+        double t = grid_t((double)xc, g.s[0]);
+        int l;
+        fold_t(t, g.n[0], l);
+        T ker[W];
+        int l0 = es_weights<T, W>(t, beta, ker) - origin;
+        l0 = min(max(l0, 0), p1 - W);
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+            atomicAdd(tre + l0 + q, (double)(cv.re * ker[q]));
+            atomicAdd(tim + l0 + q, (double)(cv.im * ker[q]));
+        }
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < p1; k += kSpread1Block) {
+        const double re = tre[k], im = tim[k];
+        if (re == 0.0 && im == 0.0) continue;
+        const int gi = wrap_grid(origin + k, g.n[0]);
+        unsafeAtomicAdd(&grid[gi].re, (T)re);
+        unsafeAtomicAdd(&grid[gi].im, (T)im);
+    }
+}
+
 template <typename T, int DIM, int W>
 __global__ void __launch_bounds__(kGmBlock) k_spread_gm(GeomArgs g, const cplx<T>* __restrict__ c,
                                                         cplx<T>* __restrict__ grid) {
@@ -816,6 +875,14 @@ __global__ void __launch_bounds__(kGmBlock) k_spread_gm(GeomArgs g, const cplx<T
         }
     }
     const cplx<T> v = c[g.cperm ? g.cperm[i] : i];
+    if constexpr (DIM == 1) {
+#pragma unroll
+        for (int q1 = 0; q1 < W; ++q1) {
+            unsafeAtomicAdd(&grid[idx[0][q1]].re, v.re * ker[0][q1]);
+            unsafeAtomicAdd(&grid[idx[0][q1]].im, v.im * ker[0][q1]);
+        }
+        return;
+    } else {
     const int n1 = g.n[0], n2 = g.n[1];
 #pragma unroll
     for (int q3 = 0; q3 < (DIM == 3 ? W : 1); ++q3) {
@@ -834,6 +901,7 @@ __global__ void __launch_bounds__(kGmBlock) k_spread_gm(GeomArgs g, const cplx<T
                 unsafeAtomicAdd(&dst[idx[0][q1]].im, vim * ker[0][q1]);
             }
         }
+    }
     }
 }
 
@@ -862,6 +930,21 @@ hipError_t spread_w(int method, const GeomArgs& g, const void* c, void* grid, hi
         return hipGetLastError();
     }
     if (g.nsub <= 0) return hipSuccess;
+    if constexpr (DIM == 1) {
+        const int p1 = g.m[0] + W;
+        const size_t lds = (size_t)p1 * 2 * sizeof(double);
+        if (lds > spread_lds_limit()) return hipErrorInvalidConfiguration;
+        static bool attr_set1 = false;
+        if (!attr_set1) {
+            hipError_t e = hipFuncSetAttribute((const void*)k_spread_sm1<T, W>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)spread_lds_limit());
+            if (e != hipSuccess) return e;
+            attr_set1 = true;
+        }
+        k_spread_sm1<T, W><<<dim3((unsigned)g.nsub), kSpread1Block, lds, st>>>(g, (const cplx<T>*)c,
+                                                                              (cplx<T>*)grid, p1);
+        return hipGetLastError();
+    } else {
     const int p1 = g.m[0] + W, p2 = g.m[1] + W, p3 = (DIM == 3) ? g.m[2] + W : 1;
     const int pc = tile_row_pitch(p1, W);
     const size_t lds = (size_t)pc * p2 * p3 * 2 * sizeof(double) + sizeof(Stage<T, DIM, W>);
@@ -877,6 +960,7 @@ hipError_t spread_w(int method, const GeomArgs& g, const void* c, void* grid, hi
     k_spread_sm<T, DIM, W><<<dim3((unsigned)g.nsub), kSpreadBlock, lds, st>>>(
         g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2, p3, pc);
     return hipGetLastError();
+    }
 }
 
 template <typename T, int DIM>
@@ -908,6 +992,7 @@ size_t stage_bytes_dim(int w) {
 size_t spread_lds_limit() { return 160 * 1024; }
 
 size_t spread_tile_bytes(int prec, int dim, int w, const int* m) {
+    if (dim == 1) return (size_t)(m[0] + w) * 2 * sizeof(double);
     size_t cells = (size_t)tile_row_pitch(m[0] + w, w);
     for (int i = 1; i < dim; ++i) cells *= (size_t)(m[i] + w);
     size_t stage = (prec == 0) ? (dim == 2 ? stage_bytes_dim<float, 2>(w) : stage_bytes_dim<float, 3>(w))
@@ -954,10 +1039,12 @@ hipError_t launch_spread(int prec, int method, const GeomArgs& g_in, const void*
     }
     if (columns && method == NUFFT_METHOD_SM)
         return prec == 0 ? spread_col<float>(g, c, grid, st) : spread_col<double>(g, c, grid, st);
-    if (prec == 0) return g.dim == 2 ? spread_dim<float, 2>(method, g, c, grid, st)
-                                     : spread_dim<float, 3>(method, g, c, grid, st);
-    return g.dim == 2 ? spread_dim<double, 2>(method, g, c, grid, st)
-                      : spread_dim<double, 3>(method, g, c, grid, st);
+    if (prec == 0) return g.dim == 1 ? spread_dim<float, 1>(method, g, c, grid, st)
+                          : g.dim == 2 ? spread_dim<float, 2>(method, g, c, grid, st)
+                                       : spread_dim<float, 3>(method, g, c, grid, st);
+    return g.dim == 1 ? spread_dim<double, 1>(method, g, c, grid, st)
+           : g.dim == 2 ? spread_dim<double, 2>(method, g, c, grid, st)
+                        : spread_dim<double, 3>(method, g, c, grid, st);
 }
 
 }  // namespace nufft

@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for the 2D/3D type 1 / type 2 NUFFT.
+"""Seeded synthetic workloads for the 1D/2D/3D type 1 / type 2 NUFFT.
 
 This module only draws random inputs and names problem sizes.  It holds none
 of the transform's arithmetic, so both the CPU oracle's tests and the GPU path
@@ -62,6 +62,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     _w("3d_n128_m16m_f32_e5", 3, 128, 16_777_216, 1e-5, "f32", seed=1003),
     _w("3d_n128_m16m_f32_e5_cluster", 3, 128, 16_777_216, 1e-5, "f32", dist="cluster", seed=1004),
     _w("3d_n256_m134m_f64_e9", 3, 256, 134_217_728, 1e-9, "f64", seed=1005),
+    # 1D (the FINUFFT discussion page reports 1D throughputs at tolerance 1e-6 without sizes)
+    _w("1d_n1m_m16m_f32_e6", 1, 1 << 20, 1 << 24, 1e-6, "f32", seed=1006),
+    _w("1d_n1m_m16m_f64_e6", 1, 1 << 20, 1 << 24, 1e-6, "f64", seed=1006),
 ]}
 
 

@@ -1,4 +1,4 @@
-"""CPU oracle for the 2D/3D type 1 / type 2 NUFFT -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the 1D/2D/3D type 1 / type 2 NUFFT -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  The GPU library never imports, links or calls it, and the two

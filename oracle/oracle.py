@@ -1,4 +1,4 @@
-"""Plain CPU oracle for the 2D/3D type 1 and type 2 NUFFT (fp64).
+"""Plain CPU oracle for the 1D/2D/3D type 1 and type 2 NUFFT (fp64).
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
 benchmark's CPU-baseline leg, never by the GPU library.  It shares no code

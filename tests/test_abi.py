@@ -42,7 +42,7 @@ def test_host_side_argument_checks():
     assert lib.nufft_destroy(None) == 0
     N = (ctypes.c_int64 * 3)(16, 16, 16)
     h = ctypes.c_void_p()
-    bad = [(3, 2, N, 1e-5, 0), (1, 4, N, 1e-5, 0), (1, 2, N, 0.0, 0), (1, 2, N, -1.0, 0),
+    bad = [(3, 2, N, 1e-5, 0), (1, 4, N, 1e-5, 0), (1, 0, N, 1e-5, 0), (1, 2, N, 0.0, 0), (1, 2, N, -1.0, 0),
            (1, 2, N, float("nan"), 0), (1, 2, N, 1e-5, 2), (1, 2, None, 1e-5, 0),
            (2, 3, (ctypes.c_int64 * 3)(16, 0, 16), 1e-5, 1)]
     for t, d, n, e, p in bad:

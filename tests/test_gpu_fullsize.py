@@ -65,6 +65,8 @@ CONFIGS = [
     ("3d_n128_m16m_f32_e5", 24, 48),
     ("3d_n128_m16m_f32_e5_cluster", 24, 48),
     ("3d_n256_m134m_f64_e9", 8, 24),
+    ("1d_n1m_m16m_f32_e6", 48, 48),
+    ("1d_n1m_m16m_f64_e6", 48, 48),
 ]
 
 

@@ -50,6 +50,9 @@ SORT_CASES = [
     ("3d_cluster_f32", Workload("s", 3, (32, 32, 32), 60_000, 1e-5, "f32", dist="cluster", seed=24)),
     ("3d_box_f64", Workload("s", 3, (16, 16, 16), 20_000, 1e-9, "f64", dist="box", seed=25)),
     ("2d_tiny", Workload("s", 2, (5, 7), 3, 1e-3, "f32", seed=26)),
+    ("1d_uniform_f32", Workload("s", 1, (1000,), 50_001, 1e-5, "f32", seed=27)),
+    ("1d_cluster_f64", Workload("s", 1, (777,), 30_000, 1e-12, "f64", dist="cluster", seed=28)),
+    ("1d_large_f32", Workload("s", 1, (1 << 16,), 200_000, 1e-6, "f32", seed=29)),
 ]
 
 
@@ -132,6 +135,9 @@ STEP_CASES = [
     Workload("st", 3, (16, 16, 16), 20_000, 1e-2, "f32", seed=34),
     Workload("st", 3, (20, 16, 12), 15_000, 1e-9, "f64", seed=35),
     Workload("st", 3, (16, 16, 16), 30_000, 1e-5, "f32", dist="box", seed=36),
+    Workload("st", 1, (1000,), 50_001, 1e-5, "f32", seed=37),
+    Workload("st", 1, (777,), 30_000, 1e-12, "f64", seed=38),
+    Workload("st", 1, (4096,), 40_000, 1e-6, "f32", dist="box", seed=39),
 ]
 
 
@@ -180,7 +186,7 @@ def test_interp_step(nf, orc, wl, method):
 
 
 @pytest.mark.parametrize("N,prec", [((100, 72), "f32"), ((33, 17), "f64"), ((24, 20, 18), "f32"),
-                                    ((9, 16, 7), "f64")])
+                                    ((9, 16, 7), "f64"), ((1000,), "f32"), ((777,), "f64")])
 def test_correction_steps(nf, orc, N, prec):
     eps = 1e-5 if prec == "f32" else 1e-11
     prm = orc.Params(N, eps)
@@ -221,6 +227,10 @@ E2E_CASES = [
     Workload("e", 3, (20, 16, 12), 15_000, 1e-9, "f64", seed=47),
     Workload("e", 3, (16, 16, 16), 30_000, 1e-5, "f32", dist="box", seed=48),
     Workload("e", 3, (9, 16, 7), 2_000, 1e-12, "f64", seed=49),
+    Workload("e", 1, (1024,), 100_000, 1e-5, "f32", seed=40),
+    Workload("e", 1, (999,), 20_000, 1e-12, "f64", seed=401),
+    Workload("e", 1, (5000,), 60_000, 1e-6, "f32", dist="cluster", seed=402),
+    Workload("e", 1, (64,), 1_000, 1e-2, "f32", seed=403),
 ]
 
 
@@ -254,7 +264,8 @@ def test_small_config_vs_exact_sums(nf, orc):
     assert orc.rel_l2(c, orc.direct_type2(inp["X"], inp["f"], wl.N)) <= 10 * wl.eps
 
 
-@pytest.mark.parametrize("N,prec,eps", [((64, 64), "f32", 1e-5), ((24, 20, 18), "f64", 1e-12)])
+@pytest.mark.parametrize("N,prec,eps", [((64, 64), "f32", 1e-5), ((24, 20, 18), "f64", 1e-12),
+                                         ((3000,), "f32", 1e-6), ((1001,), "f64", 1e-12)])
 def test_adjointness_on_gpu(nf, N, prec, eps):
     """<type1(c), f> = <c, type2(f)> (the steps are exact transposes)."""
     wl = Workload("a", len(N), N, 20_000, eps, prec, seed=51)
@@ -276,6 +287,19 @@ def test_methods_agree_and_caps(nf, orc):
                {"method": 2, "bins": (8, 8, 8)}, {"method": 2, "bins": (4, 8, 16)}):
         f = gpu_type1(nf, inp["X"], inp["c"], wl.N, wl.eps, wl.precision, **kw)
         assert orc.rel_l2(f, ref) <= 1e-5, kw
+
+
+def test_empty_and_single_point_1d(nf, orc):
+    for prec in ("f32", "f64"):
+        rd = np.float32 if prec == "f32" else np.float64
+        cd = np.complex64 if prec == "f32" else np.complex128
+        f = gpu_type1(nf, [np.zeros(0, rd)], np.zeros(0, cd), (40,), 1e-6, prec)
+        assert np.all(f == 0)
+        for x0 in (-math.pi, 0.3, np.nextafter(math.pi, 0)):
+            X1 = [np.array([x0]).astype(rd)]
+            f = gpu_type1(nf, X1, np.ones(1, cd), (41,), 1e-6, prec)
+            ref = orc.nufft_type1(X1, np.ones(1, complex), (41,), 1e-6)
+            assert orc.rel_l2(f, ref) <= tol_for(prec)
 
 
 def test_empty_and_single_point(nf, orc):
@@ -385,8 +409,9 @@ def test_column_kernel_widths(nf, orc, prec, eps):
 
 @pytest.mark.parametrize("wl", [Workload("gm", 3, (24, 20, 18), 30_000, 1e-5, "f32", seed=91),
                                 Workload("gm", 2, (48, 40), 20_000, 1e-12, "f64", seed=92),
-                                Workload("gm", 3, (20, 16, 12), 10_000, 1e-9, "f64", dist="cluster", seed=93)],
-                         ids=["3d_f32", "2d_f64", "3d_f64_cluster"])
+                                Workload("gm", 3, (20, 16, 12), 10_000, 1e-9, "f64", dist="cluster", seed=93),
+                                Workload("gm", 1, (3000,), 50_000, 1e-6, "f32", seed=94)],
+                         ids=["3d_f32", "2d_f64", "3d_f64_cluster", "1d_f32"])
 def test_gm_method(nf, orc, wl):
     """GM (Sec. III-A): setpts keeps the caller's order (identity permutation, no subproblems, no
     binning: the bin counts read zero); type 1 and the adjoint type 2 match the oracle NUFFT."""
