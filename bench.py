@@ -159,6 +159,56 @@ def compare_methods(steps, workloads):
                 print(json.dumps({"workload": name, "method": mname, "type": typ, **res}), flush=True)
 
 
+def many_vectors(steps, nvec, workloads):
+    """Many-vector execution on one setpts: per workload, nvec type 1 + adjoint type 2 pairs as
+    nvec single executes and as one execute_many + execute_adjoint_many; one JSON line each with
+    the time per vector pair and NU points/s (points already set, inputs in HBM)."""
+    import numpy as np
+    import torch
+
+    import nonuniform_fft_amd as nf
+    from nonuniform_fft_amd.workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    for name in workloads:
+        wl = WORKLOADS[name]
+        X = [torch.from_numpy(x).to(dev) for x in make_inputs(wl, want_c=False, want_f=False)["X"]]
+        rng = np.random.default_rng(5)
+        cdt = torch.complex64 if wl.precision == "f32" else torch.complex128
+        fshape = (nvec,) + tuple(reversed(wl.N))
+        c_in = torch.complex(torch.from_numpy(rng.standard_normal((nvec, wl.M))),
+                             torch.from_numpy(rng.standard_normal((nvec, wl.M)))).to(cdt).to(dev)
+        f_in = torch.complex(torch.from_numpy(rng.standard_normal(fshape)),
+                             torch.from_numpy(rng.standard_normal(fshape))).to(cdt).to(dev)
+        f_out = torch.empty(fshape, dtype=cdt, device=dev)
+        c_out = torch.empty((nvec, wl.M), dtype=cdt, device=dev)
+        plan = nf.Plan(1, wl.N, wl.eps, wl.precision)
+        plan.setpts(*X)
+
+        def single():
+            for v in range(nvec):
+                plan.execute(c_in[v], f_out[v])
+                plan.execute_adjoint(c_out[v], f_in[v])
+
+        def many():
+            plan.execute_many(c_in, f_out)
+            plan.execute_adjoint_many(c_out, f_in)
+
+        res = {}
+        for key, fn in (("single", single), ("many", many)):
+            fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / (steps * nvec)
+            res[key] = {"ms_per_vector_pair": ms, "pts_per_s": wl.M / (ms * 1e-3)}
+        plan.destroy()
+        print(json.dumps({"workload": name, "nvec": nvec, **res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,7 +222,13 @@ def main():
                     help="only run a plain copy of this many bytes (counter calibration)")
     ap.add_argument("--compare", action="store_true",
                     help="only compare the GM, GM-sort and SM methods (JSON line per method and type)")
+    ap.add_argument("--many", type=int, default=0,
+                    help="only time many-vector execution with this many vectors per call")
     args = ap.parse_args()
+    if args.many:
+        many_vectors(args.steps, args.many, ["2d_n64_m1e4_f32_e5", "2d_n1024_m4m_f32_e5", "3d_n128_m16m_f32_e5",
+                                             "1d_n1m_m16m_f32_e6"])
+        return
     if args.probe_copy:
         probe_copy(args.probe_copy)
         return

@@ -72,6 +72,7 @@ typedef struct {
     int subproblem_cap;       /* max points per subproblem; 0 = default */
     size_t max_device_bytes;  /* 0 = no limit; otherwise plan-owned device memory above this fails */
     int timing;               /* 1 = record per-stage HIP-event times (see nufft_get_stage_times) */
+    int max_batch;            /* vectors per batch in nufft_execute_many; 0 = automatic */
 } nufft_opts;
 
 /* Fill *opts with defaults (all zero = automatic choices).  NUFFT_ERR_BAD_ARG if opts is NULL. */
@@ -124,6 +125,22 @@ int nufft_execute(nufft_plan plan, void* c, void* f);
  * conventions and errors as nufft_execute.
  */
 int nufft_execute_adjoint(nufft_plan plan, void* c, void* f);
+
+/*
+ * Many-vector execution on the points of the last setpts (the paper's use case of new
+ * strength vectors on the same sorted points, Sec. I-A): nvec >= 1 transforms of the plan's
+ * type, vector v reading c + v*M / f + v*prod(N) and writing the other (c holds nvec*M complex
+ * values, f nvec*prod(N), both vector-major).  Vectors run in batches: every step of a batch is
+ * one launch over all its vectors (blockIdx.y = vector) into a batch of fine grids, and the FFT
+ * is one batched rocFFT call.  The batch size is opts.max_batch, or automatic (at most 16
+ * vectors and about 2 GiB of batch grids); batch grids are plan-owned and kept for later calls.
+ * Per-stage times (opts.timing) cover the last batch.  Errors as nufft_execute, plus
+ * NUFFT_ERR_BAD_ARG for nvec < 1.
+ */
+int nufft_execute_many(nufft_plan plan, int nvec, void* c, void* f);
+
+/* The adjoint transform of nufft_execute_adjoint for nvec vectors, as nufft_execute_many. */
+int nufft_execute_adjoint_many(nufft_plan plan, int nvec, void* c, void* f);
 
 /* Free everything the plan owns (waits for its stream first).  NULL is accepted. */
 int nufft_destroy(nufft_plan plan);

@@ -22,7 +22,7 @@ _D = ctypes.c_double
 
 class NufftOpts(ctypes.Structure):
     _fields_ = [("method", ctypes.c_int), ("bin", ctypes.c_int * 3), ("subproblem_cap", ctypes.c_int),
-                ("max_device_bytes", ctypes.c_size_t), ("timing", ctypes.c_int)]
+                ("max_device_bytes", ctypes.c_size_t), ("timing", ctypes.c_int), ("max_batch", ctypes.c_int)]
 
 
 SIGNATURES = {
@@ -32,6 +32,8 @@ SIGNATURES = {
     "nufft_setpts": (_I, [_P, _L, _P, _P, _P]),
     "nufft_execute": (_I, [_P, _P, _P]),
     "nufft_execute_adjoint": (_I, [_P, _P, _P]),
+    "nufft_execute_many": (_I, [_P, _I, _P, _P]),
+    "nufft_execute_adjoint_many": (_I, [_P, _I, _P, _P]),
     "nufft_destroy": (_I, [_P]),
     "nufft_strerror": (ctypes.c_char_p, [_I]),
     "nufft_last_error": (ctypes.c_char_p, [_P]),
@@ -107,7 +109,8 @@ class Plan:
 
     def __init__(self, nufft_type: int, N: Sequence[int], eps: float, precision: str = "f32",
                  stream=None, method: int = METHOD_AUTO, bins: Optional[Sequence[int]] = None,
-                 subproblem_cap: int = 0, timing: bool = False, max_device_bytes: int = 0):
+                 subproblem_cap: int = 0, timing: bool = False, max_device_bytes: int = 0,
+                 max_batch: int = 0):
         lib = load_library()
         torch = _torch()
         if precision not in ("f32", "f64"):
@@ -127,6 +130,7 @@ class Plan:
         opts.subproblem_cap = int(subproblem_cap)
         opts.timing = 1 if timing else 0
         opts.max_device_bytes = int(max_device_bytes)
+        opts.max_batch = int(max_batch)
         if stream is None:
             stream = torch.cuda.current_stream()
         self._stream_obj = stream
@@ -229,6 +233,28 @@ class Plan:
         cp = self._dev_tensor(c, cd, self.M, "c")
         fp = self._dev_tensor(f, cd, self.nmodes, "f")
         self._check(self._lib.nufft_execute_adjoint(self._h, cp, fp))
+        return c if self.type == 1 else f
+
+    def _many(self, fn, c, f):
+        if self.M < 0:
+            raise NufftError(NUFFT_ERR_BAD_STATE, "setpts first")
+        nvec = c.shape[0] if c.dim() > 1 else 1
+        if f.shape[0] != nvec or c.dim() != 2 or f.dim() != self.dim + 1:
+            raise ValueError("c must be (nvec, M) and f (nvec, N3, N2, N1)-shaped with the same nvec")
+        cd = _complex_dtype(self.prec)
+        cp = self._dev_tensor(c, cd, nvec * self.M, "c")
+        fp = self._dev_tensor(f, cd, nvec * self.nmodes, "f")
+        self._check(fn(self._h, nvec, cp, fp))
+
+    def execute_many(self, c, f):
+        """nvec transforms of the plan's type on the same points: c (nvec, M), f (nvec, *N
+        reversed); type 1 writes f, type 2 writes c."""
+        self._many(self._lib.nufft_execute_many, c, f)
+        return f if self.type == 1 else c
+
+    def execute_adjoint_many(self, c, f):
+        """nvec adjoint transforms on the same points (type 2 for a type 1 plan, and back)."""
+        self._many(self._lib.nufft_execute_adjoint_many, c, f)
         return c if self.type == 1 else f
 
     def spread(self, c, grid):

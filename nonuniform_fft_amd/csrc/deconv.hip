@@ -15,6 +15,9 @@ __global__ void __launch_bounds__(kBlock) k_deconvolve(int N1, int N2, int N3, i
                                                        const T* __restrict__ p,
                                                        const cplx<T>* __restrict__ fhat,
                                                        cplx<T>* __restrict__ f) {
+    // vector blockIdx.y of a many-vector launch
+    fhat += (int64_t)blockIdx.y * n1 * n2 * n3;
+    f += (int64_t)blockIdx.y * N1 * N2 * N3;
     const int64_t total = (int64_t)N1 * N2 * N3;
     const int64_t pos = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (pos >= total) return;
@@ -41,6 +44,9 @@ __global__ void __launch_bounds__(kBlock) k_precorrect_pad(int N1, int N2, int N
                                                            const T* __restrict__ p,
                                                            const cplx<T>* __restrict__ f,
                                                            cplx<T>* __restrict__ fhat) {
+    // vector blockIdx.y of a many-vector launch
+    fhat += (int64_t)blockIdx.y * n1 * n2 * n3;
+    f += (int64_t)blockIdx.y * N1 * N2 * N3;
     const int64_t total = (int64_t)n1 * n2 * n3;
     const int64_t cell = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (cell >= total) return;
@@ -73,11 +79,11 @@ __global__ void __launch_bounds__(kBlock) k_precorrect_pad(int N1, int N2, int N
 }  // namespace
 
 hipError_t launch_deconvolve(int prec, int dim, const int64_t* N, const int64_t* n, const void* pcorr,
-                             const void* fhat, void* f, hipStream_t st) {
+                             const void* fhat, void* f, hipStream_t st, int nv) {
     int N3 = dim == 3 ? (int)N[2] : 1, n3 = dim == 3 ? (int)n[2] : 1;
     int64_t total = N[0] * N[1] * (int64_t)N3;
     if (total == 0) return hipSuccess;
-    dim3 g((unsigned)((total + kBlock - 1) / kBlock));
+    dim3 g((unsigned)((total + kBlock - 1) / kBlock), (unsigned)nv);
     if (prec == 0) {
         if (dim <= 2) k_deconvolve<float, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const float*)pcorr, (const cplx<float>*)fhat, (cplx<float>*)f);
         else k_deconvolve<float, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, (const float*)pcorr, (const cplx<float>*)fhat, (cplx<float>*)f);
@@ -89,10 +95,10 @@ hipError_t launch_deconvolve(int prec, int dim, const int64_t* N, const int64_t*
 }
 
 hipError_t launch_precorrect_pad(int prec, int dim, const int64_t* N, const int64_t* n, const void* pcorr,
-                                 const void* f, void* fhat, hipStream_t st) {
+                                 const void* f, void* fhat, hipStream_t st, int nv) {
     int N3 = dim == 3 ? (int)N[2] : 1, n3 = dim == 3 ? (int)n[2] : 1;
     int64_t total = n[0] * n[1] * (int64_t)n3;
-    dim3 g((unsigned)((total + kBlock - 1) / kBlock));
+    dim3 g((unsigned)((total + kBlock - 1) / kBlock), (unsigned)nv);
     if (prec == 0) {
         if (dim <= 2) k_precorrect_pad<float, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const float*)pcorr, (const cplx<float>*)f, (cplx<float>*)fhat);
         else k_precorrect_pad<float, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, (const float*)pcorr, (const cplx<float>*)f, (cplx<float>*)fhat);

@@ -18,6 +18,9 @@ constexpr int kInterpBlock = 128;
 template <typename T, int DIM, int W>
 __global__ void __launch_bounds__(kInterpBlock) k_interp_gm(GeomArgs g, const cplx<T>* __restrict__ grid,
                                                             cplx<T>* __restrict__ c) {
+    // vector blockIdx.y of a many-vector launch (strides in complex values)
+    c += (int64_t)blockIdx.y * g.cvs;
+    grid += (int64_t)blockIdx.y * g.gvs;
     const int64_t i = (int64_t)blockIdx.x * kInterpBlock + threadIdx.x;
     if (i >= g.M) return;
     const T beta = (T)g.beta;
@@ -84,6 +87,9 @@ template <typename T, int DIM, int W>
 __global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs g, const cplx<T>* __restrict__ grid,
                                                               cplx<T>* __restrict__ c, int p1, int p2,
                                                               int p3) {
+    // vector blockIdx.y of a many-vector launch (strides in complex values)
+    c += (int64_t)blockIdx.y * g.cvs;
+    grid += (int64_t)blockIdx.y * g.gvs;
     extern __shared__ __align__(16) unsigned char smem[];
     cplx<T>* tile = (cplx<T>*)smem;
     const int pc = p1, pp = p1 * p2;
@@ -193,7 +199,7 @@ template <typename T, int DIM, int W>
 hipError_t interp_w(int method, const GeomArgs& g, const void* grid, void* c, hipStream_t st) {
     if (g.M <= 0) return hipSuccess;
     if (method == NUFFT_METHOD_GM_SORT || method == NUFFT_METHOD_GM) {
-        dim3 grd((unsigned)((g.M + kInterpBlock - 1) / kInterpBlock));
+        dim3 grd((unsigned)((g.M + kInterpBlock - 1) / kInterpBlock), (unsigned)g.nv);
         k_interp_gm<T, DIM, W><<<grd, kInterpBlock, 0, st>>>(g, (const cplx<T>*)grid, (cplx<T>*)c);
         return hipGetLastError();
     }
@@ -209,7 +215,7 @@ hipError_t interp_w(int method, const GeomArgs& g, const void* grid, void* c, hi
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_interp_sm<T, DIM, W><<<dim3((unsigned)g.nsub), (kInterpSmBlock<T, DIM>), lds, st>>>(
+    k_interp_sm<T, DIM, W><<<dim3((unsigned)g.nsub, (unsigned)g.nv), (kInterpSmBlock<T, DIM>), lds, st>>>(
         g, (const cplx<T>*)grid, (cplx<T>*)c, p1, p2, p3);
     return hipGetLastError();
 }

@@ -118,9 +118,15 @@ struct nufft_plan_s {
     size_t sort_tmp_cap = 0;
     size_t pts_cap = 0;                 // capacity (points) of xs / perm
 
+    // many-vector batches: nv fine grids, and (fp64) the strengths gathered in sorted order
+    nufft::DevBuf grid_many;
+    nufft::DevBuf c_many;
+
     // rocFFT
     rocfft_plan fft_fwd = nullptr;
     rocfft_plan fft_bwd = nullptr;
+    rocfft_plan fft_many[2] = {nullptr, nullptr};   // batched forward / backward
+    int fft_many_nv[2] = {0, 0};
     rocfft_execution_info fft_info = nullptr;
 
     // timing
@@ -186,20 +192,25 @@ struct GeomArgs {
     const int32_t* cperm;  // spreading reads strength cperm[j] for sorted point j; null: c is sorted
     const int32_t* sub;    // (bin, start, len)
     int64_t nsub;
+    // many-vector launches: nv vectors along blockIdx.y; vector v reads / writes c + v cvs and
+    // grid + v gvs (strides in complex values; nv = 1 for a single transform)
+    int nv;
+    int64_t cvs, gvs;
 };
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // columns: the points of each bin are in column order (3D), so the column-run kernel may run.
-// c_scratch: device scratch of at least M complex values (fp64 plans gather c into it in sorted
-// order before spreading).
+// c_scratch: device scratch of at least nv M complex values (fp64 plans gather c into it in
+// sorted order before spreading).
 hipError_t launch_spread(int prec, int method, const GeomArgs& g, const void* c, void* grid,
                          hipStream_t st, bool columns, void* c_scratch);
 hipError_t launch_interp(int prec, int method, const GeomArgs& g, const void* grid, void* c,
                          hipStream_t st);
 size_t interp_tile_bytes(int prec, int dim, int w, const int* m);
+// nv vectors: fhat holds nv fine grids, f nv mode arrays, back to back.
 hipError_t launch_deconvolve(int prec, int dim, const int64_t* N, const int64_t* n,
-                             const void* pcorr, const void* fhat, void* f, hipStream_t st);
+                             const void* pcorr, const void* fhat, void* f, hipStream_t st, int nv = 1);
 hipError_t launch_precorrect_pad(int prec, int dim, const int64_t* N, const int64_t* n,
-                                 const void* pcorr, const void* f, void* fhat, hipStream_t st);
+                                 const void* pcorr, const void* f, void* fhat, hipStream_t st, int nv = 1);
 // Largest LDS tile (bytes) the SM spreading kernel may use.
 size_t spread_lds_limit();
 size_t spread_tile_bytes(int prec, int dim, int w, const int* m);

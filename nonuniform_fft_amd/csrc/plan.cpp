@@ -234,6 +234,9 @@ nufft::GeomArgs geom(const nufft_plan p) {
     g.cperm = g.perm;
     g.sub = (const int32_t*)p->sub.p;
     g.nsub = p->nsub;
+    g.nv = 1;
+    g.cvs = std::max<int64_t>(p->M, 0);
+    g.gvs = grid_cells(p);
     return g;
 }
 
@@ -249,9 +252,15 @@ int fft_exec(nufft_plan plan, rocfft_plan fp, void* data) {
 }
 
 // rocFFT plan for one direction (forward for type 1, backward for type 2), in place,
-// unnormalised; the work buffer is shared by both directions and grown when needed.
-int make_fft_plan(nufft_plan plan, int direction) {
-    rocfft_plan& slot = (direction == 1) ? plan->fft_fwd : plan->fft_bwd;
+// unnormalised, over nv contiguous fine grids; the work buffer is shared by all plans and
+// grown when needed.
+int make_fft_plan(nufft_plan plan, int direction, int nv = 1) {
+    rocfft_plan& slot = (nv == 1) ? ((direction == 1) ? plan->fft_fwd : plan->fft_bwd)
+                                  : plan->fft_many[direction - 1];
+    if (nv > 1 && plan->fft_many_nv[direction - 1] != nv && slot) {
+        rocfft_plan_destroy(slot);
+        slot = nullptr;
+    }
     if (slot) return NUFFT_OK;
     std::call_once(g_rocfft_once, [] { g_rocfft_setup = rocfft_setup(); });
     if (g_rocfft_setup != rocfft_status_success) return fail(plan, NUFFT_ERR_FFT, "rocfft_setup failed");
@@ -260,10 +269,11 @@ int make_fft_plan(nufft_plan plan, int direction) {
     rocfft_transform_type tt = (direction == 1) ? rocfft_transform_type_complex_forward
                                                 : rocfft_transform_type_complex_inverse;
     rocfft_plan fp = nullptr;
-    if (rocfft_plan_create(&fp, rocfft_placement_inplace, tt, fprec, (size_t)plan->dim, lengths, 1, nullptr) !=
-        rocfft_status_success)
+    if (rocfft_plan_create(&fp, rocfft_placement_inplace, tt, fprec, (size_t)plan->dim, lengths, (size_t)nv,
+                           nullptr) != rocfft_status_success)
         return fail(plan, NUFFT_ERR_FFT, "rocfft_plan_create failed");
     slot = fp;
+    if (nv > 1) plan->fft_many_nv[direction - 1] = nv;
     if (!plan->fft_info) {
         if (rocfft_execution_info_create(&plan->fft_info) != rocfft_status_success)
             return fail(plan, NUFFT_ERR_FFT, "rocfft_execution_info_create failed");
@@ -286,41 +296,84 @@ int make_fft_plan(nufft_plan plan, int direction) {
 // [8..11] the type 2 steps (pad, FFT, interp), [5..6] the sort.
 enum { EV_T1 = 0, EV_SORT0 = 5, EV_SORT1 = 6, EV_T2 = 8 };
 
-// Type 1 on the plan's points: c (M) -> f (N^d).
-int run_type1(nufft_plan plan, const void* c, void* f) {
-    int rc;
-    if ((rc = make_fft_plan(plan, 1)) != NUFFT_OK) return rc;
-    nufft::GeomArgs g = geom(plan);
+// Fine grids (and fp64 gather scratch) for one batch of nv vectors: the plan's own buffers for
+// nv = 1, the many-vector buffers otherwise.
+int batch_buffers(nufft_plan plan, int nv, void** grid, void** cscratch) {
+    if (nv == 1) {
+        *grid = plan->grid.p;
+        *cscratch = plan->sort_tmp.p;
+        return NUFFT_OK;
+    }
     const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan);
+    int rc;
+    if ((rc = dev_alloc(plan, plan->grid_many, gbytes * nv, "many-vector fine grids")) != NUFFT_OK) return rc;
+    if (plan->prec == 1 && plan->M > 0 &&
+        (rc = dev_alloc(plan, plan->c_many, (size_t)plan->M * 16 * nv, "many-vector strengths")) != NUFFT_OK)
+        return rc;
+    *grid = plan->grid_many.p;
+    *cscratch = plan->prec == 1 ? plan->c_many.p : plan->sort_tmp.p;
+    return NUFFT_OK;
+}
+
+// Type 1 on the plan's points for nv vectors: c (nv x M) -> f (nv x N^d).
+int run_type1(nufft_plan plan, const void* c, void* f, int nv = 1) {
+    int rc;
+    if ((rc = make_fft_plan(plan, 1, nv)) != NUFFT_OK) return rc;
+    void *grid, *cs;
+    if ((rc = batch_buffers(plan, nv, &grid, &cs)) != NUFFT_OK) return rc;
+    nufft::GeomArgs g = geom(plan);
+    g.nv = nv;
+    const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan) * nv;
     record(plan, EV_T1 + 0);
-    NUFFT_HIP(nufft::launch_fill_zero(plan->grid.p, gbytes, plan->stream));
+    NUFFT_HIP(nufft::launch_fill_zero(grid, gbytes, plan->stream));
     record(plan, EV_T1 + 1);
-    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, plan->grid.p, plan->stream, plan->colw > 0,
-                                   plan->sort_tmp.p));
+    NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, grid, plan->stream, plan->colw > 0, cs));
     record(plan, EV_T1 + 2);
-    if ((rc = fft_exec(plan, plan->fft_fwd, plan->grid.p)) != NUFFT_OK) return rc;
+    if ((rc = fft_exec(plan, nv == 1 ? plan->fft_fwd : plan->fft_many[0], grid)) != NUFFT_OK) return rc;
     record(plan, EV_T1 + 3);
-    NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, plan->grid.p, f,
-                                       plan->stream));
+    NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, grid, f,
+                                       plan->stream, nv));
     record(plan, EV_T1 + 4);
     plan->stage_recorded |= 1;
     return NUFFT_OK;
 }
 
-// Type 2 on the plan's points: f (N^d) -> c (M).
-int run_type2(nufft_plan plan, void* c, const void* f) {
+// Type 2 on the plan's points for nv vectors: f (nv x N^d) -> c (nv x M).
+int run_type2(nufft_plan plan, void* c, const void* f, int nv = 1) {
     int rc;
-    if ((rc = make_fft_plan(plan, 2)) != NUFFT_OK) return rc;
+    if ((rc = make_fft_plan(plan, 2, nv)) != NUFFT_OK) return rc;
+    void *grid, *cs;
+    if ((rc = batch_buffers(plan, nv, &grid, &cs)) != NUFFT_OK) return rc;
     nufft::GeomArgs g = geom(plan);
+    g.nv = nv;
     record(plan, EV_T2 + 0);
-    NUFFT_HIP(nufft::launch_precorrect_pad(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, f, plan->grid.p,
-                                           plan->stream));
+    NUFFT_HIP(nufft::launch_precorrect_pad(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, f, grid,
+                                           plan->stream, nv));
     record(plan, EV_T2 + 1);
-    if ((rc = fft_exec(plan, plan->fft_bwd, plan->grid.p)) != NUFFT_OK) return rc;
+    if ((rc = fft_exec(plan, nv == 1 ? plan->fft_bwd : plan->fft_many[1], grid)) != NUFFT_OK) return rc;
     record(plan, EV_T2 + 2);
-    NUFFT_HIP(nufft::launch_interp(plan->prec, plan->method, g, plan->grid.p, c, plan->stream));
+    NUFFT_HIP(nufft::launch_interp(plan->prec, plan->method, g, grid, c, plan->stream));
     record(plan, EV_T2 + 3);
     plan->stage_recorded |= 2;
+    return NUFFT_OK;
+}
+
+// nvec transforms of the given type in batches (see nufft_execute_many).
+int run_many(nufft_plan plan, int type, int nvec, void* c, void* f) {
+    const size_t cbytes = (size_t)std::max<int64_t>(plan->M, 0) * 2 * real_size(plan);
+    const size_t fbytes = (size_t)mode_count(plan) * 2 * real_size(plan);
+    int b = plan->opts.max_batch > 0 ? plan->opts.max_batch : 16;
+    if (plan->opts.max_batch <= 0) {
+        const size_t per = (size_t)grid_cells(plan) * 2 * real_size(plan) + (plan->prec == 1 ? cbytes : 0);
+        while (b > 1 && (size_t)b * per > (size_t(2) << 30)) --b;
+    }
+    for (int v0 = 0; v0 < nvec; v0 += b) {
+        const int nv = std::min(b, nvec - v0);
+        char* cv = (char*)c + (size_t)v0 * cbytes;
+        char* fv = (char*)f + (size_t)v0 * fbytes;
+        int rc = type == 1 ? run_type1(plan, cv, fv, nv) : run_type2(plan, cv, fv, nv);
+        if (rc != NUFFT_OK) return rc;
+    }
     return NUFFT_OK;
 }
 
@@ -366,9 +419,11 @@ int nufft_destroy(nufft_plan plan) {
     (void)hipStreamSynchronize(plan->stream);
     if (plan->fft_fwd) rocfft_plan_destroy(plan->fft_fwd);
     if (plan->fft_bwd) rocfft_plan_destroy(plan->fft_bwd);
+    for (rocfft_plan fp : plan->fft_many)
+        if (fp) rocfft_plan_destroy(fp);
     if (plan->fft_info) rocfft_execution_info_destroy(plan->fft_info);
     for (DevBuf* b : {&plan->grid, &plan->pcorr, &plan->fft_work, &plan->xs, &plan->perm, &plan->counts,
-                      &plan->offsets, &plan->sub, &plan->sort_tmp})
+                      &plan->offsets, &plan->sub, &plan->sort_tmp, &plan->grid_many, &plan->c_many})
         dev_free(plan, *b);
     if (plan->ev_ok)
         for (auto& e : plan->ev) (void)hipEventDestroy(e);
@@ -616,6 +671,24 @@ int nufft_execute_adjoint(nufft_plan plan, void* c, void* f) {
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
     if ((plan->M > 0 && !c) || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
     return plan->type == 1 ? run_type2(plan, c, f) : run_type1(plan, c, f);
+}
+
+int nufft_execute_many(nufft_plan plan, int nvec, void* c, void* f) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    int rc;
+    if ((rc = check_points(plan)) != NUFFT_OK) return rc;
+    if (nvec < 1) return fail(plan, NUFFT_ERR_BAD_ARG, "nvec must be >= 1");
+    if ((plan->M > 0 && !c) || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
+    return run_many(plan, plan->type, nvec, c, f);
+}
+
+int nufft_execute_adjoint_many(nufft_plan plan, int nvec, void* c, void* f) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    int rc;
+    if ((rc = check_points(plan)) != NUFFT_OK) return rc;
+    if (nvec < 1) return fail(plan, NUFFT_ERR_BAD_ARG, "nvec must be >= 1");
+    if ((plan->M > 0 && !c) || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
+    return run_many(plan, plan->type == 1 ? 2 : 1, nvec, c, f);
 }
 
 int nufft_get_stage_times(nufft_plan plan, double* ms) {

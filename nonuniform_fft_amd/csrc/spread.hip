@@ -78,6 +78,9 @@ template <typename T, int DIM, int W>
 __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c,
                                                             cplx<T>* __restrict__ grid, int p1, int p2,
                                                             int p3, int pc) {
+    // vector blockIdx.y of a many-vector launch (strides in complex values)
+    c += (int64_t)blockIdx.y * g.cvs;
+    grid += (int64_t)blockIdx.y * g.gvs;
     using St = Stage<T, DIM, W>;
     constexpr int CH = St::CH;
     constexpr int WW = W * W;
@@ -306,6 +309,9 @@ struct ColPt {
 template <typename T, int W>
 __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
                                                                      cplx<T>* __restrict__ grid, int p1, int p2) {
+    // vector blockIdx.y of a many-vector launch (strides in complex values)
+    c += (int64_t)blockIdx.y * g.cvs;
+    grid += (int64_t)blockIdx.y * g.gvs;
     using C = ColCfg<T, W>;
     using St = ColStage<T, W>;
     constexpr int Z = C::kZ;
@@ -522,6 +528,9 @@ struct WgStage {
 template <typename T, int W>
 __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g, const cplx<T>* __restrict__ c,
                                                                         cplx<T>* __restrict__ grid, int p1, int p2) {
+    // vector blockIdx.y of a many-vector launch (strides in complex values)
+    c += (int64_t)blockIdx.y * g.cvs;
+    grid += (int64_t)blockIdx.y * g.gvs;
     using C = ColCfg<T, W>;
     using St = WgStage<T, W>;
     constexpr int Z = C::kZ;
@@ -775,10 +784,10 @@ hipError_t spread_col_w(const GeomArgs& g, const void* c, void* grid, hipStream_
         attr_set = true;
     }
     if constexpr (kWgStaging<T>)
-        k_spread_col_wg<T, W><<<dim3((unsigned)g.nsub), ColCfg<T, W>::kBlock, lds, st>>>(
+        k_spread_col_wg<T, W><<<dim3((unsigned)g.nsub, (unsigned)g.nv), ColCfg<T, W>::kBlock, lds, st>>>(
             g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2);
     else
-        k_spread_col<T, W><<<dim3((unsigned)g.nsub), ColCfg<T, W>::kBlock, lds, st>>>(
+        k_spread_col<T, W><<<dim3((unsigned)g.nsub, (unsigned)g.nv), ColCfg<T, W>::kBlock, lds, st>>>(
             g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2);
     return hipGetLastError();
 }
@@ -806,6 +815,9 @@ constexpr int kSpread1Block = 512;
 template <typename T, int W>
 __global__ void __launch_bounds__(kSpread1Block) k_spread_sm1(GeomArgs g, const cplx<T>* __restrict__ c,
                                                               cplx<T>* __restrict__ grid, int p1) {
+    // vector blockIdx.y of a many-vector launch (strides in complex values)
+    c += (int64_t)blockIdx.y * g.cvs;
+    grid += (int64_t)blockIdx.y * g.gvs;
     extern __shared__ __align__(16) unsigned char smem[];
     double* tre = (double*)smem;
     double* tim = tre + p1;
@@ -856,6 +868,9 @@ __global__ void __launch_bounds__(kSpread1Block) k_spread_sm1(GeomArgs g, const 
 template <typename T, int DIM, int W>
 __global__ void __launch_bounds__(kGmBlock) k_spread_gm(GeomArgs g, const cplx<T>* __restrict__ c,
                                                         cplx<T>* __restrict__ grid) {
+    // vector blockIdx.y of a many-vector launch (strides in complex values)
+    c += (int64_t)blockIdx.y * g.cvs;
+    grid += (int64_t)blockIdx.y * g.gvs;
     const int64_t i = (int64_t)blockIdx.x * kGmBlock + threadIdx.x;
     if (i >= g.M) return;
     const T beta = (T)g.beta;
@@ -908,6 +923,8 @@ __global__ void __launch_bounds__(kGmBlock) k_spread_gm(GeomArgs g, const cplx<T
 // cs[i] = c[perm[i]]: the strengths in the bin-sorted order the spreading kernels walk.
 __global__ void __launch_bounds__(256) k_gather_c(const int32_t* __restrict__ perm, const cplx<double>* __restrict__ c,
                                                   cplx<double>* __restrict__ cs, int64_t M) {
+    c += (int64_t)blockIdx.y * M;
+    cs += (int64_t)blockIdx.y * M;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < M) cs[i] = c[perm[i]];
 }
@@ -925,7 +942,7 @@ template <typename T, int DIM, int W>
 hipError_t spread_w(int method, const GeomArgs& g, const void* c, void* grid, hipStream_t st) {
     if (g.M <= 0) return hipSuccess;
     if (method == NUFFT_METHOD_GM_SORT || method == NUFFT_METHOD_GM) {
-        dim3 grd((unsigned)((g.M + kGmBlock - 1) / kGmBlock));
+        dim3 grd((unsigned)((g.M + kGmBlock - 1) / kGmBlock), (unsigned)g.nv);
         k_spread_gm<T, DIM, W><<<grd, kGmBlock, 0, st>>>(g, (const cplx<T>*)c, (cplx<T>*)grid);
         return hipGetLastError();
     }
@@ -941,7 +958,7 @@ hipError_t spread_w(int method, const GeomArgs& g, const void* c, void* grid, hi
             if (e != hipSuccess) return e;
             attr_set1 = true;
         }
-        k_spread_sm1<T, W><<<dim3((unsigned)g.nsub), kSpread1Block, lds, st>>>(g, (const cplx<T>*)c,
+        k_spread_sm1<T, W><<<dim3((unsigned)g.nsub, (unsigned)g.nv), kSpread1Block, lds, st>>>(g, (const cplx<T>*)c,
                                                                               (cplx<T>*)grid, p1);
         return hipGetLastError();
     } else {
@@ -957,7 +974,7 @@ hipError_t spread_w(int method, const GeomArgs& g, const void* c, void* grid, hi
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_spread_sm<T, DIM, W><<<dim3((unsigned)g.nsub), kSpreadBlock, lds, st>>>(
+    k_spread_sm<T, DIM, W><<<dim3((unsigned)g.nsub, (unsigned)g.nv), kSpreadBlock, lds, st>>>(
         g, (const cplx<T>*)c, (cplx<T>*)grid, p1, p2, p3, pc);
     return hipGetLastError();
     }
@@ -1030,7 +1047,7 @@ hipError_t launch_spread(int prec, int method, const GeomArgs& g_in, const void*
     if (method == NUFFT_METHOD_GM) {
         g.cperm = nullptr;   // the points are in the caller's order
     } else if (prec == 1 && g.M > 0) {
-        k_gather_c<<<(unsigned)((g.M + 255) / 256), 256, 0, st>>>(g.perm, (const cplx<double>*)c_in,
+        k_gather_c<<<dim3((unsigned)((g.M + 255) / 256), (unsigned)g.nv), 256, 0, st>>>(g.perm, (const cplx<double>*)c_in,
                                                                    (cplx<double>*)c_scratch, g.M);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
