@@ -95,14 +95,30 @@ BETA_OVER_W = 2.30
 W_MIN, W_MAX = 2, 16
 
 
-def kernel_params(eps: float) -> Tuple[int, float]:
+# Upsampling factors other than 2 (the page fixes sigma = 2 and names smaller ones as future work,
+# Sec. I-B item (3)).  Reading: the kernel's Fourier transform must have decayed where the first
+# alias of the band, xi = alpha (n - N/2) = w pi (1 - 1/(2 sigma)), starts, so
+# beta = GAMMA pi (1 - 1/(2 sigma)) w, with GAMMA fixed by the page's beta = 2.30 w at sigma = 2;
+# the error of the truncated kernel falls like exp(-pi w sqrt(1 - 1/sigma)), so
+# w = ceil(ln(1/eps) / (pi sqrt(1 - 1/sigma))), which reproduces the page's width table at sigma = 2.
+SIGMA_MIN, SIGMA_MAX = 1.25, 2.0
+GAMMA = BETA_OVER_W / (0.75 * math.pi)
+
+
+def kernel_params(eps: float, sigma: float = 2.0) -> Tuple[int, float]:
     """Eq. (6): w = ceil(log10(1/eps)) + 1 (values within 1e-9 of an integer count as it),
-    clamped to [2, 16]; beta = 2.30 * w."""
+    clamped to [2, 16]; beta = 2.30 * w.  For sigma < 2 the rule of the reading above."""
     if not (eps > 0):
         raise ValueError("eps must be positive")
-    w = int(math.ceil(math.log10(1.0 / eps) - 1e-9)) + 1
+    if not (SIGMA_MIN <= sigma <= SIGMA_MAX):
+        raise ValueError("sigma must be in [1.25, 2]")
+    if sigma == 2.0:
+        w = int(math.ceil(math.log10(1.0 / eps) - 1e-9)) + 1
+        w = max(W_MIN, min(W_MAX, w))
+        return w, BETA_OVER_W * w
+    w = int(math.ceil(math.log(1.0 / eps) / (math.pi * math.sqrt(1.0 - 1.0 / sigma)) - 1e-9))
     w = max(W_MIN, min(W_MAX, w))
-    return w, BETA_OVER_W * w
+    return w, GAMMA * math.pi * (1.0 - 0.5 / sigma) * w
 
 
 def _is_5smooth(v: int) -> bool:
@@ -112,9 +128,9 @@ def _is_5smooth(v: int) -> bool:
     return v == 1
 
 
-def fine_size(N: int, w: int, sigma: int = 2) -> int:
-    """Sec. II: smallest 2^q 3^p 5^r that is >= max(sigma*N, w)."""
-    v = max(sigma * int(N), int(w), 1)
+def fine_size(N: int, w: int, sigma: float = 2.0) -> int:
+    """Sec. II: smallest 2^q 3^p 5^r that is >= max(sigma*N, w) (sigma N rounded up)."""
+    v = max(int(math.ceil(sigma * int(N) - 1e-9)), int(w), 1)
     while not _is_5smooth(v):
         v += 1
     return v
@@ -154,14 +170,15 @@ def correction_1d(N: int, n: int, w: int, beta: float) -> np.ndarray:
 class Params:
     """Everything the algorithm fixes from (d, N, eps) and the bin geometry."""
 
-    def __init__(self, N: Sequence[int], eps: float):
+    def __init__(self, N: Sequence[int], eps: float, sigma: float = 2.0):
         self.N = tuple(int(v) for v in N)
         self.dim = len(self.N)
         if self.dim not in (1, 2, 3):
             raise ValueError("dimension must be 1, 2 or 3")
         self.eps = float(eps)
-        self.w, self.beta = kernel_params(eps)
-        self.n = tuple(fine_size(Ni, self.w) for Ni in self.N)
+        self.sigma = float(sigma)
+        self.w, self.beta = kernel_params(eps, self.sigma)
+        self.n = tuple(fine_size(Ni, self.w, self.sigma) for Ni in self.N)
         self.p = [correction_1d(Ni, ni, self.w, self.beta) for Ni, ni in zip(self.N, self.n)]
 
 
@@ -270,22 +287,22 @@ def precorrect_pad(f: np.ndarray, prm: Params) -> np.ndarray:
     return bhat
 
 
-def nufft_type1(X, c, N: Sequence[int], eps: float) -> np.ndarray:
+def nufft_type1(X, c, N: Sequence[int], eps: float, sigma: float = 2.0) -> np.ndarray:
     """Approximate eq. (1) by eqs. (7), (9), (10).  Returns f with shape (N3, N2, N1)."""
-    prm = Params(N, eps)
+    prm = Params(N, eps, sigma)
     b = spread(X, c, prm.n, prm.w, prm.beta)
     return truncate_correct(fft_forward(b), prm)
 
 
-def type2_grid(f, N: Sequence[int], eps: float):
+def type2_grid(f, N: Sequence[int], eps: float, sigma: float = 2.0):
     """Type 2 steps 1-2 (eqs. (11), (12)): the fine grid b that step 3 interpolates from."""
-    prm = Params(N, eps)
+    prm = Params(N, eps, sigma)
     return fft_backward(precorrect_pad(f, prm)), prm
 
 
-def nufft_type2(X, f, N: Sequence[int], eps: float) -> np.ndarray:
+def nufft_type2(X, f, N: Sequence[int], eps: float, sigma: float = 2.0) -> np.ndarray:
     """Approximate eq. (3) by eqs. (11), (12) and the interpolation sum.  Returns c (M,)."""
-    b, prm = type2_grid(f, N, eps)
+    b, prm = type2_grid(f, N, eps, sigma)
     return interp(X, b, prm.w, prm.beta)
 
 

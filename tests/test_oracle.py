@@ -67,6 +67,21 @@ def test_fine_size_against_enumeration(oracle_mod):
             assert oracle_mod.fine_size(N, w) == expect, (N, w)
 
 
+def test_fine_size_sigma_below_two(oracle_mod):
+    """sigma < 2: smallest 5-smooth number >= max(ceil(sigma N), w), against an enumeration."""
+    smooth = sorted({2 ** a * 3 ** b * 5 ** c for a in range(14) for b in range(9) for c in range(7)})
+    for sigma in (1.25, 1.5):
+        for N in list(range(1, 200)) + [1000, 1023]:
+            for w in (4, 9):
+                target = max(-(-int(sigma * 4) * N // 4), w)      # ceil(sigma N) in integers
+                expect = next(s for s in smooth if s >= target)
+                assert oracle_mod.fine_size(N, w, sigma) == expect, (sigma, N, w)
+    with pytest.raises(ValueError):
+        oracle_mod.kernel_params(1e-6, 1.1)
+    with pytest.raises(ValueError):
+        oracle_mod.kernel_params(1e-6, 2.5)
+
+
 # ---------------------------------------------------------------------------------------------
 # Kernel and its Fourier transform (eqs. (4), (5))
 # ---------------------------------------------------------------------------------------------
@@ -249,6 +264,37 @@ def test_nufft_vs_direct_within_10eps(oracle_mod, N, M, eps, prec):
     c2 = oracle_mod.nufft_type2(X, f, N, eps)
     cd = oracle_mod.direct_type2(X, f, N)
     assert oracle_mod.rel_l2(c2, cd) <= 10 * eps
+
+
+SIGMA_CASES = [
+    ((300,), 2000, 1e-3, 1.25), ((300,), 2000, 1e-9, 1.25), ((257,), 1500, 1e-6, 1.5),
+    ((32, 28), 1500, 1e-4, 1.25), ((32, 32), 1000, 1e-12, 1.5), ((24, 20), 1200, 1e-6, 1.5),
+    ((12, 10, 9), 900, 1e-3, 1.25), ((12, 12, 12), 900, 1e-6, 1.25), ((10, 9, 8), 700, 1e-9, 1.5),
+]
+
+
+@pytest.mark.parametrize("N,M,eps,sigma", SIGMA_CASES)
+def test_nufft_sigma_below_two_vs_direct(oracle_mod, N, M, eps, sigma):
+    """Upsampling sigma < 2 with the width and shape of the reading: both types within 10 eps of
+    the exact sums (eqs. (1), (3)), the accuracy statement after eq. (6)."""
+    wl = Workload(name="t", dim=len(N), N=N, M=M, eps=eps, precision="f64", seed=13)
+    inp = make_inputs(wl)
+    X, c, f = inp["X"], inp["c"], inp["f"]
+    prm = oracle_mod.Params(N, eps, sigma)
+    assert all(ni < 2 * Ni or ni == prm.w or ni <= 8 for ni, Ni in zip(prm.n, N))
+    assert oracle_mod.rel_l2(oracle_mod.nufft_type1(X, c, N, eps, sigma), oracle_mod.direct_type1(X, c, N)) <= 10 * eps
+    assert oracle_mod.rel_l2(oracle_mod.nufft_type2(X, f, N, eps, sigma), oracle_mod.direct_type2(X, f, N)) <= 10 * eps
+
+
+def test_nufft_sigma_adjoint(oracle_mod):
+    rng = _rng(14)
+    N, eps, sigma = (40, 30), 1e-7, 1.25
+    X = _uniform_points(rng, 2, 250)
+    c = _rand_complex(rng, 250)
+    f = _rand_complex(rng, (30, 40))
+    lhs = np.vdot(f.ravel(), oracle_mod.nufft_type1(X, c, N, eps, sigma).ravel())
+    rhs = np.vdot(oracle_mod.nufft_type2(X, f, N, eps, sigma), c)
+    assert abs(lhs - rhs) <= 1e-13 * abs(lhs)
 
 
 def test_nufft_clustered_vs_direct(oracle_mod):
