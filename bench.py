@@ -218,6 +218,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=1 << 22,
                     help="points of the workload timed on the CPU oracle (0 = skip)")
     ap.add_argument("--method", type=int, default=0)
+    ap.add_argument("--upsampfac", type=float, default=0.0,
+                    help="fine-grid upsampling factor sigma in [1.25, 2] (0 = 2)")
     ap.add_argument("--probe-copy", type=int, default=0,
                     help="only run a plain copy of this many bytes (counter calibration)")
     ap.add_argument("--compare", action="store_true",
@@ -257,7 +259,8 @@ def main():
     f_out = torch.empty(tuple(reversed(wl.N)), dtype=cdt, device=dev)
     c_out = torch.empty(wl.M, dtype=cdt, device=dev)
     stream = torch.cuda.current_stream()
-    plan = nf.Plan(1, wl.N, wl.eps, wl.precision, stream=stream, timing=True, method=args.method)
+    plan = nf.Plan(1, wl.N, wl.eps, wl.precision, stream=stream, timing=True, method=args.method,
+                   upsampfac=args.upsampfac)
 
     def step():
         plan.setpts(*X)                   # bin-sort + subproblems
@@ -305,7 +308,8 @@ def main():
         "dtype": "f32" if wl.precision == "f32" else "f64",
         "data": "synthetic",
         "config": {"workload": f"{wl.dim}D type1+type2 pair N={'x'.join(map(str, wl.N))} M={wl.M} "
-                               f"{wl.dist} {wl.precision} eps={wl.eps:g}",
+                               f"{wl.dist} {wl.precision} eps={wl.eps:g}"
+                               + (f" sigma={args.upsampfac:g}" if args.upsampfac else ""),
                    "fine_grid": list(info["n"]), "w": info["w"], "bins": list(info["bins"]),
                    "nsubproblems": info["nsubproblems"]},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,

@@ -73,6 +73,7 @@ typedef struct {
     size_t max_device_bytes;  /* 0 = no limit; otherwise plan-owned device memory above this fails */
     int timing;               /* 1 = record per-stage HIP-event times (see nufft_get_stage_times) */
     int max_batch;            /* vectors per batch in nufft_execute_many; 0 = automatic */
+    double upsampfac;         /* fine-grid upsampling factor sigma in [1.25, 2]; 0 = 2 (the paper's) */
 } nufft_opts;
 
 /* Fill *opts with defaults (all zero = automatic choices).  NUFFT_ERR_BAD_ARG if opts is NULL. */
@@ -85,12 +86,18 @@ int nufft_default_opts(nufft_opts* opts);
  *   N         host array of dim mode counts (N1[, N2[, N3]]), each >= 1.
  *   eps       requested relative tolerance > 0.  Kernel width w = ceil(log10(1/eps)) + 1
  *             and shape beta = 2.30 w (eq. (6)); w is clamped to [2, 16] with
- *             NUFFT_WARN_EPS_CLAMPED.
+ *             NUFFT_WARN_EPS_CLAMPED.  With opts->upsampfac = sigma < 2 (the paper fixes
+ *             sigma = 2 and names smaller factors as future work, Sec. I-B item (3)):
+ *             w = ceil(ln(1/eps) / (pi sqrt(1 - 1/sigma))) and
+ *             beta = gamma pi (1 - 1/(2 sigma)) w, gamma = 2.30 / (0.75 pi), so that the
+ *             kernel transform has decayed where the first alias of the band starts; at
+ *             sigma = 2 these reduce to the paper's values.  sigma outside [1.25, 2] is
+ *             NUFFT_ERR_BAD_ARG.
  *   precision 0 = single (float / complex<float>), 1 = double.
  *   stream    hipStream_t on the current device, or NULL for the null stream.
  *   opts      NULL or tuning/test options.
  *   out       receives the plan.  Nothing is allocated on error.
- * Allocates the fine grid (n_i = smallest 2^a 3^b 5^c >= max(2 N_i, w)), the
+ * Allocates the fine grid (n_i = smallest 2^a 3^b 5^c >= max(ceil(sigma N_i), w)), the
  * correction factors (eq. (10), computed on the host in fp64) and the rocFFT plan.
  */
 int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int precision,
@@ -159,7 +166,7 @@ const char* nufft_last_error(nufft_plan plan);
  *                  column order (kernel width w when the points of a 3D bin are ordered by the
  *                  x-y column block where their kernel support starts, see nufft_get_sort;
  *                  else 0), column block edge s (1 when there is no column order)
- *   info_d[0..1]:  beta, eps
+ *   info_d[0..2]:  beta, eps, sigma
  * Either pointer may be NULL.
  */
 int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d);

@@ -22,7 +22,8 @@ _D = ctypes.c_double
 
 class NufftOpts(ctypes.Structure):
     _fields_ = [("method", ctypes.c_int), ("bin", ctypes.c_int * 3), ("subproblem_cap", ctypes.c_int),
-                ("max_device_bytes", ctypes.c_size_t), ("timing", ctypes.c_int), ("max_batch", ctypes.c_int)]
+                ("max_device_bytes", ctypes.c_size_t), ("timing", ctypes.c_int), ("max_batch", ctypes.c_int),
+                ("upsampfac", ctypes.c_double)]
 
 
 SIGNATURES = {
@@ -110,7 +111,7 @@ class Plan:
     def __init__(self, nufft_type: int, N: Sequence[int], eps: float, precision: str = "f32",
                  stream=None, method: int = METHOD_AUTO, bins: Optional[Sequence[int]] = None,
                  subproblem_cap: int = 0, timing: bool = False, max_device_bytes: int = 0,
-                 max_batch: int = 0):
+                 max_batch: int = 0, upsampfac: float = 0.0):
         lib = load_library()
         torch = _torch()
         if precision not in ("f32", "f64"):
@@ -131,6 +132,7 @@ class Plan:
         opts.timing = 1 if timing else 0
         opts.max_device_bytes = int(max_device_bytes)
         opts.max_batch = int(max_batch)
+        opts.upsampfac = float(upsampfac)
         if stream is None:
             stream = torch.cuda.current_stream()
         self._stream_obj = stream
@@ -190,14 +192,14 @@ class Plan:
 
     def info(self):
         ii = (ctypes.c_int64 * 20)()
-        dd = (ctypes.c_double * 2)()
+        dd = (ctypes.c_double * 3)()
         self._check(self._lib.nufft_get_info(self._h, ii, dd))
         v = list(ii)
         return {"type": v[0], "dim": v[1], "precision": v[2], "w": v[3], "n": tuple(v[4:4 + self.dim]),
                 "N": tuple(v[7:7 + self.dim]), "bins": tuple(v[10:10 + self.dim]), "nbins": v[13],
                 "nsubproblems": v[14], "M": v[15], "cap": v[16], "method": v[17], "colw": v[18],
                 "colstep": v[19],
-                "beta": dd[0], "eps": dd[1]}
+                "beta": dd[0], "eps": dd[1], "sigma": dd[2]}
 
     # -- API -----------------------------------------------------------------------------------
     def setpts(self, x, y=None, z=None):

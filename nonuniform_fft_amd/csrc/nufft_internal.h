@@ -82,6 +82,7 @@ struct nufft_plan_s {
     int64_t n[3] = {1, 1, 1};
     int w = 0;
     double beta = 0, eps = 0;
+    double sigma = 2.0;                 // fine-grid upsampling factor
     double s[3] = {0, 0, 0};            // n_i / (2 pi)
     hipStream_t stream = nullptr;
     int device = 0;

@@ -451,17 +451,26 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
     if (opts) plan->opts = *opts;
     int status = NUFFT_OK;
 
-    // eq. (6): w = ceil(log10(1/eps)) + 1 (an exact power of ten counts as its integer log), beta = 2.30 w
-    int w = (int)std::ceil(std::log10(1.0 / eps) - 1e-9) + 1;
+    // eq. (6): w = ceil(log10(1/eps)) + 1 (an exact power of ten counts as its integer log), beta = 2.30 w.
+    // sigma < 2 (not on the page): the kernel transform must have decayed at the first alias of the
+    // band, xi = w pi (1 - 1/(2 sigma)), and the truncation error falls like exp(-pi w sqrt(1 - 1/sigma))
+    const double sigma = plan->opts.upsampfac == 0.0 ? 2.0 : plan->opts.upsampfac;
+    if (!(sigma >= 1.25 && sigma <= 2.0)) {
+        delete plan;
+        return NUFFT_ERR_BAD_ARG;
+    }
+    plan->sigma = sigma;
+    int w = (sigma == 2.0) ? (int)std::ceil(std::log10(1.0 / eps) - 1e-9) + 1
+                           : (int)std::ceil(std::log(1.0 / eps) / (nufft::kPi * std::sqrt(1.0 - 1.0 / sigma)) - 1e-9);
     if (w < nufft::kMinW || w > nufft::kMaxW) {
         w = std::min(std::max(w, nufft::kMinW), nufft::kMaxW);
         status = NUFFT_WARN_EPS_CLAMPED;
     }
     plan->w = w;
-    plan->beta = 2.30 * w;
+    plan->beta = (sigma == 2.0) ? 2.30 * w : (2.30 / (0.75 * nufft::kPi)) * nufft::kPi * (1.0 - 0.5 / sigma) * w;
     for (int i = 0; i < 3; ++i) {
         plan->N[i] = i < dim ? N[i] : 1;
-        plan->n[i] = i < dim ? next_5smooth(std::max<int64_t>(2 * N[i], w)) : 1;
+        plan->n[i] = i < dim ? next_5smooth(std::max<int64_t>((int64_t)std::ceil(sigma * (double)N[i] - 1e-9), w)) : 1;
         plan->s[i] = (double)plan->n[i] / (2.0 * nufft::kPi);
     }
     if (grid_cells(plan) > (int64_t(1) << 31) - 1) {
@@ -726,6 +735,7 @@ int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d) {
     if (info_d) {
         info_d[0] = plan->beta;
         info_d[1] = plan->eps;
+        info_d[2] = plan->sigma;
     }
     return NUFFT_OK;
 }

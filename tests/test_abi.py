@@ -49,6 +49,13 @@ def test_host_side_argument_checks():
         assert lib.nufft_plan_create(t, d, n, e, p, None, None, ctypes.byref(h)) == -1
         assert not h.value
     assert lib.nufft_plan_create(1, 2, N, 1e-5, 0, None, None, None) == -1
+    # an upsampling factor outside [1.25, 2] is rejected before any device work
+    for sigma in (1.1, 2.5, -1.0, float("nan")):
+        o = NufftOpts()
+        lib.nufft_default_opts(ctypes.byref(o))
+        o.upsampfac = sigma
+        assert lib.nufft_plan_create(1, 2, N, 1e-5, 0, None, ctypes.byref(o), ctypes.byref(h)) == -1
+        assert not h.value
     for code in (0, 1, -1, -2, -3, -4, -5, -6, -7):
         assert lib.nufft_strerror(code)
     assert lib.nufft_strerror(12345) == b"unknown status"

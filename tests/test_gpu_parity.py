@@ -317,6 +317,69 @@ def test_empty_and_single_point(nf, orc):
         assert orc.rel_l2(f, ref) <= tol_for(prec)
 
 
+SIGMA_CASES = [
+    Workload("sg", 1, (2000,), 40_000, 1e-6, "f32", seed=111),
+    Workload("sg", 2, (100, 72), 50_001, 1e-5, "f32", seed=112),
+    Workload("sg", 2, (64, 48), 20_000, 1e-12, "f64", seed=113),
+    Workload("sg", 3, (24, 20, 18), 40_000, 1e-5, "f32", seed=114),
+    Workload("sg", 3, (20, 16, 12), 15_000, 1e-9, "f64", seed=115),
+    Workload("sg", 3, (32, 32, 32), 60_000, 1e-5, "f32", dist="cluster", seed=116),
+]
+
+
+def _sigma_tol(prm, prec, M=None):
+    """Parity bar for sigma < 2, derived from the arithmetic.  The fine grid is rounded to the
+    plan precision (unit roundoff u) and the FFT adds O(log n) roundings of that size; the
+    correction of eq. (10) scales mode k by p(k), so the output's relative error is about
+    u kappa with kappa = rms(p / p_min) rms(p_min / p).  For type 1 (M given) each cell also
+    sums K = M w^d / n^d contributions, accumulated in fp64 in an order other than the oracle's:
+    another u64 sqrt(K) kappa.  At sigma = 2 kappa is a few units; at sigma = 1.25 in 3D it
+    reaches hundreds (fp32, w = 9) to millions (fp64, w = 15).  Bar: max(1e-5 fp32 / 1e-10
+    fp64, 4 kappa (u + u64 sqrt(1 + K)))."""
+    P = np.abs(orc_outer(prm))
+    pm = P.min()
+    kappa = math.sqrt(np.mean((P / pm) ** 2)) * math.sqrt(np.mean((pm / P) ** 2))
+    u = 2.0 ** -24 if prec == "f32" else 2.0 ** -53
+    acc = 0.0
+    if M is not None:
+        K = M * prm.w ** prm.dim / float(np.prod(prm.n))
+        acc = 2.0 ** -53 * math.sqrt(1.0 + K)
+    return max(tol_for(prec), 4 * kappa * (u + acc))
+
+
+def orc_outer(prm):
+    out = np.array(1.0)
+    for p in prm.p[::-1]:
+        out = np.multiply.outer(out, p)
+    return out
+
+
+@pytest.mark.parametrize("wl", SIGMA_CASES, ids=lambda w: f"{w.dim}d_{w.N}_{w.precision}_{w.eps:g}_{w.dist}")
+@pytest.mark.parametrize("sigma", [1.25, 1.5])
+def test_upsampfac_vs_oracle(nf, orc, wl, sigma):
+    """sigma < 2: the plan's w, beta and fine grid equal the oracle's, and both types match the
+    oracle NUFFT at the same sigma, within the bar derived in _sigma_tol."""
+    _announce(f"sigma={sigma} {wl.N} M={wl.M} {wl.precision} eps={wl.eps} {wl.dist}")
+    inp = make_inputs(wl)
+    prm = orc.Params(wl.N, wl.eps, sigma)
+    p = nf.Plan(1, wl.N, wl.eps, wl.precision, upsampfac=sigma)
+    info = p.info()
+    assert info["w"] == prm.w and info["n"] == prm.n and info["sigma"] == sigma
+    assert abs(info["beta"] - prm.beta) <= 1e-12 * prm.beta
+    p.setpts(*[to_dev(x) for x in inp["X"]])
+    cd = cdtype(wl.precision)
+    f = torch.empty(tuple(reversed(wl.N)), dtype=cd, device=dev())
+    c = torch.empty(wl.M, dtype=cd, device=dev())
+    p.execute(to_dev(inp["c"]), f)
+    p.execute_adjoint(c, to_dev(inp["f"]))
+    torch.cuda.synchronize()
+    p.destroy()
+    e1 = orc.rel_l2(f.cpu().numpy(), orc.nufft_type1(inp["X"], inp["c"], wl.N, wl.eps, sigma))
+    e2 = orc.rel_l2(c.cpu().numpy(), orc.nufft_type2(inp["X"], inp["f"], wl.N, wl.eps, sigma))
+    tol1, tol2 = _sigma_tol(prm, wl.precision, wl.M), _sigma_tol(prm, wl.precision)
+    assert e1 <= tol1 and e2 <= tol2, (e1, e2, tol1, tol2)
+
+
 def test_type2_bitwise_reproducible_type1_close(nf):
     wl = Workload("r", 3, (32, 32, 32), 50_000, 1e-5, "f32", seed=53)
     inp = make_inputs(wl)
