@@ -9,7 +9,9 @@
 // give longer runs per digit in the scatter, so fuller memory transactions).  Each pass is (1) a per-workgroup digit histogram in LDS (integer LDS
 // atomics), (2) an exclusive scan over digit-major histograms, (3) a stable scatter that ranks
 // equal digits inside a wavefront with 64-bit ballots and across the four wavefronts of a
-// workgroup through LDS counters.  Every pass is stable, so points keep their original order
+// workgroup through LDS counters, then reorders the tile by digit one array at a time through
+// a single LDS buffer (so several workgroups fit per CU) and writes each digit's run to
+// consecutive addresses, with neighbouring tiles kept on one XCD.  Every pass is stable, so points keep their original order
 // inside a bin and the permutation is deterministic.
 #include "nufft_internal.h"
 
@@ -192,6 +194,15 @@ hipError_t exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* s
 // ------------------------------------------------------------------------------------------
 // Radix sort passes
 // ------------------------------------------------------------------------------------------
+// Tile handled by this workgroup.  Workgroups are dispatched to the 8 XCDs round-robin by
+// index; mapping index b to tile start(b % 8) + b / 8, with each XCD owning a contiguous range
+// of tiles, puts neighbouring tiles -- whose runs of one digit are adjacent in the output --
+// behind the same L2, so their partial lines merge before they are written back.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t nt) {
+    const int64_t q = nt / 8, r = nt % 8, x = b % 8;
+    return x * q + (x < r ? x : r) + b / 8;
+}
+
 __global__ void __launch_bounds__(kBlock) k_radix_hist(const int32_t* __restrict__ keys, int64_t M,
                                                         int shift, int bits, int64_t ntiles,
                                                         int32_t* __restrict__ hist) {
@@ -221,8 +232,9 @@ struct Payload {
 //
 // Each wavefront ranks its own contiguous chunk of the tile (kItems rounds of 64 keys) with
 // ballots and wavefront-private digit counters, so ranking needs no workgroup barrier; the
-// per-digit counts of the four chunks are then combined into tile offsets, the tile is
-// reordered by digit in LDS, and each digit's run is written to consecutive addresses.
+// per-digit counts of the four chunks are then combined into tile offsets, and keys, values
+// and coordinates are reordered by digit through one LDS buffer in turn, each digit's run
+// written to consecutive addresses.
 // IDV: the values are the keys' positions (the first pass), so none are read.
 template <typename T, int NP, bool IDV>
 __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restrict__ keys_in,
@@ -239,11 +251,11 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
     __shared__ int32_t gbase[kRadix];                   // global start of each digit's run of this tile
     __shared__ int32_t tbase[kRadix];                   // start of each digit's run inside the tile
     __shared__ int32_t wsum[kWaves];
-    __shared__ int32_t sk[kTile];
-    __shared__ int32_t sv[kTile];
-    __shared__ T sc[NP > 0 ? NP : 1][kTile];
+    __shared__ uint32_t sbuf[kTile * (sizeof(T) > 4 ? 2 : 1)];   // one reordered array at a time
+    __shared__ uint8_t sdig[kTile];                              // digit of each reordered slot
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t base = (int64_t)blockIdx.x * kTile;
+    const int64_t tile = xcd_tile(blockIdx.x, ntiles);
+    const int64_t base = tile * kTile;
     const int count = (int)min<int64_t>(kTile, M - base);
 
     // load this wavefront's chunk (coalesced per round)
@@ -306,7 +318,7 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
         int32_t run = inc - tot;
         for (int i = 0; i < wv; ++i) run += wsum[i];
         tbase[d] = run;
-        gbase[d] = (d <= mask) ? offs[(int64_t)d * ntiles + blockIdx.x] : 0;
+        gbase[d] = (d <= mask) ? offs[(int64_t)d * ntiles + tile] : 0;
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) {
             cnt[i][d] = run;
@@ -314,28 +326,37 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
         }
     }
     __syncthreads();
+    // slot of each item in the digit-ordered tile (-1: past the end of the input)
+    int pos[kItems];
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
+        pos[r] = -1;
         if (wv * kChunk + r * 64 + lane < count) {
             const int digit = (keys[r] >> shift) & mask;
-            const int pos = cnt[wv][digit] + rank[r];
-            sk[pos] = keys[r];
-            sv[pos] = vals[r];
-#pragma unroll
-            for (int d = 0; d < NP; ++d) sc[d][pos] = cvs[r][d];
+            pos[r] = cnt[wv][digit] + rank[r];
+            sdig[pos[r]] = (uint8_t)digit;
         }
     }
-    __syncthreads();
-    // write out: position i of the reordered tile goes to gbase[digit] + (i - tbase[digit])
-    for (int i = tid; i < count; i += kBlock) {
-        const int32_t key = sk[i];
-        const int digit = (key >> shift) & mask;
-        const int64_t pos = (int64_t)gbase[digit] + (i - tbase[digit]);
-        keys_out[pos] = key;
-        vals_out[pos] = sv[i];
+    // the arrays are reordered through one LDS buffer in turn: keys, values, then coordinates;
+    // slot i goes to gbase[digit] + (i - tbase[digit])
+    auto emit = [&](auto get, auto put) {
 #pragma unroll
-        for (int d = 0; d < NP; ++d) pl.out[d][pos] = sc[d][i];
-    }
+        for (int r = 0; r < kItems; ++r)
+            if (pos[r] >= 0) get(r, pos[r]);
+        __syncthreads();
+        for (int i = tid; i < count; i += kBlock) {
+            const int digit = sdig[i];
+            put((int64_t)gbase[digit] + (i - tbase[digit]), i);
+        }
+        __syncthreads();
+    };
+    int32_t* bi = (int32_t*)sbuf;
+    emit([&](int r, int p) { bi[p] = keys[r]; }, [&](int64_t o, int i) { keys_out[o] = bi[i]; });
+    emit([&](int r, int p) { bi[p] = vals[r]; }, [&](int64_t o, int i) { vals_out[o] = bi[i]; });
+    T* bt = (T*)sbuf;
+#pragma unroll
+    for (int d = 0; d < NP; ++d)
+        emit([&](int r, int p) { bt[p] = cvs[r][d]; }, [&](int64_t o, int i) { pl.out[d][o] = bt[i]; });
 }
 
 __global__ void k_iota(int32_t* __restrict__ v, int64_t M) {
