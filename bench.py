@@ -316,6 +316,13 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dom_name) if args.workload == "3d_n128_m16m_f32_e5" else None,
                      "algorithmic_bytes": bytes_alg, "avg_ms": dom_ms},
+        # the same kernel against the vector ALU: 4 flops per (point, cell) of complex x real
+        # accumulate; peak = fp32 / fp64 vector rate (packed fp32 counted, as the published figure)
+        "roofline_alu": {"bound": "alu", "kernel": dom_name,
+                         "achieved": wl.M * 4 * info["w"] ** wl.dim / (dom_ms * 1e-3) / 1e12,
+                         "peak": 157.3 if wl.precision == "f32" else 78.6, "unit": "TFLOP/s",
+                         "frac": wl.M * 4 * info["w"] ** wl.dim / (dom_ms * 1e-3) / 1e12
+                                 / (157.3 if wl.precision == "f32" else 78.6)},
         "stages_ms": stg,
         "exec_pts_per_s": {"type1": wl.M / (exec1 * 1e-3), "type2": wl.M / (exec2 * 1e-3)},
     }

@@ -77,9 +77,10 @@ __global__ void __launch_bounds__(kInterpBlock) k_interp_gm(GeomArgs g, const cp
     c[g.perm[i]] = out;
 }
 
-// 3D fp64 tiles leave room for one workgroup per CU: 768 lanes keep three wavefronts per SIMD
+// 3D: 768 lanes.  fp64 tiles leave room for one workgroup per CU (three wavefronts per SIMD);
+// fp32 tiles for two (six per SIMD), which measured faster than 512 or 1024 lanes.
 template <typename T, int DIM>
-constexpr int kInterpSmBlock = (sizeof(T) == 8 && DIM == 3) ? 768 : 512;
+constexpr int kInterpSmBlock = (DIM == 3) ? 768 : 512;
 
 __host__ __device__ inline int interp_row_pitch(int p1) { return p1; }
 

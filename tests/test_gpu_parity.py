@@ -332,10 +332,11 @@ def _sigma_tol(prm, prec, M=None):
     plan precision (unit roundoff u) and the FFT adds O(log n) roundings of that size; the
     correction of eq. (10) scales mode k by p(k), so the output's relative error is about
     u kappa with kappa = rms(p / p_min) rms(p_min / p).  For type 1 (M given) each cell also
-    sums K = M w^d / n^d contributions, accumulated in fp64 in an order other than the oracle's:
-    another u64 sqrt(K) kappa.  At sigma = 2 kappa is a few units; at sigma = 1.25 in 3D it
-    reaches hundreds (fp32, w = 9) to millions (fp64, w = 15).  Bar: max(1e-5 fp32 / 1e-10
-    fp64, 4 kappa (u + u64 sqrt(1 + K)))."""
+    sums K = M w^d / n^d contributions (on average), partly in the plan precision (the 3D
+    column runs accumulate in registers before the fp64 LDS bin) and in another order than the
+    oracle's: another u sqrt(K) kappa.  At sigma = 2 kappa is a few units; at sigma = 1.25 in
+    3D it reaches hundreds (fp32, w = 9) to millions (fp64, w = 15).  Bar: max(1e-5 fp32 /
+    1e-10 fp64, 4 kappa u (1 + sqrt(1 + K))) for type 1, max(.., 4 kappa u) for type 2."""
     P = np.abs(orc_outer(prm))
     pm = P.min()
     kappa = math.sqrt(np.mean((P / pm) ** 2)) * math.sqrt(np.mean((pm / P) ** 2))
@@ -343,7 +344,7 @@ def _sigma_tol(prm, prec, M=None):
     acc = 0.0
     if M is not None:
         K = M * prm.w ** prm.dim / float(np.prod(prm.n))
-        acc = 2.0 ** -53 * math.sqrt(1.0 + K)
+        acc = u * math.sqrt(1.0 + K)
     return max(tol_for(prec), 4 * kappa * (u + acc))
 
 
