@@ -388,6 +388,100 @@ def direct_type2(X, f, N: Sequence[int], sel: Optional[Sequence[int]] = None) ->
 # Bin-sort and subproblems (Sec. III-A)
 # ----------------------------------------------------------------------------------------------
 
+# ----------------------------------------------------------------------------------------------
+# Type 3, nonuniform to nonuniform: f_k = sum_j c_j exp(+i s_k . x_j).  The cuFINUFFT page lists
+# it as not provided (Sec. I-B, item 4); the imaging equation of the GPU training page ("A toy
+# problem": irregular visibility samples to image points) is a sum of this class.  The steps
+# below are a reading built from the type 1 and type 2 steps of Sec. II:
+#   1. centre and half-width per dimension: sources x in C +- X, targets s in D +- S;
+#   2. fine grid n (smallest even 5-smooth >= max(2 sigma X S / pi + w, 2 w)), h = 2 pi / n and
+#      scale gamma = n / (2 sigma S): the scaled sources y = (x - C) / gamma keep the kernel's
+#      reach inside [-pi, pi), and the scaled targets xi = (s - D) gamma stay inside the band
+#      |xi h| <= pi / sigma that the kernel resolves (as the modes of type 1 do);
+#   3. c'_j = c_j exp(i D.(x_j - C)); spread c' at y onto the grid (eq. (7));
+#   4. sum_l b_l exp(i xi t_l) over cells t_l = l h - pi is a type 2 sum with N = n modes
+#      (f_k = b_{k + floor(n/2)}) at points theta = xi h, evaluated by the type 2 NUFFT;
+#   5. divide by the kernel transform, sum_l psi(t_l - y) exp(i xi t_l) ~ (1/h) psihat(xi)
+#      exp(i xi y) with psihat(xi) = alpha phihat(alpha xi), alpha = w h / 2, i.e. multiply by
+#      prod_i (2/w) / phihat(alpha_i xi_i), and restore the phases exp(i s.C) and
+#      exp(i xi (h floor(n/2) - pi)).
+# ----------------------------------------------------------------------------------------------
+
+def _even_5smooth(v: float) -> int:
+    u = max(int(math.ceil(v - 1e-9)), 2)
+    while u % 2 or not _is_5smooth(u):
+        u += 1
+    return u
+
+
+class Type3Params:
+    """Centres, half-widths, fine grid, scales and kernel of a type 3 transform (steps 1, 2)."""
+
+    def __init__(self, X, S, eps: float, sigma: float = 2.0):
+        self.dim = len(X)
+        self.w, self.beta = kernel_params(eps, sigma)
+        self.sigma = float(sigma)
+        xs = [np.asarray(x, dtype=np.float64) for x in X]
+        ss = [np.asarray(s, dtype=np.float64) for s in S]
+        self.C = [0.5 * (x.max() + x.min()) if x.size else 0.0 for x in xs]
+        self.X = [0.5 * (x.max() - x.min()) if x.size else 0.0 for x in xs]
+        self.D = [0.5 * (s.max() + s.min()) if s.size else 0.0 for s in ss]
+        self.S = [0.5 * (s.max() - s.min()) if s.size else 0.0 for s in ss]
+        w = self.w
+        self.n = tuple(_even_5smooth(max(2 * sigma * Xi * Si / math.pi + w, 2 * w)) for Xi, Si in zip(self.X, self.S))
+        self.h = [2 * math.pi / ni for ni in self.n]
+        self.gamma = []
+        for Xi, Si, ni in zip(self.X, self.S, self.n):
+            if Si > 0:
+                self.gamma.append(ni / (2 * sigma * Si))
+            elif Xi > 0:
+                self.gamma.append(Xi * ni / (math.pi * (ni - w)))
+            else:
+                self.gamma.append(1.0)
+
+
+def nufft_type3(X, c, S, eps: float, sigma: float = 2.0) -> np.ndarray:
+    """Type 3 by the steps above: f_k ~ sum_j c_j exp(+i s_k . x_j), k = 1..K."""
+    prm = Type3Params(X, S, eps, sigma)
+    xs = [np.asarray(x, dtype=np.float64) for x in X]
+    ss = [np.asarray(s, dtype=np.float64) for s in S]
+    y = [(x - Ci) / g for x, Ci, g in zip(xs, prm.C, prm.gamma)]
+    pre = np.zeros(xs[0].size)
+    for x, Ci, Di in zip(xs, prm.C, prm.D):
+        pre = pre + Di * (x - Ci)
+    cp = np.asarray(c, dtype=np.complex128) * np.exp(1j * pre)
+    b = spread(y, cp, prm.n, prm.w, prm.beta)
+    theta = [(s - Di) * g * hi for s, Di, g, hi in zip(ss, prm.D, prm.gamma, prm.h)]
+    cin = nufft_type2(theta, b, prm.n, eps, sigma)
+    out = cin.astype(np.complex128)
+    for s, Ci, Di, g, hi, ni in zip(ss, prm.C, prm.D, prm.gamma, prm.h, prm.n):
+        xi = (s - Di) * g
+        alpha = prm.w * hi / 2
+        out = out * (2.0 / prm.w) / phihat(alpha * xi, prm.w, prm.beta)
+        out = out * np.exp(1j * (xi * (hi * (ni // 2) - math.pi) + s * Ci))
+    return out
+
+
+def direct_type3(X, c, S, sel: Optional[Sequence[int]] = None) -> np.ndarray:
+    """The exact type 3 sum f_k = sum_j c_j exp(+i s_k . x_j) in fp64 (targets in chunks); `sel`
+    restricts it to the listed targets."""
+    xs = [np.asarray(x, dtype=np.float64) for x in X]
+    ss = [np.asarray(s, dtype=np.float64) for s in S]
+    if sel is not None:
+        sel = np.asarray(sel, dtype=np.int64)
+        ss = [s[sel] for s in ss]
+    cc = np.asarray(c, dtype=np.complex128)
+    K = ss[0].size
+    out = np.zeros(K, dtype=np.complex128)
+    step = max(1, (1 << 22) // max(1, xs[0].size))
+    for a in range(0, K, step):
+        ph = np.zeros((min(K, a + step) - a, xs[0].size))
+        for s, x in zip(ss, xs):
+            ph += np.multiply.outer(s[a:a + step], x)
+        out[a:a + step] = np.exp(1j * ph) @ cc
+    return out
+
+
 def binsort(X, n: Sequence[int], m: Sequence[int], w_col: int = 0, col_step: int = 1):
     """Returns (bin_of_point, counts, perm) as int64 arrays; see the C routine.  With w_col > 0
     (3D) the points of a bin are ordered by the col_step x col_step block of the x-y column where

@@ -297,6 +297,71 @@ def test_nufft_sigma_adjoint(oracle_mod):
     assert abs(lhs - rhs) <= 1e-13 * abs(lhs)
 
 
+# ---------------------------------------------------------------------------------------------
+# Type 3 (nonuniform to nonuniform)
+# ---------------------------------------------------------------------------------------------
+
+def test_direct_type3_on_integer_targets_is_type1(oracle_mod):
+    """Targets s = -k on the modes I_N: the type 3 sum is the type 1 sum of eq. (1)."""
+    rng = _rng(21)
+    N = (6, 5, 4)
+    X = _uniform_points(rng, 3, 50)
+    c = _rand_complex(rng, 50)
+    ks = np.meshgrid(*[oracle_mod.mode_range(Ni) for Ni in N[::-1]], indexing="ij")[::-1]
+    S = [-k.ravel().astype(np.float64) for k in ks]
+    f3 = oracle_mod.direct_type3(X, c, S)
+    f1 = oracle_mod.direct_type1(X, c, N).ravel()
+    np.testing.assert_allclose(f3, f1, rtol=1e-12, atol=1e-12 * np.abs(f1).max())
+
+
+def test_direct_type3_bruteforce_loops(oracle_mod):
+    rng = _rng(22)
+    X = [rng.uniform(-5, 9, 7), rng.uniform(0, 1, 7)]
+    S = [rng.uniform(-30, 3, 5), rng.uniform(-2, 2, 5)]
+    c = _rand_complex(rng, 7)
+    expect = np.array([sum(c[j] * complex(math.cos(S[0][k] * X[0][j] + S[1][k] * X[1][j]),
+                                          math.sin(S[0][k] * X[0][j] + S[1][k] * X[1][j])) for j in range(7))
+                       for k in range(5)])
+    np.testing.assert_allclose(oracle_mod.direct_type3(X, c, S), expect, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle_mod.direct_type3(X, c, S, sel=[4, 1]), expect[[4, 1]], rtol=1e-13, atol=1e-13)
+
+
+T3_CASES = [(1, 1e-3, 2.0), (1, 1e-9, 2.0), (1, 1e-12, 2.0), (2, 1e-6, 2.0), (2, 1e-12, 2.0), (3, 1e-4, 2.0),
+            (3, 1e-9, 2.0), (2, 1e-6, 1.5), (3, 1e-5, 1.25)]
+
+
+@pytest.mark.parametrize("d,eps,sigma", T3_CASES)
+def test_nufft_type3_vs_direct(oracle_mod, d, eps, sigma):
+    """The type 3 steps within 10 eps of the exact sum, for point clouds off centre and of widths
+    other than 2 pi (sources in [-3, 7)^d, targets in [-20, 5)^d)."""
+    rng = _rng(23 + d)
+    M, K = 900, 700
+    X = [rng.uniform(-3, 7, M) for _ in range(d)]
+    S = [rng.uniform(-20, 5, K) for _ in range(d)]
+    c = _rand_complex(rng, M)
+    f = oracle_mod.nufft_type3(X, c, S, eps, sigma)
+    assert oracle_mod.rel_l2(f, oracle_mod.direct_type3(X, c, S)) <= 10 * eps
+
+
+def test_nufft_type3_degenerate_and_translation(oracle_mod):
+    rng = _rng(27)
+    eps = 1e-8
+    x = [rng.uniform(-1, 1, 300)]
+    c = _rand_complex(rng, 300)
+    # every target at one frequency; every source at one place; a single target
+    for X, S in (([x[0]], [np.full(40, 3.3)]), ([np.full(300, 0.7)], [rng.uniform(-5, 5, 40)]),
+                 ([x[0]], [np.array([12.5])])):
+        f = oracle_mod.nufft_type3(X, c, S, eps)
+        assert oracle_mod.rel_l2(f, oracle_mod.direct_type3(X, c, S)) <= 10 * eps
+    # moving every source by a multiplies f_k by exp(i s_k a)
+    S = [rng.uniform(-40, 40, 200), rng.uniform(-10, 30, 200)]
+    X = [rng.uniform(-2, 2, 300), rng.uniform(0, 3, 300)]
+    a = (5.25, -1.5)
+    f0 = oracle_mod.nufft_type3(X, c, S, eps)
+    f1 = oracle_mod.nufft_type3([X[0] + a[0], X[1] + a[1]], c, S, eps)
+    assert oracle_mod.rel_l2(f1, f0 * np.exp(1j * (S[0] * a[0] + S[1] * a[1]))) <= 20 * eps
+
+
 def test_nufft_clustered_vs_direct(oracle_mod):
     wl = scaled(WORKLOADS["3d_n128_m16m_f32_e5_cluster"], N=(16, 16, 16), M=3000)
     inp = make_inputs(wl)
