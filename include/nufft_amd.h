@@ -81,7 +81,10 @@ int nufft_default_opts(nufft_opts* opts);
 
 /*
  * Create a plan.
- *   type      1 (nonuniform -> uniform, eq. (1)) or 2 (uniform -> nonuniform, eq. (3)).
+ *   type      1 (nonuniform -> uniform, eq. (1)), 2 (uniform -> nonuniform, eq. (3)) or
+ *             3 (nonuniform -> nonuniform, f_k = sum_j c_j exp(+i s_k.x_j); see
+ *             nufft_setpts_type3; N is not used and may be NULL; sigma must be 2, else
+ *             NUFFT_ERR_UNSUPPORTED).
  *   dim       1, 2 or 3.
  *   N         host array of dim mode counts (N1[, N2[, N3]]), each >= 1.
  *   eps       requested relative tolerance > 0.  Kernel width w = ceil(log10(1/eps)) + 1
@@ -117,9 +120,29 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
 int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z);
 
 /*
+ * Type 3 points: M sources (x, y, z: device arrays, any finite values) and K targets (s, t, u:
+ * device arrays of K frequencies, any finite values); unused dimensions NULL.  nufft_execute
+ * then maps c (M complex) to f (K complex), f_k ~ sum_j c_j exp(+i (s_k x_j + t_k y_j + u_k z_j)).
+ * Type 3 is not on the cuFINUFFT paper's pages (Sec. I-B, item (4), lists it as not provided);
+ * the steps are built from those of Sec. II: per dimension the sources are centred and scaled
+ * into [-pi, pi) and spread (eq. (7)) onto a fine grid of n = smallest even 5-smooth >=
+ * max(2 sigma X S / pi + w, 2 w) cells (X, S: half-widths of the sources and targets), the
+ * grid's Fourier sum is evaluated at the scaled targets by a type 2 NUFFT with N = n modes, and
+ * each target is divided by the kernel transform phihat (eq. (4)) with the centring phases
+ * restored.  The accuracy is about that of the tolerance, as for types 1 and 2.  Errors:
+ * NUFFT_ERR_BAD_ARG (not a type 3 plan, M or K out of range, null array, fine grid above
+ * 2^31 - 1 cells), NUFFT_ERR_POINTS (a non-finite coordinate).  Blocks the host (reads back the
+ * coordinate ranges, then the inner sorts).  nufft_execute_adjoint, the many-vector calls and
+ * the single-step calls return NUFFT_ERR_UNSUPPORTED on a type 3 plan.
+ */
+int nufft_setpts_type3(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z, int64_t K,
+                       const void* s, const void* t, const void* u);
+
+/*
  * Run the transform on the points of the last setpts.
  *   type 1: reads c (M complex), writes f (prod N complex).
  *   type 2: reads f, writes c.
+ *   type 3: reads c (M complex), writes f (K complex).
  * Asynchronous on the plan's stream.  NUFFT_ERR_BAD_STATE before a successful setpts.
  */
 int nufft_execute(nufft_plan plan, void* c, void* f);
@@ -167,6 +190,8 @@ const char* nufft_last_error(nufft_plan plan);
  *                  x-y column block where their kernel support starts, see nufft_get_sort;
  *                  else 0), column block edge s (1 when there is no column order)
  *   info_d[0..2]:  beta, eps, sigma
+ * For a type 3 plan n1..n3 is the transform's fine grid (after setpts_type3), N1..N3 are 1 and
+ * the bin fields are those of the plan itself (0 / 1).
  * Either pointer may be NULL.
  */
 int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d);

@@ -31,6 +31,7 @@ SIGNATURES = {
     "nufft_plan_create": (_I, [_I, _I, ctypes.POINTER(_L), _D, _I, _P, ctypes.POINTER(NufftOpts),
                                ctypes.POINTER(_P)]),
     "nufft_setpts": (_I, [_P, _L, _P, _P, _P]),
+    "nufft_setpts_type3": (_I, [_P, _L, _P, _P, _P, _L, _P, _P, _P]),
     "nufft_execute": (_I, [_P, _P, _P]),
     "nufft_execute_adjoint": (_I, [_P, _P, _P]),
     "nufft_execute_many": (_I, [_P, _I, _P, _P]),
@@ -101,11 +102,15 @@ def _complex_dtype(prec: int):
 
 
 class Plan:
-    """A type 1 or type 2 NUFFT plan on the current HIP device (see include/nufft_amd.h).
+    """A type 1, 2 or 3 NUFFT plan on the current HIP device (see include/nufft_amd.h).
 
     plan = Plan(1, (N1, N2, N3), eps=1e-5, precision="f32")
     plan.setpts(x, y, z)          # device tensors of M coordinates in [-pi, pi)
     plan.execute(c, f)            # type 1: c (M,) complex in, f (N3, N2, N1) complex out
+
+    plan = Plan(3, d, eps)        # type 3 in d dimensions (N is the dimension count)
+    plan.setpts_type3([x, y], [s, t])   # M sources, K targets (device tensors, any finite values)
+    plan.execute(c, f)            # c (M,) in, f (K,) out
     """
 
     def __init__(self, nufft_type: int, N: Sequence[int], eps: float, precision: str = "f32",
@@ -119,8 +124,13 @@ class Plan:
         self._lib = lib
         self._h = None
         self.type = int(nufft_type)
-        self.N = tuple(int(v) for v in N)
+        if self.type == 3:
+            d = int(N) if not hasattr(N, "__len__") else len(N)
+            self.N = (1,) * d
+        else:
+            self.N = tuple(int(v) for v in N)
         self.dim = len(self.N)
+        self.K = -1
         self.prec = 0 if precision == "f32" else 1
         opts = NufftOpts()
         lib.nufft_default_opts(ctypes.byref(opts))
@@ -218,12 +228,26 @@ class Plan:
         self._pts_keepalive = coords   # the library copies; kept only until the stream passes
         return self
 
+    def setpts_type3(self, X, S):
+        """Type 3: sources X (list of d device tensors of M values) and targets S (list of d
+        device tensors of K frequencies)."""
+        if self.type != 3 or len(X) != self.dim or len(S) != self.dim:
+            raise ValueError(f"a type 3 plan in {self.dim}D takes {self.dim} source and target arrays")
+        rd = _real_dtype(self.prec)
+        M, K = X[0].numel(), S[0].numel()
+        xp = [self._dev_tensor(t, rd, M, "x") for t in X] + [ctypes.c_void_p(0)] * (3 - self.dim)
+        sp = [self._dev_tensor(t, rd, K, "s") for t in S] + [ctypes.c_void_p(0)] * (3 - self.dim)
+        self._check(self._lib.nufft_setpts_type3(self._h, M, *xp, K, *sp))
+        self.M, self.K = M, K
+        self.n = self.info()["n"]
+        return self
+
     def execute(self, c, f):
         if self.M < 0:
             raise NufftError(NUFFT_ERR_BAD_STATE, "setpts first")
         cd = _complex_dtype(self.prec)
         cp = self._dev_tensor(c, cd, self.M, "c")
-        fp = self._dev_tensor(f, cd, self.nmodes, "f")
+        fp = self._dev_tensor(f, cd, self.K if self.type == 3 else self.nmodes, "f")
         self._check(self._lib.nufft_execute(self._h, cp, fp))
         return f if self.type == 1 else c
 

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnufft_amd.so")
 
-SOURCES = ["plan.cpp", "binsort.hip", "spread.hip", "interp.hip", "deconv.hip"]
+SOURCES = ["plan.cpp", "binsort.hip", "spread.hip", "interp.hip", "deconv.hip", "t3.hip"]
 ARCH = "gfx950"
 
 # Packed FP32 instructions are disabled for every device compilation (the compiler otherwise

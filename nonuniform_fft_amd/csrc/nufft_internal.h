@@ -119,6 +119,21 @@ struct nufft_plan_s {
     size_t sort_tmp_cap = 0;
     size_t pts_cap = 0;                 // capacity (points) of xs / perm
 
+    // type 3: an inner type 1 plan spreads the scaled sources onto its fine grid (t3_n), an inner
+    // type 2 plan evaluates that grid's Fourier sum at the scaled targets
+    nufft_plan t3_spread = nullptr;
+    nufft_plan t3_eval = nullptr;
+    int64_t t3_n[3] = {0, 0, 0};
+    int64_t K = -1;                     // targets (type 3)
+    nufft::DevBuf t3_part;              // min / max partials
+    nufft::DevBuf t3_y;                 // scaled sources, d arrays of M
+    nufft::DevBuf t3_theta;             // scaled targets, d arrays of K
+    nufft::DevBuf t3_pre;               // per-source phases (M complex)
+    nufft::DevBuf t3_post;              // per-target factors (K complex)
+    nufft::DevBuf t3_cp;                // phased strengths (M complex)
+    nufft::DevBuf t3_cin;               // inner type 2 output (K complex)
+    nufft::DevBuf t3_tab;               // quadrature table for phihat
+
     // many-vector batches: nv fine grids, and (fp64) the strengths gathered in sorted order
     nufft::DevBuf grid_many;
     nufft::DevBuf c_many;
@@ -212,6 +227,20 @@ hipError_t launch_deconvolve(int prec, int dim, const int64_t* N, const int64_t*
                              const void* pcorr, const void* fhat, void* f, hipStream_t st, int nv = 1);
 hipError_t launch_precorrect_pad(int prec, int dim, const int64_t* N, const int64_t* n,
                                  const void* pcorr, const void* f, void* fhat, hipStream_t st, int nv = 1);
+// Type 3 helpers (t3.hip).  minmax: per-block (min, max) pairs of one array into part
+// (t3_minmax_blocks() pairs; min is NaN when the block saw a non-finite value).
+int t3_minmax_blocks();
+hipError_t launch_t3_minmax(int prec, const void* a, int64_t n, double* part, hipStream_t st);
+// y = (((x - ctr) / div) * mul1) * mul2 in fp64, rounded to the plan precision
+hipError_t launch_t3_scale(int prec, const void* x, int64_t n, double ctr, double div, double mul1, double mul2,
+                           void* y, hipStream_t st);
+// per-source phases pre (M complex) and per-target factors post (K complex); tab holds nq
+// quadrature abscissae sin(theta_q) then nq weights for phihat(u) = sum_q wt_q cos(u sin(theta_q))
+hipError_t launch_t3_factors(int prec, int dim, const double* C, const double* D, const double* gamma,
+                             const double* alpha, const double* off, double corr, const void* const* x, int64_t M,
+                             void* pre, const void* const* s, int64_t K, const double* tab, int nq, void* post,
+                             hipStream_t st);
+hipError_t launch_t3_cmul(int prec, const void* a, const void* b, int64_t n, void* out, hipStream_t st);
 // Largest LDS tile (bytes) the SM spreading kernel may use.
 size_t spread_lds_limit();
 size_t spread_tile_bytes(int prec, int dim, int w, const int* m);

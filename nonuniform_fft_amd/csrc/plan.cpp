@@ -382,6 +382,23 @@ int check_plan(nufft_plan p) {
     return NUFFT_OK;
 }
 
+// Entry points that act on the fine grid of a type 1 / type 2 plan.
+int check_not_type3(nufft_plan p) {
+    if (p->type == 3) return fail(p, NUFFT_ERR_UNSUPPORTED, "not available on a type 3 plan");
+    return NUFFT_OK;
+}
+
+// Type 3 (see nufft_setpts_type3): f = post * T2(spread(pre * c)).
+int run_type3(nufft_plan plan, const void* c, void* f) {
+    if (plan->M > 0) NUFFT_HIP(nufft::launch_t3_cmul(plan->prec, c, plan->t3_pre.p, plan->M, plan->t3_cp.p, plan->stream));
+    int rc = nufft_spread(plan->t3_spread, plan->t3_cp.p, plan->t3_spread->grid.p);
+    if (rc != NUFFT_OK) return fail(plan, rc, std::string("type 3 spreading: ") + plan->t3_spread->last_error);
+    rc = nufft_execute(plan->t3_eval, plan->t3_cin.p, plan->t3_spread->grid.p);
+    if (rc != NUFFT_OK) return fail(plan, rc, std::string("type 3 evaluation: ") + plan->t3_eval->last_error);
+    if (plan->K > 0) NUFFT_HIP(nufft::launch_t3_cmul(plan->prec, plan->t3_cin.p, plan->t3_post.p, plan->K, f, plan->stream));
+    return NUFFT_OK;
+}
+
 int check_points(nufft_plan p) {
     if (p->M < 0) return fail(p, NUFFT_ERR_BAD_STATE, "no points: call nufft_setpts first");
     return NUFFT_OK;
@@ -422,8 +439,12 @@ int nufft_destroy(nufft_plan plan) {
     for (rocfft_plan fp : plan->fft_many)
         if (fp) rocfft_plan_destroy(fp);
     if (plan->fft_info) rocfft_execution_info_destroy(plan->fft_info);
+    if (plan->t3_spread) nufft_destroy(plan->t3_spread);
+    if (plan->t3_eval) nufft_destroy(plan->t3_eval);
     for (DevBuf* b : {&plan->grid, &plan->pcorr, &plan->fft_work, &plan->xs, &plan->perm, &plan->counts,
-                      &plan->offsets, &plan->sub, &plan->sort_tmp, &plan->grid_many, &plan->c_many})
+                      &plan->offsets, &plan->sub, &plan->sort_tmp, &plan->grid_many, &plan->c_many, &plan->t3_part,
+                      &plan->t3_y, &plan->t3_theta, &plan->t3_pre, &plan->t3_post, &plan->t3_cp, &plan->t3_cin,
+                      &plan->t3_tab})
         dev_free(plan, *b);
     if (plan->ev_ok)
         for (auto& e : plan->ev) (void)hipEventDestroy(e);
@@ -435,10 +456,10 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
                       const nufft_opts* opts, nufft_plan* out) {
     if (!out) return NUFFT_ERR_BAD_ARG;
     *out = nullptr;
-    if ((type != 1 && type != 2) || dim < 1 || dim > 3 || !N || (precision != 0 && precision != 1))
+    if (type < 1 || type > 3 || dim < 1 || dim > 3 || (!N && type != 3) || (precision != 0 && precision != 1))
         return NUFFT_ERR_BAD_ARG;
     if (!(eps > 0.0) || !std::isfinite(eps)) return NUFFT_ERR_BAD_ARG;
-    for (int i = 0; i < dim; ++i)
+    for (int i = 0; type != 3 && i < dim; ++i)
         if (N[i] < 1 || N[i] > (int64_t(1) << 28)) return NUFFT_ERR_BAD_ARG;
 
     nufft_plan plan = new (std::nothrow) nufft_plan_s();
@@ -468,6 +489,20 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
     }
     plan->w = w;
     plan->beta = (sigma == 2.0) ? 2.30 * w : (2.30 / (0.75 * nufft::kPi)) * nufft::kPi * (1.0 - 0.5 / sigma) * w;
+    if (type == 3) {
+        // the fine grid, the inner plans and everything else depend on the points (setpts_type3)
+        if (sigma != 2.0) {
+            delete plan;
+            return NUFFT_ERR_UNSUPPORTED;
+        }
+        hipError_t he3 = hipGetDevice(&plan->device);
+        if (he3 != hipSuccess) {
+            delete plan;
+            return NUFFT_ERR_HIP;
+        }
+        *out = plan;
+        return status;
+    }
     for (int i = 0; i < 3; ++i) {
         plan->N[i] = i < dim ? N[i] : 1;
         plan->n[i] = i < dim ? next_5smooth(std::max<int64_t>((int64_t)std::ceil(sigma * (double)N[i] - 1e-9), w)) : 1;
@@ -580,6 +615,7 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
 
 int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (plan->type == 3) return fail(plan, NUFFT_ERR_BAD_ARG, "a type 3 plan takes nufft_setpts_type3");
     if (M < 0 || M > INT32_MAX) return fail(plan, NUFFT_ERR_BAD_ARG, "M out of range [0, 2^31-1]");
     const void* X[3] = {x, y, z};
     if (M > 0)
@@ -666,16 +702,171 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     return NUFFT_OK;
 }
 
+int nufft_setpts_type3(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z, int64_t K,
+                       const void* s, const void* t, const void* u) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (plan->type != 3) return fail(plan, NUFFT_ERR_BAD_ARG, "nufft_setpts_type3 needs a type 3 plan");
+    if (M < 0 || M > INT32_MAX || K < 0 || K > INT32_MAX)
+        return fail(plan, NUFFT_ERR_BAD_ARG, "M or K out of range [0, 2^31-1]");
+    const void* X[3] = {x, y, z};
+    const void* S[3] = {s, t, u};
+    const int dim = plan->dim;
+    for (int i = 0; i < dim; ++i)
+        if ((M > 0 && !X[i]) || (K > 0 && !S[i])) return fail(plan, NUFFT_ERR_BAD_ARG, "null coordinate array");
+    plan->M = -1;
+    plan->K = -1;
+    const size_t rs = real_size(plan);
+    int rc;
+
+    // centres and half-widths of sources and targets
+    const int nb = nufft::t3_minmax_blocks();
+    if ((rc = dev_alloc(plan, plan->t3_part, (size_t)2 * dim * nb * 2 * sizeof(double), "type 3 partials")) != NUFFT_OK)
+        return rc;
+    double* part = (double*)plan->t3_part.p;
+    for (int i = 0; i < dim; ++i) {
+        NUFFT_HIP(nufft::launch_t3_minmax(plan->prec, X[i], M, part + (size_t)(2 * i) * nb * 2, plan->stream));
+        NUFFT_HIP(nufft::launch_t3_minmax(plan->prec, S[i], K, part + (size_t)(2 * i + 1) * nb * 2, plan->stream));
+    }
+    std::vector<double> hp((size_t)2 * dim * nb * 2);
+    NUFFT_HIP(hipMemcpyAsync(hp.data(), part, hp.size() * sizeof(double), hipMemcpyDeviceToHost, plan->stream));
+    NUFFT_HIP(hipStreamSynchronize(plan->stream));
+    double C[3] = {0, 0, 0}, Xh[3] = {0, 0, 0}, D[3] = {0, 0, 0}, Sh[3] = {0, 0, 0};
+    for (int a = 0; a < 2 * dim; ++a) {
+        double lo = INFINITY, hi = -INFINITY;
+        for (int b = 0; b < nb; ++b) {
+            const double l = hp[((size_t)a * nb + b) * 2], h = hp[((size_t)a * nb + b) * 2 + 1];
+            if (std::isnan(l)) return fail(plan, NUFFT_ERR_POINTS, "a type 3 coordinate is not finite");
+            lo = std::min(lo, l);
+            hi = std::max(hi, h);
+        }
+        const bool any = (a % 2 == 0) ? M > 0 : K > 0;
+        const double ctr = any ? 0.5 * (hi + lo) : 0.0, half = any ? 0.5 * (hi - lo) : 0.0;
+        if (a % 2 == 0) {
+            C[a / 2] = ctr;
+            Xh[a / 2] = half;
+        } else {
+            D[a / 2] = ctr;
+            Sh[a / 2] = half;
+        }
+    }
+
+    // fine grid n (smallest even 5-smooth >= max(2 sigma X S / pi + w, 2 w)), h = 2 pi / n and
+    // scale gamma: n / (2 sigma S) keeps the scaled targets in the kernel's band and, by the
+    // choice of n, the scaled sources (x - C) / gamma inside [-pi, pi) with the kernel's reach
+    const int w = plan->w;
+    const double sigma = plan->sigma;
+    int64_t n[3] = {1, 1, 1};
+    double h[3] = {1, 1, 1}, gam[3] = {1, 1, 1}, alpha[3] = {0, 0, 0}, off[3] = {0, 0, 0};
+    int64_t cells = 1;
+    for (int i = 0; i < dim; ++i) {
+        const double v = std::max(2.0 * sigma * Xh[i] * Sh[i] / nufft::kPi + w, 2.0 * w);
+        if (!(v < (double)(int64_t(1) << 30))) return fail(plan, NUFFT_ERR_BAD_ARG, "type 3 fine grid too large");
+        int64_t ni = std::max<int64_t>((int64_t)std::ceil(v - 1e-9), 2);
+        while (ni % 2 || !is_5smooth(ni)) ++ni;
+        n[i] = ni;
+        h[i] = 2.0 * nufft::kPi / (double)ni;
+        if (Sh[i] > 0) gam[i] = (double)ni / (2.0 * sigma * Sh[i]);
+        else if (Xh[i] > 0) gam[i] = Xh[i] * (double)ni / (nufft::kPi * (double)(ni - w));
+        else gam[i] = 1.0;
+        alpha[i] = w * h[i] / 2.0;
+        off[i] = h[i] * (double)(ni / 2) - nufft::kPi;
+        cells *= ni;
+        if (cells > (int64_t(1) << 31) - 1) return fail(plan, NUFFT_ERR_BAD_ARG, "type 3 fine grid too large");
+    }
+
+    // inner plans: a type 1 plan whose fine grid is n (N = n / 2) and a type 2 plan with N = n modes
+    bool same = plan->t3_spread != nullptr;
+    for (int i = 0; i < dim; ++i) same = same && plan->t3_n[i] == n[i];
+    if (!same) {
+        if (plan->t3_spread) nufft_destroy(plan->t3_spread);
+        if (plan->t3_eval) nufft_destroy(plan->t3_eval);
+        plan->t3_spread = plan->t3_eval = nullptr;
+        nufft_opts o = plan->opts;
+        o.upsampfac = 0.0;
+        o.timing = 0;
+        o.max_device_bytes = 0;
+        int64_t Nh[3], Nf[3];
+        for (int i = 0; i < dim; ++i) {
+            Nh[i] = n[i] / 2;
+            Nf[i] = n[i];
+        }
+        rc = nufft_plan_create(1, dim, Nh, plan->eps, plan->prec, plan->stream, &o, &plan->t3_spread);
+        if (rc < 0) return fail(plan, rc, "type 3: inner spreading plan");
+        rc = nufft_plan_create(2, dim, Nf, plan->eps, plan->prec, plan->stream, &o, &plan->t3_eval);
+        if (rc < 0) return fail(plan, rc, std::string("type 3: inner evaluation plan: ") + nufft_strerror(rc));
+        for (int i = 0; i < dim; ++i) {
+            if (plan->t3_spread->n[i] != n[i]) return fail(plan, NUFFT_ERR_BAD_ARG, "type 3: inner fine grid mismatch");
+            plan->t3_n[i] = n[i];
+            plan->n[i] = n[i];
+        }
+    }
+
+    // scaled sources and targets, sorted by the inner plans
+    const size_t Mm = (size_t)std::max<int64_t>(M, 1), Km = (size_t)std::max<int64_t>(K, 1);
+    if ((rc = dev_alloc(plan, plan->t3_y, Mm * dim * rs, "type 3 scaled sources")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->t3_theta, Km * dim * rs, "type 3 scaled targets")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->t3_pre, Mm * 2 * rs, "type 3 source phases")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->t3_cp, Mm * 2 * rs, "type 3 phased strengths")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->t3_post, Km * 2 * rs, "type 3 target factors")) != NUFFT_OK ||
+        (rc = dev_alloc(plan, plan->t3_cin, Km * 2 * rs, "type 3 inner output")) != NUFFT_OK)
+        return rc;
+    const void* yv[3] = {nullptr, nullptr, nullptr};
+    const void* tv[3] = {nullptr, nullptr, nullptr};
+    for (int i = 0; i < dim; ++i) {
+        void* yi = (char*)plan->t3_y.p + (size_t)i * Mm * rs;
+        void* ti = (char*)plan->t3_theta.p + (size_t)i * Km * rs;
+        NUFFT_HIP(nufft::launch_t3_scale(plan->prec, X[i], M, C[i], gam[i], 1.0, 1.0, yi, plan->stream));
+        NUFFT_HIP(nufft::launch_t3_scale(plan->prec, S[i], K, D[i], 1.0, gam[i], h[i], ti, plan->stream));
+        yv[i] = yi;
+        tv[i] = ti;
+    }
+    rc = nufft_setpts(plan->t3_spread, M, yv[0], yv[1], yv[2]);
+    if (rc != NUFFT_OK) return fail(plan, rc, std::string("type 3 sources: ") + plan->t3_spread->last_error);
+    rc = nufft_setpts(plan->t3_eval, K, tv[0], tv[1], tv[2]);
+    if (rc != NUFFT_OK) return fail(plan, rc, std::string("type 3 targets: ") + plan->t3_eval->last_error);
+
+    // per-source phases and per-target factors; phihat by Gauss-Legendre in theta (z = sin theta),
+    // 64 nodes on [-pi/2, pi/2] folded to the 32 positive ones (the integrand is even)
+    const int nq = 32;
+    std::vector<double> g64, w64, tab(2 * nq);
+    gauss_legendre(2 * nq, g64, w64);
+    int q = 0;
+    for (int i = 0; i < 2 * nq; ++i) {
+        if (g64[i] <= 0) continue;
+        const double th = 0.5 * nufft::kPi * g64[i];
+        tab[q] = std::sin(th);
+        tab[nq + q] = 2.0 * 0.5 * nufft::kPi * w64[i] * std::exp(plan->beta * (std::cos(th) - 1.0)) * std::cos(th);
+        ++q;
+    }
+    if (q != nq) return fail(plan, NUFFT_ERR_BAD_ARG, "type 3: quadrature table");
+    if ((rc = dev_alloc(plan, plan->t3_tab, tab.size() * sizeof(double), "type 3 quadrature table")) != NUFFT_OK)
+        return rc;
+    NUFFT_HIP(hipMemcpyAsync(plan->t3_tab.p, tab.data(), tab.size() * sizeof(double), hipMemcpyHostToDevice,
+                             plan->stream));
+    NUFFT_HIP(nufft::launch_t3_factors(plan->prec, dim, C, D, gam, alpha, off, 2.0 / w, X, M, plan->t3_pre.p, S, K,
+                                       (const double*)plan->t3_tab.p, nq, plan->t3_post.p, plan->stream));
+    // the host table must outlive the copy
+    NUFFT_HIP(hipStreamSynchronize(plan->stream));
+    plan->M = M;
+    plan->K = K;
+    return NUFFT_OK;
+}
+
 int nufft_execute(nufft_plan plan, void* c, void* f) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
     int rc;
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
+    if (plan->type == 3) {
+        if ((plan->M > 0 && !c) || (plan->K > 0 && !f)) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
+        return run_type3(plan, c, f);
+    }
     if ((plan->M > 0 && !c) || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
     return plan->type == 1 ? run_type1(plan, c, f) : run_type2(plan, c, f);
 }
 
 int nufft_execute_adjoint(nufft_plan plan, void* c, void* f) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (check_not_type3(plan) != NUFFT_OK) return NUFFT_ERR_UNSUPPORTED;
     int rc;
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
     if ((plan->M > 0 && !c) || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
@@ -684,6 +875,7 @@ int nufft_execute_adjoint(nufft_plan plan, void* c, void* f) {
 
 int nufft_execute_many(nufft_plan plan, int nvec, void* c, void* f) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (check_not_type3(plan) != NUFFT_OK) return NUFFT_ERR_UNSUPPORTED;
     int rc;
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
     if (nvec < 1) return fail(plan, NUFFT_ERR_BAD_ARG, "nvec must be >= 1");
@@ -693,6 +885,7 @@ int nufft_execute_many(nufft_plan plan, int nvec, void* c, void* f) {
 
 int nufft_execute_adjoint_many(nufft_plan plan, int nvec, void* c, void* f) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (check_not_type3(plan) != NUFFT_OK) return NUFFT_ERR_UNSUPPORTED;
     int rc;
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
     if (nvec < 1) return fail(plan, NUFFT_ERR_BAD_ARG, "nvec must be >= 1");
@@ -742,6 +935,7 @@ int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d) {
 
 int nufft_spread(nufft_plan plan, const void* c, void* grid) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (check_not_type3(plan) != NUFFT_OK) return NUFFT_ERR_UNSUPPORTED;
     int rc;
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
     if (!grid || (plan->M > 0 && !c)) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
@@ -754,6 +948,7 @@ int nufft_spread(nufft_plan plan, const void* c, void* grid) {
 
 int nufft_interp(nufft_plan plan, const void* grid, void* c) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (check_not_type3(plan) != NUFFT_OK) return NUFFT_ERR_UNSUPPORTED;
     int rc;
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
     if (!grid || (plan->M > 0 && !c)) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
@@ -764,6 +959,7 @@ int nufft_interp(nufft_plan plan, const void* grid, void* c) {
 
 int nufft_deconvolve(nufft_plan plan, const void* fhat, void* f) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (check_not_type3(plan) != NUFFT_OK) return NUFFT_ERR_UNSUPPORTED;
     if (!fhat || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
     NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, fhat, f,
                                        plan->stream));
@@ -772,6 +968,7 @@ int nufft_deconvolve(nufft_plan plan, const void* fhat, void* f) {
 
 int nufft_precorrect_pad(nufft_plan plan, const void* f, void* fhat) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (check_not_type3(plan) != NUFFT_OK) return NUFFT_ERR_UNSUPPORTED;
     if (!fhat || !f) return fail(plan, NUFFT_ERR_BAD_ARG, "null data pointer");
     NUFFT_HIP(nufft::launch_precorrect_pad(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, f, fhat,
                                            plan->stream));
@@ -780,6 +977,7 @@ int nufft_precorrect_pad(nufft_plan plan, const void* f, void* fhat) {
 
 int nufft_get_sort(nufft_plan plan, int32_t* perm, int32_t* counts, int32_t* subproblems) {
     if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (check_not_type3(plan) != NUFFT_OK) return NUFFT_ERR_UNSUPPORTED;
     int rc;
     if ((rc = check_points(plan)) != NUFFT_OK) return rc;
     if (perm && plan->M > 0)

@@ -440,18 +440,21 @@ class Type3Params:
                 self.gamma.append(1.0)
 
 
-def nufft_type3(X, c, S, eps: float, sigma: float = 2.0) -> np.ndarray:
-    """Type 3 by the steps above: f_k ~ sum_j c_j exp(+i s_k . x_j), k = 1..K."""
+def nufft_type3(X, c, S, eps: float, sigma: float = 2.0, coord_dtype=np.float64) -> np.ndarray:
+    """Type 3 by the steps above: f_k ~ sum_j c_j exp(+i s_k . x_j), k = 1..K.  The scaled
+    coordinates y = (x - C) / gamma and theta = ((s - D) gamma) h are computed in fp64 and then
+    stored in coord_dtype (a single-precision transform keeps them in single precision)."""
     prm = Type3Params(X, S, eps, sigma)
     xs = [np.asarray(x, dtype=np.float64) for x in X]
     ss = [np.asarray(s, dtype=np.float64) for s in S]
-    y = [(x - Ci) / g for x, Ci, g in zip(xs, prm.C, prm.gamma)]
+    y = [((x - Ci) / g).astype(coord_dtype).astype(np.float64) for x, Ci, g in zip(xs, prm.C, prm.gamma)]
     pre = np.zeros(xs[0].size)
     for x, Ci, Di in zip(xs, prm.C, prm.D):
         pre = pre + Di * (x - Ci)
     cp = np.asarray(c, dtype=np.complex128) * np.exp(1j * pre)
     b = spread(y, cp, prm.n, prm.w, prm.beta)
-    theta = [(s - Di) * g * hi for s, Di, g, hi in zip(ss, prm.D, prm.gamma, prm.h)]
+    theta = [((s - Di) * g * hi).astype(coord_dtype).astype(np.float64)
+             for s, Di, g, hi in zip(ss, prm.D, prm.gamma, prm.h)]
     cin = nufft_type2(theta, b, prm.n, eps, sigma)
     out = cin.astype(np.complex128)
     for s, Ci, Di, g, hi, ni in zip(ss, prm.C, prm.D, prm.gamma, prm.h, prm.n):

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "nufft_amd.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nufft_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(nufft_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -42,13 +42,19 @@ def test_host_side_argument_checks():
     assert lib.nufft_destroy(None) == 0
     N = (ctypes.c_int64 * 3)(16, 16, 16)
     h = ctypes.c_void_p()
-    bad = [(3, 2, N, 1e-5, 0), (1, 4, N, 1e-5, 0), (1, 0, N, 1e-5, 0), (1, 2, N, 0.0, 0), (1, 2, N, -1.0, 0),
+    bad = [(4, 2, N, 1e-5, 0), (0, 2, N, 1e-5, 0), (1, 4, N, 1e-5, 0), (1, 0, N, 1e-5, 0), (1, 2, N, 0.0, 0), (1, 2, N, -1.0, 0),
            (1, 2, N, float("nan"), 0), (1, 2, N, 1e-5, 2), (1, 2, None, 1e-5, 0),
            (2, 3, (ctypes.c_int64 * 3)(16, 0, 16), 1e-5, 1)]
     for t, d, n, e, p in bad:
         assert lib.nufft_plan_create(t, d, n, e, p, None, None, ctypes.byref(h)) == -1
         assert not h.value
     assert lib.nufft_plan_create(1, 2, N, 1e-5, 0, None, None, None) == -1
+    # type 3 supports sigma = 2 only
+    o = NufftOpts()
+    lib.nufft_default_opts(ctypes.byref(o))
+    o.upsampfac = 1.5
+    assert lib.nufft_plan_create(3, 2, None, 1e-5, 0, None, ctypes.byref(o), ctypes.byref(h)) == -7
+    assert not h.value
     # an upsampling factor outside [1.25, 2] is rejected before any device work
     for sigma in (1.1, 2.5, -1.0, float("nan")):
         o = NufftOpts()
