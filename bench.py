@@ -209,6 +209,47 @@ def many_vectors(steps, nvec, workloads):
         print(json.dumps({"workload": name, "nvec": nvec, **res}), flush=True)
 
 
+def type3_bench(steps):
+    """Type 3 timing: M sources uniform in [-pi, pi)^d, K targets uniform in [-F, F)^d (F = N/2,
+    so the space-bandwidth product matches a type 1 of N^d modes); one JSON line per case with
+    setpts and execute times and sources+targets per second of execute."""
+    import numpy as np
+    import torch
+
+    import nonuniform_fft_amd as nf
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cases = [(3, 1 << 22, 1 << 22, 128, 1e-5, "f32"), (2, 1 << 22, 1 << 22, 1024, 1e-5, "f32"),
+             (1, 1 << 24, 1 << 24, 1 << 20, 1e-6, "f32")]
+    for d, M, K, N, eps, prec in cases:
+        rng = np.random.default_rng(1010 + d)
+        rd = np.float32 if prec == "f32" else np.float64
+        X = [torch.from_numpy(rng.uniform(-np.pi, np.pi, M).astype(rd)).to(dev) for _ in range(d)]
+        S = [torch.from_numpy(rng.uniform(-N / 2, N / 2, K).astype(rd)).to(dev) for _ in range(d)]
+        cdt = torch.complex64 if prec == "f32" else torch.complex128
+        c = torch.randn(M, dtype=cdt, device=dev)
+        f = torch.empty(K, dtype=cdt, device=dev)
+        p = nf.Plan(3, d, eps, prec)
+        p.setpts_type3(X, S)
+        p.execute(c, f)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            p.setpts_type3(X, S)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            p.execute(c, f)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        set_ms, ex_ms = (t1 - t0) * 1e3 / steps, (t2 - t1) * 1e3 / steps
+        print(json.dumps({"type3": f"{d}D M={M} K={K} targets in [-{N // 2}, {N // 2})^{d} {prec} eps={eps:g}",
+                          "fine_grid": list(p.n), "setpts_ms": set_ms, "exec_ms": ex_ms,
+                          "pts_per_s_exec": (M + K) / (ex_ms * 1e-3)}), flush=True)
+        p.destroy()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,9 +265,13 @@ def main():
                     help="only run a plain copy of this many bytes (counter calibration)")
     ap.add_argument("--compare", action="store_true",
                     help="only compare the GM, GM-sort and SM methods (JSON line per method and type)")
+    ap.add_argument("--type3", action="store_true", help="only time type 3 transforms")
     ap.add_argument("--many", type=int, default=0,
                     help="only time many-vector execution with this many vectors per call")
     args = ap.parse_args()
+    if args.type3:
+        type3_bench(args.steps)
+        return
     if args.many:
         many_vectors(args.steps, args.many, ["2d_n64_m1e4_f32_e5", "2d_n1024_m4m_f32_e5", "3d_n128_m16m_f32_e5",
                                              "1d_n1m_m16m_f32_e6"])
