@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
         int l = 0;
         if (!fold_t(t, a.n[i], l)) { ok = false; l = 0; }
         tf[i] = t;   // folded
-        bidx[i] = l / a.m[i];
+        bidx[i] = fast_div(l, a.fdm[i]);
     }
     int key = bidx[0] + a.nb[0] * (bidx[1] + a.nb[1] * bidx[2]);
     if (DIM == 3 && a.colw > 0) {
@@ -57,8 +57,8 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
             lo[i] = (int)ceil(__dsub_rn(tf[i], 0.5 * (double)a.colw)) - (bidx[i] * a.m[i] - a.colw / 2);
             lo[i] = min(max(lo[i], 0), a.m[i]);
         }
-        const int ncx = (a.m[0] + a.colstep) / a.colstep;
-        key = key * a.ncol + ((lo[1] / a.colstep) * ncx + lo[0] / a.colstep) * (a.m[2] + 1) + lo[2];
+        const int ncx = fast_div(a.m[0] + a.colstep, a.fdc);
+        key = key * a.ncol + (fast_div(lo[1], a.fdc) * ncx + fast_div(lo[0], a.fdc)) * (a.m[2] + 1) + lo[2];
     }
     if (!ok) {
         key = 0;
@@ -463,9 +463,12 @@ hipError_t scatter_dim(int dim, const int32_t* ki, const int32_t* vi, int32_t* k
 
 size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec) { return layout(M, nbins, dim, prec).end; }
 
-hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_t* offsets,
+hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int32_t* offsets,
                        void* xs_out, void* scratch, size_t scratch_bytes, int64_t* nsub_dev,
                        int* bad_dev, hipStream_t st) {
+    SortArgs a = a_in;
+    for (int i = 0; i < 3; ++i) a.fdm[i] = make_fastdiv(std::max(a.m[i], 1));
+    a.fdc = make_fastdiv(std::max(a.colstep, 1));
     SortLayout L = layout(a.M, a.nbins, a.dim, a.prec);
     if (scratch_bytes < L.end) return hipErrorInvalidValue;
     char* base = (char*)scratch;

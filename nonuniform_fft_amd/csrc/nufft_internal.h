@@ -157,6 +157,22 @@ namespace nufft {
 // Kernel launchers (defined in the .hip files).  All return hipError_t of the launch.
 
 // binsort.hip
+// Division by a fixed d >= 1 as a multiply-high: q = (umulhi(x, mul) + x) >> shift with
+// shift = ceil(log2 d), mul = floor(2^32 (2^shift - d) / d) + 1, exact for 0 <= x < 2^32.
+struct FastDiv {
+    uint32_t mul;
+    int shift;
+};
+inline FastDiv make_fastdiv(int d) {
+    int s = 0;
+    while ((uint32_t(1) << s) < (uint32_t)d) ++s;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - (uint64_t)d)) / (uint64_t)d + 1;
+    return {(uint32_t)m, s};
+}
+__device__ __forceinline__ int fast_div(int x, FastDiv f) {
+    return (int)(((uint64_t)__umulhi((uint32_t)x, f.mul) + (uint64_t)(uint32_t)x) >> f.shift);
+}
+
 struct SortArgs {
     int dim;
     int prec;
@@ -174,6 +190,8 @@ struct SortArgs {
                    //       0: by original index only
     int colstep;   // column block edge s: support starts c_i in [0, m_i] grouped as c_i / s
     int ncol;      // keys per bin, ceil((m1 + 1) / s) ceil((m2 + 1) / s) (m3 + 1), else 1
+    FastDiv fdm[3];  // division by m_i and by colstep (set by launch_sort)
+    FastDiv fdc;
 };
 // Bytes of scratch the sort needs for M points and the plan's bin count.
 size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec);
