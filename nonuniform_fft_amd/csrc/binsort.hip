@@ -365,12 +365,12 @@ __global__ void k_iota(int32_t* __restrict__ v, int64_t M) {
 }
 
 // offsets[b] = first sorted position whose bin is >= b (offsets[nbins] = M); key = bin * ncol + column.
-__global__ void k_bin_offsets(const int32_t* __restrict__ skeys, int64_t M, int nbins, int ncol,
+__global__ void k_bin_offsets(const int32_t* __restrict__ skeys, int64_t M, int nbins, FastDiv ncol,
                               int32_t* __restrict__ offsets) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i > M) return;
-    int lo = (i == 0) ? 0 : skeys[i - 1] / ncol + 1;
-    int hi = (i == M) ? nbins : skeys[i] / ncol;
+    int lo = (i == 0) ? 0 : fast_div(skeys[i - 1], ncol) + 1;
+    int hi = (i == M) ? nbins : fast_div(skeys[i], ncol);
     for (int b = lo; b <= hi; ++b) offsets[b] = (int32_t)i;
 }
 
@@ -533,7 +533,8 @@ hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int
             k_iota<<<dim3((unsigned)cdiv(M, kBlock)), kBlock, 0, st>>>(perm, M);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        k_bin_offsets<<<dim3((unsigned)cdiv(M + 1, kBlock)), kBlock, 0, st>>>(ki, M, a.nbins, a.ncol, offsets);
+        k_bin_offsets<<<dim3((unsigned)cdiv(M + 1, kBlock)), kBlock, 0, st>>>(ki, M, a.nbins,
+                                                                               make_fastdiv(std::max(a.ncol, 1)), offsets);
     } else {
         if ((e = hipMemsetAsync(offsets, 0, sizeof(int32_t) * (a.nbins + 1), st)) != hipSuccess)
             return e;
