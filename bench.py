@@ -250,6 +250,43 @@ def type3_bench(steps):
         p.destroy()
 
 
+def distribution_stress():
+    """Stage times (HIP events, best of 3 after a warm-up) of the headline workload with its
+    points drawn uniform, Gaussian-clustered and inside an 8-cell box, for SM and GM-sort; one
+    JSON line per (distribution, method)."""
+    import torch
+
+    import nonuniform_fft_amd as nf
+    from nonuniform_fft_amd.workloads import WORKLOADS, make_inputs, scaled
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    base = WORKLOADS["3d_n128_m16m_f32_e5"]
+    for dist in ("uniform", "cluster", "box"):
+        wl = base if dist == "uniform" else scaled(base, dist=dist)
+        inp = make_inputs(wl)
+        X = [torch.from_numpy(x).to(dev) for x in inp["X"]]
+        c = torch.from_numpy(inp["c"]).to(dev)
+        f = torch.from_numpy(inp["f"]).to(dev)
+        fo = torch.empty(tuple(reversed(wl.N)), dtype=c.dtype, device=dev)
+        co = torch.empty(wl.M, dtype=c.dtype, device=dev)
+        for method in (2, 1):
+            p = nf.Plan(1, wl.N, wl.eps, wl.precision, timing=True, method=method)
+            res = {}
+            for k in range(4):
+                p.setpts(*X)
+                p.execute(c, fo)
+                p.execute_adjoint(co, f)
+                torch.cuda.synchronize()
+                st = p.stage_times()
+                if k:
+                    for key in ("sort", "spread", "interp"):
+                        res[key] = min(res.get(key, 1e9), st[key])
+            print(json.dumps({"dist": dist, "method": method, "nsub": p.info()["nsubproblems"],
+                              **{k: round(v, 3) for k, v in res.items()}}), flush=True)
+            p.destroy()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,11 +303,16 @@ def main():
     ap.add_argument("--compare", action="store_true",
                     help="only compare the GM, GM-sort and SM methods (JSON line per method and type)")
     ap.add_argument("--type3", action="store_true", help="only time type 3 transforms")
+    ap.add_argument("--stress", action="store_true",
+                    help="only time uniform / clustered / box point distributions (SM and GM-sort)")
     ap.add_argument("--many", type=int, default=0,
                     help="only time many-vector execution with this many vectors per call")
     args = ap.parse_args()
     if args.type3:
         type3_bench(args.steps)
+        return
+    if args.stress:
+        distribution_stress()
         return
     if args.many:
         many_vectors(args.steps, args.many, ["2d_n64_m1e4_f32_e5", "2d_n1024_m4m_f32_e5", "3d_n128_m16m_f32_e5",
