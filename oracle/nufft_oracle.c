@@ -176,15 +176,15 @@ int oracle_interp(int d, const int64_t* n, int w, double beta, int64_t M,
  * Outputs: bin[j]; counts[b] = number of points in bin b; perm = the points
  * listed bin by bin (a stable counting sort: the list is read out in bin
  * order).  Inside a bin the order is the original index, or, when w_col > 0
- * (3D only), the x-y column block of the point's kernel support first, then
+ * (2D and 3D), the x-y block of the point's kernel support first, then (3D)
  * the z start of the support, then the original index.  The support of a point
  * starts at l0_i = ceil(t_i - w/2); relative to its bin's padded origin
  * o_i = b_i m_i - floor(w/2) that start is c_i = l0_i - o_i in [0, m_i].
  * Starts are grouped in blocks of s x s (s = col_step >= 1): the block is
  * (c_1 / s, c_2 / s), numbered (c_2 / s) ceil((m1 + 1) / s) + c_1 / s, and the
- * in-bin key is block (m3 + 1) + c_3.  This ordering is not from the pages:
- * it is the order the 3D kernels consume, stated here so the permutation can
- * be checked exactly.
+ * in-bin key is block (m3 + 1) + c_3 in 3D, the block in 2D.  This ordering is
+ * not from the pages: it is the order the block-run kernels consume, stated
+ * here so the permutation can be checked exactly.
  */
 int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const double* const* X,
                    int w_col, int col_step, int64_t* bin, int64_t* counts, int64_t* perm)
@@ -195,9 +195,9 @@ int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const d
         if (n[i] < 1 || m[i] < 1) return ORACLE_BAD_ARG;
         nb[i] = (n[i] + m[i] - 1) / m[i];
     }
-    int use_col = (w_col > 0 && d == 3);
+    int use_col = (w_col > 0 && d >= 2);
     int64_t ncx = (m[0] + col_step) / col_step, ncy = (m[1] + col_step) / col_step;
-    int64_t ncol = use_col ? ncx * ncy * (m[2] + 1) : 1;
+    int64_t ncol = use_col ? ncx * ncy * (d == 3 ? m[2] + 1 : 1) : 1;
     int64_t nbins = nb[0] * nb[1] * nb[2];
     int64_t nkeys = nbins * ncol;
     int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
@@ -217,8 +217,12 @@ int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const d
         }
         bin[j] = bi[0] + nb[0] * (bi[1] + nb[1] * bi[2]);
         counts[bin[j]] += 1;
-        key[j] = use_col ? bin[j] * ncol + ((lo[1] / col_step) * ncx + lo[0] / col_step) * (m[2] + 1) + lo[2]
-                         : bin[j];
+        if (!use_col)
+            key[j] = bin[j];
+        else if (d == 3)
+            key[j] = bin[j] * ncol + ((lo[1] / col_step) * ncx + lo[0] / col_step) * (m[2] + 1) + lo[2];
+        else
+            key[j] = bin[j] * ncol + (lo[1] / col_step) * ncx + lo[0] / col_step;
         next[key[j]] += 1;
     }
     int64_t run = 0;

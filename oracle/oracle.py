@@ -487,8 +487,8 @@ def direct_type3(X, c, S, sel: Optional[Sequence[int]] = None) -> np.ndarray:
 
 def binsort(X, n: Sequence[int], m: Sequence[int], w_col: int = 0, col_step: int = 1):
     """Returns (bin_of_point, counts, perm) as int64 arrays; see the C routine.  With w_col > 0
-    (3D) the points of a bin are ordered by the col_step x col_step block of the x-y column where
-    their kernel support starts, then by the z start of the support."""
+    (2D, 3D) the points of a bin are ordered by the col_step x col_step block of the x-y column
+    where their kernel support starts, then (3D) by the z start of the support."""
     lib = _load()
     d = len(n)
     xs, xa = _coords(X)

@@ -572,6 +572,16 @@ def test_bins_column_order_within_bins(oracle_mod, step):
     col = (lo[1] // step) * ncx + lo[0] // step
     expect = np.lexsort((np.arange(4000), lo[2], col, binv))
     np.testing.assert_array_equal(perm, expect)
-    # 2D ignores the column order
-    _, _, p2 = oracle_mod.binsort(X[:2], n[:2], m[:2], w_col=w)
-    np.testing.assert_array_equal(p2, np.argsort(oracle_mod.binsort(X[:2], n[:2], m[:2])[0], kind="stable"))
+    # 2D: the block of the support start, then the original index
+    b2, _, p2 = oracle_mod.binsort(X[:2], n[:2], m[:2], w_col=w, col_step=step)
+    nb0 = (n[0] + m[0] - 1) // m[0]
+    lo2 = []
+    for i in range(2):
+        t = (np.longdouble(X[i]) + np.longdouble(math.pi)) * n[i] / (2 * np.longdouble(math.pi))
+        bi = b2 % nb0 if i == 0 else b2 // nb0
+        lo2.append(np.ceil(t - w / 2).astype(np.int64) - (bi * m[i] - w // 2))
+    col2 = (lo2[1] // step) * ncx + lo2[0] // step
+    np.testing.assert_array_equal(p2, np.lexsort((np.arange(4000), col2, b2)))
+    # 1D ignores the column order
+    _, _, p1 = oracle_mod.binsort(X[:1], n[:1], m[:1], w_col=w)
+    np.testing.assert_array_equal(p1, np.argsort(oracle_mod.binsort(X[:1], n[:1], m[:1])[0], kind="stable"))
