@@ -183,8 +183,9 @@ int oracle_interp(int d, const int64_t* n, int w, double beta, int64_t M,
  * Starts are grouped in blocks of s x s (s = col_step >= 1): the block is
  * (c_1 / s, c_2 / s), numbered (c_2 / s) ceil((m1 + 1) / s) + c_1 / s, and the
  * in-bin key is block (m3 + 1) + c_3 in 3D, the block in 2D.  This ordering is
- * not from the pages: it is the order the block-run kernels consume, stated
- * here so the permutation can be checked exactly.
+ * not from the pages: in 3D it is the order the column-run kernels consume,
+ * stated here so the permutation can be checked exactly (the 2D form is kept
+ * for block orders in 2D; the library's 2D plans use the original index).
  */
 int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const double* const* X,
                    int w_col, int col_step, int64_t* bin, int64_t* counts, int64_t* perm)
