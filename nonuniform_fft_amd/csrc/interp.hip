@@ -82,8 +82,6 @@ __global__ void __launch_bounds__(kInterpBlock) k_interp_gm(GeomArgs g, const cp
 template <typename T, int DIM>
 constexpr int kInterpSmBlock = (DIM == 3) ? 768 : 512;
 
-__host__ __device__ inline int interp_row_pitch(int p1) { return p1; }
-
 template <typename T, int DIM, int W>
 __global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs g, const cplx<T>* __restrict__ grid,
                                                               cplx<T>* __restrict__ c, int p1, int p2,
