@@ -116,25 +116,21 @@ __global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs
     }
     // copy the padded bin (with periodic wrap) into LDS; consecutive lanes read consecutive x
     const int P = p1 * p2 * p3;
-    for (int k = threadIdx.x; k < P; k += (kInterpSmBlock<T, DIM>)) {
-        const int s1 = k % p1;
-        const int rest = k / p1;
-        const int s2 = rest % p2;
-        const int s3 = rest / p2;
-        int g1 = origin[0] + s1, g2 = origin[1] + s2, g3 = (DIM == 3) ? origin[2] + s3 : 0;
-        while (g1 < 0) g1 += g.n[0];
-        while (g1 >= g.n[0]) g1 -= g.n[0];
-        while (g2 < 0) g2 += g.n[1];
-        while (g2 >= g.n[1]) g2 -= g.n[1];
-        if (DIM == 3) {
-            while (g3 < 0) g3 += g.n[2];
-            while (g3 >= g.n[2]) g3 -= g.n[2];
+    const int pd[3] = {p1, p2, p3};
+    auto copy = [&](auto fast) {
+        constexpr bool FAST = decltype(fast)::value;
+        CellWalk cw(threadIdx.x, kInterpSmBlock<T, DIM>, p1, p2);
+        for (int k = threadIdx.x; k < P; k += (kInterpSmBlock<T, DIM>), cw.next()) {
+            const int g1 = wrap_pad<FAST>(origin[0] + cw.s1, g.n[0]);
+            const int g2 = (DIM >= 2) ? wrap_pad<FAST>(origin[1] + cw.s2, g.n[1]) : 0;
+            const int g3 = (DIM == 3) ? wrap_pad<FAST>(origin[2] + cw.s3, g.n[2]) : 0;
+            tile[k] = grid[grid_index<FAST>(g1, g2, g3, g.n)];
         }
-        tile[k] = grid[(size_t)g1 + (size_t)g.n[0] * ((size_t)g2 + (size_t)g.n[1] * (size_t)g3)];
-    }
+    };
+    if (tile_fast(origin, pd, g.n, DIM)) copy(std::true_type{});
+    else copy(std::false_type{});
     __syncthreads();
     const T beta = (T)g.beta;
-    const int pd[3] = {p1, p2, p3};
     for (int i = threadIdx.x; i < len; i += (kInterpSmBlock<T, DIM>)) {
         const int64_t j = (int64_t)start + i;
         T xc[DIM];

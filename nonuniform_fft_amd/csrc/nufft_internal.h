@@ -40,6 +40,59 @@ __device__ __forceinline__ bool fold_t(double& t, int n, int& l) {
     return true;
 }
 
+// (s1, s2, s3) of cell index k = s1 + p1 (s2 + p2 s3), advanced by a fixed stride without division.
+struct CellWalk {
+    int s1, s2, s3, d1, d2, d3, p1, p2;
+    __device__ CellWalk(int k, int stride, int p1_, int p2_) : p1(p1_), p2(p2_) {
+        s1 = k % p1; int r = k / p1; s2 = r % p2; s3 = r / p2;
+        d1 = stride % p1; r = stride / p1; d2 = r % p2; d3 = r / p2;
+    }
+    __device__ void next() {
+        s1 += d1; int c = s1 >= p1; s1 -= c ? p1 : 0;
+        s2 += d2 + c; c = s2 >= p2; s2 -= c ? p2 : 0;
+        s3 += d3 + c;
+    }
+};
+
+// Periodic wrap of a padded-tile coordinate onto [0, n).  A padded bin can reach past the grid
+// end by up to m + w cells, which is more than one period on small grids, hence the loops.
+__device__ __forceinline__ int wrap_grid(int v, int n) {
+    while (v >= n) v -= n;
+    while (v < 0) v += n;
+    return v;
+}
+
+// The same wrap for v in [-n, 2n) without branches: of v - n, v and v + n, the one in [0, n) is
+// the smallest as an unsigned number (the others are negative or at least n).
+__device__ __forceinline__ int wrap_step(int v, int n) {
+    const unsigned a = (unsigned)v, b = (unsigned)(v - n), c = (unsigned)(v + n);
+    return (int)min(min(a, b), c);
+}
+
+template <bool FAST>
+__device__ __forceinline__ int wrap_pad(int v, int n) {
+    if constexpr (FAST) return wrap_step(v, n);
+    else return wrap_grid(v, n);
+}
+
+// Linear fine-grid index of cell (g1, g2, g3); FAST when the grid has fewer than 2^32 cells.
+template <bool FAST>
+__device__ __forceinline__ size_t grid_index(int g1, int g2, int g3, const int* n) {
+    if constexpr (FAST)
+        return (uint32_t)g1 + (uint32_t)n[0] * ((uint32_t)g2 + (uint32_t)n[1] * (uint32_t)g3);
+    else
+        return (size_t)g1 + (size_t)n[0] * ((size_t)g2 + (size_t)n[1] * (size_t)g3);
+}
+
+// Whether a padded tile can take the FAST forms above: origin[i] + s, s in [0, p[i]), stays in
+// [-n[i], 2 n[i]) along the first dim dimensions (every grid at least as large as the tile), and
+// the grid's cells are indexable in 32 bits.  The result is uniform over a workgroup.
+__device__ __forceinline__ bool tile_fast(const int* origin, const int* p, const int* n, int dim) {
+    bool ok = (uint64_t)n[0] * (uint64_t)(dim >= 2 ? n[1] : 1) * (uint64_t)(dim == 3 ? n[2] : 1) < (1ull << 32);
+    for (int i = 0; i < dim; ++i) ok = ok && origin[i] >= -n[i] && origin[i] + p[i] <= 2 * n[i];
+    return ok;
+}
+
 // ES kernel weights (cuFINUFFT paper eq. (5), rescaled as in eq. (8)) of a point with folded
 // scaled coordinate t along one dimension: the support is the W cells starting at
 // l0 = ceil(t - W/2); weight q has argument z = (l0 + q - t) * 2/W.  The offset l0 - t is

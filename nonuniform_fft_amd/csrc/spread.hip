@@ -52,28 +52,6 @@ __host__ __device__ inline int tile_row_pitch(int p1, int w) {
     return pc;
 }
 
-// (s1, s2, s3) of cell index k = s1 + p1 (s2 + p2 s3), advanced by a fixed stride without division.
-struct CellWalk {
-    int s1, s2, s3, d1, d2, d3, p1, p2;
-    __device__ CellWalk(int k, int stride, int p1_, int p2_) : p1(p1_), p2(p2_) {
-        s1 = k % p1; int r = k / p1; s2 = r % p2; s3 = r / p2;
-        d1 = stride % p1; r = stride / p1; d2 = r % p2; d3 = r / p2;
-    }
-    __device__ void next() {
-        s1 += d1; int c = s1 >= p1; s1 -= c ? p1 : 0;
-        s2 += d2 + c; c = s2 >= p2; s2 -= c ? p2 : 0;
-        s3 += d3 + c;
-    }
-};
-
-// Periodic wrap of a padded-tile coordinate onto [0, n).  A padded bin can reach past the grid
-// end by up to m + w cells, which is more than one period on small grids, hence the loops.
-__device__ __forceinline__ int wrap_grid(int v, int n) {
-    while (v >= n) v -= n;
-    while (v < 0) v += n;
-    return v;
-}
-
 template <typename T, int DIM, int W>
 __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c,
                                                             cplx<T>* __restrict__ grid, int p1, int p2,
@@ -194,18 +172,23 @@ __global__ void __launch_bounds__(kSpreadBlock) k_spread_sm(GeomArgs g, const cp
     __syncthreads();
     // flush the padded bin with periodic wrap (eq. (15)); consecutive lanes take consecutive x
     const int P = p1 * p2 * p3;
-    CellWalk cw(threadIdx.x, kSpreadBlock, p1, p2);
-    for (int k = threadIdx.x; k < P; k += kSpreadBlock, cw.next()) {
-        const int li = cw.s1 + cw.s2 * pc + cw.s3 * pp;
-        const double re = tre[li], im = tim[li];
-        if (re == 0.0 && im == 0.0) continue;
-        const int g1 = wrap_grid(origin[0] + cw.s1, g.n[0]);
-        const int g2 = wrap_grid(origin[1] + cw.s2, g.n[1]);
-        const int g3 = (DIM == 3) ? wrap_grid(origin[2] + cw.s3, g.n[2]) : 0;
-        const size_t gi = (size_t)g1 + (size_t)g.n[0] * ((size_t)g2 + (size_t)g.n[1] * (size_t)g3);
-        unsafeAtomicAdd(&grid[gi].re, (T)re);
-        unsafeAtomicAdd(&grid[gi].im, (T)im);
-    }
+    auto flush = [&](auto fast) {
+        constexpr bool FAST = decltype(fast)::value;
+        CellWalk cw(threadIdx.x, kSpreadBlock, p1, p2);
+        for (int k = threadIdx.x; k < P; k += kSpreadBlock, cw.next()) {
+            const int li = cw.s1 + cw.s2 * pc + cw.s3 * pp;
+            const double re = tre[li], im = tim[li];
+            if (re == 0.0 && im == 0.0) continue;
+            const int g1 = wrap_pad<FAST>(origin[0] + cw.s1, g.n[0]);
+            const int g2 = wrap_pad<FAST>(origin[1] + cw.s2, g.n[1]);
+            const int g3 = (DIM == 3) ? wrap_pad<FAST>(origin[2] + cw.s3, g.n[2]) : 0;
+            const size_t gi = grid_index<FAST>(g1, g2, g3, g.n);
+            unsafeAtomicAdd(&grid[gi].re, (T)re);
+            unsafeAtomicAdd(&grid[gi].im, (T)im);
+        }
+    };
+    if (tile_fast(origin, pd, g.n, DIM)) flush(std::true_type{});
+    else flush(std::false_type{});
 }
 
 // ------------------------------------------------------------------------------------------
@@ -305,6 +288,31 @@ struct ColPt {
         col_acc<W, Z, Z0>(are, aim, kz, cv.re * wxy, cv.im * wxy);
     }
 };
+
+// Adds a column kernel's padded bin (z fastest with pitch PZ, z extent pd[2]) to the fine grid
+// with periodic wrap (eq. (15)); consecutive lanes take consecutive x, then y, then z.
+template <typename T, int BLOCK, int PZ>
+__device__ __forceinline__ void flush_columns(const GeomArgs& g, const double* tre, const double* tim,
+                                              cplx<T>* grid, const int* origin, const int* pd, int p1, int p2) {
+    const int P = p1 * p2 * pd[2];
+    auto run = [&](auto fast) {
+        constexpr bool FAST = decltype(fast)::value;
+        CellWalk cw(threadIdx.x, BLOCK, p1, p2);
+        for (int k = threadIdx.x; k < P; k += BLOCK, cw.next()) {
+            const int li = (cw.s1 + cw.s2 * p1) * PZ + cw.s3;
+            const double re = tre[li], im = tim[li];
+            if (re == 0.0 && im == 0.0) continue;
+            const int g1 = wrap_pad<FAST>(origin[0] + cw.s1, g.n[0]);
+            const int g2 = wrap_pad<FAST>(origin[1] + cw.s2, g.n[1]);
+            const int g3 = wrap_pad<FAST>(origin[2] + cw.s3, g.n[2]);
+            const size_t gi = grid_index<FAST>(g1, g2, g3, g.n);
+            unsafeAtomicAdd(&grid[gi].re, (T)re);
+            unsafeAtomicAdd(&grid[gi].im, (T)im);
+        }
+    };
+    if (tile_fast(origin, pd, g.n, 3)) run(std::true_type{});
+    else run(std::false_type{});
+}
 
 template <typename T, int W>
 __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
@@ -486,19 +494,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
     }
     __syncthreads();
     // add the padded bin to the fine grid with periodic wrap (eq. (15))
-    const int P = p1 * p2 * Z;
-    CellWalk cw(threadIdx.x, BLOCK, p1, p2);
-    for (int k = threadIdx.x; k < P; k += BLOCK, cw.next()) {
-        const int li = (cw.s1 + cw.s2 * p1) * PZ + cw.s3;
-        const double re = tre[li], im = tim[li];
-        if (re == 0.0 && im == 0.0) continue;
-        const int g1 = wrap_grid(origin[0] + cw.s1, g.n[0]);
-        const int g2 = wrap_grid(origin[1] + cw.s2, g.n[1]);
-        const int g3 = wrap_grid(origin[2] + cw.s3, g.n[2]);
-        const size_t gi = (size_t)g1 + (size_t)g.n[0] * ((size_t)g2 + (size_t)g.n[1] * (size_t)g3);
-        unsafeAtomicAdd(&grid[gi].re, (T)re);
-        unsafeAtomicAdd(&grid[gi].im, (T)im);
-    }
+    flush_columns<T, BLOCK, PZ>(g, tre, tim, grid, origin, pd, p1, p2);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -727,19 +723,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
     }
     __syncthreads();
     // add the padded bin to the fine grid with periodic wrap (eq. (15))
-    const int P = p1 * p2 * Z;
-    CellWalk cw(threadIdx.x, BLOCK, p1, p2);
-    for (int k = threadIdx.x; k < P; k += BLOCK, cw.next()) {
-        const int li = (cw.s1 + cw.s2 * p1) * PZ + cw.s3;
-        const double re = tre[li], im = tim[li];
-        if (re == 0.0 && im == 0.0) continue;
-        const int g1 = wrap_grid(origin[0] + cw.s1, g.n[0]);
-        const int g2 = wrap_grid(origin[1] + cw.s2, g.n[1]);
-        const int g3 = wrap_grid(origin[2] + cw.s3, g.n[2]);
-        const size_t gi = (size_t)g1 + (size_t)g.n[0] * ((size_t)g2 + (size_t)g.n[1] * (size_t)g3);
-        unsafeAtomicAdd(&grid[gi].re, (T)re);
-        unsafeAtomicAdd(&grid[gi].im, (T)im);
-    }
+    flush_columns<T, BLOCK, PZ>(g, tre, tim, grid, origin, pd, p1, p2);
 }
 
 // fp64 plans stage per workgroup; fp32 plans per wavefront
@@ -856,13 +840,18 @@ __global__ void __launch_bounds__(kSpread1Block) k_spread_sm1(GeomArgs g, const 
         }
     }
     __syncthreads();
-    for (int k = threadIdx.x; k < p1; k += kSpread1Block) {
-        const double re = tre[k], im = tim[k];
-        if (re == 0.0 && im == 0.0) continue;
-        const int gi = wrap_grid(origin + k, g.n[0]);
-        unsafeAtomicAdd(&grid[gi].re, (T)re);
-        unsafeAtomicAdd(&grid[gi].im, (T)im);
-    }
+    auto flush = [&](auto fast) {
+        constexpr bool FAST = decltype(fast)::value;
+        for (int k = threadIdx.x; k < p1; k += kSpread1Block) {
+            const double re = tre[k], im = tim[k];
+            if (re == 0.0 && im == 0.0) continue;
+            const int gi = wrap_pad<FAST>(origin + k, g.n[0]);
+            unsafeAtomicAdd(&grid[gi].re, (T)re);
+            unsafeAtomicAdd(&grid[gi].im, (T)im);
+        }
+    };
+    if (tile_fast(&origin, &p1, g.n, 1)) flush(std::true_type{});
+    else flush(std::false_type{});
 }
 
 template <typename T, int DIM, int W>
