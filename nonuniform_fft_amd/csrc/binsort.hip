@@ -21,6 +21,8 @@ namespace {
 constexpr int kBlock = 256;                 // threads per workgroup (4 wavefronts)
 constexpr int kItems = 16;                  // keys per thread per sort tile
 constexpr int kTile = kBlock * kItems;      // keys per sort tile
+constexpr int kScatBlock = 512;            // threads per scatter workgroup (8 wavefronts)
+constexpr int kScatItems = kTile / kScatBlock;  // keys per thread in the scatter
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kScanItems = 8;               // elements per thread in the scan
@@ -237,7 +239,7 @@ struct Payload {
 // written to consecutive addresses.
 // IDV: the values are the keys' positions (the first pass), so none are read.
 template <typename T, int NP, bool IDV>
-__global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restrict__ keys_in,
+__global__ void __launch_bounds__(kScatBlock) k_radix_scatter(const int32_t* __restrict__ keys_in,
                                                            const int32_t* __restrict__ vals_in,
                                                            int32_t* __restrict__ keys_out,
                                                            int32_t* __restrict__ vals_out,
@@ -245,8 +247,8 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
                                                            const int32_t* __restrict__ offs,
                                                            Payload<T, NP> pl) {
     const int mask = (1 << bits) - 1;
-    constexpr int kWaves = kBlock / 64;
-    constexpr int kChunk = kItems * 64;                  // keys per wavefront
+    constexpr int kWaves = kScatBlock / 64;
+    constexpr int kChunk = kScatItems * 64;              // keys per wavefront
     __shared__ int32_t cnt[kWaves][kRadix];             // per-wavefront digit counts, then offsets
     __shared__ int32_t gbase[kRadix];                   // global start of each digit's run of this tile
     __shared__ int32_t tbase[kRadix];                   // start of each digit's run inside the tile
@@ -259,10 +261,10 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
     const int count = (int)min<int64_t>(kTile, M - base);
 
     // load this wavefront's chunk (coalesced per round)
-    int32_t keys[kItems], vals[kItems];
-    T cvs[kItems][NP > 0 ? NP : 1];
+    int32_t keys[kScatItems], vals[kScatItems];
+    T cvs[kScatItems][NP > 0 ? NP : 1];
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < kScatItems; ++r) {
         const int li = wv * kChunk + r * 64 + lane;
         const bool valid = li < count;
         keys[r] = valid ? keys_in[base + li] : 0;
@@ -277,9 +279,9 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
 
     // rank inside the wavefront's chunk: rounds in order, lanes in order
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int32_t rank[kItems];
+    int32_t rank[kScatItems];
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < kScatItems; ++r) {
         const bool valid = wv * kChunk + r * 64 + lane < count;
         const int digit = (keys[r] >> shift) & mask;
         uint64_t peers = __ballot(valid);
@@ -298,13 +300,16 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
     }
     __syncthreads();
 
-    // tile offsets: digit-major exclusive scan of the tile counts, then per-wavefront offsets
+    // tile offsets: digit-major exclusive scan of the tile counts (one thread per digit, the
+    // first kRadix threads), then per-wavefront offsets
     {
-        const int d = tid;                                // kBlock == kRadix
+        static_assert(kRadix % 64 == 0 && kRadix <= kScatBlock, "one thread per digit");
+        const int d = tid;
+        const bool dt = tid < kRadix;
         int32_t c[kWaves], tot = 0;
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) {
-            c[i] = cnt[i][d];
+            c[i] = dt ? cnt[i][d] : 0;
             tot += c[i];
         }
         int32_t inc = tot;
@@ -313,23 +318,25 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
             const int32_t u = __shfl_up(inc, off, 64);
             if (lane >= off) inc += u;
         }
-        if (lane == 63) wsum[wv] = inc;
+        if (dt && lane == 63) wsum[wv] = inc;
         __syncthreads();
-        int32_t run = inc - tot;
-        for (int i = 0; i < wv; ++i) run += wsum[i];
-        tbase[d] = run;
-        gbase[d] = (d <= mask) ? offs[(int64_t)d * ntiles + tile] : 0;
+        if (dt) {
+            int32_t run = inc - tot;
+            for (int i = 0; i < wv; ++i) run += wsum[i];
+            tbase[d] = run;
+            gbase[d] = (d <= mask) ? offs[(int64_t)d * ntiles + tile] : 0;
 #pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-            cnt[i][d] = run;
-            run += c[i];
+            for (int i = 0; i < kWaves; ++i) {
+                cnt[i][d] = run;
+                run += c[i];
+            }
         }
     }
     __syncthreads();
     // slot of each item in the digit-ordered tile (-1: past the end of the input)
-    int pos[kItems];
+    int pos[kScatItems];
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < kScatItems; ++r) {
         pos[r] = -1;
         if (wv * kChunk + r * 64 + lane < count) {
             const int digit = (keys[r] >> shift) & mask;
@@ -341,10 +348,10 @@ __global__ void __launch_bounds__(kBlock) k_radix_scatter(const int32_t* __restr
     // slot i goes to gbase[digit] + (i - tbase[digit])
     auto emit = [&](auto get, auto put) {
 #pragma unroll
-        for (int r = 0; r < kItems; ++r)
+        for (int r = 0; r < kScatItems; ++r)
             if (pos[r] >= 0) get(r, pos[r]);
         __syncthreads();
-        for (int i = tid; i < count; i += kBlock) {
+        for (int i = tid; i < count; i += kScatBlock) {
             const int digit = sdig[i];
             put((int64_t)gbase[digit] + (i - tbase[digit]), i);
         }
@@ -450,8 +457,8 @@ hipError_t scatter_dim(int dim, const int32_t* ki, const int32_t* vi, int32_t* k
         Payload<T, D> pl{};
         for (int d = 0; d < D; ++d) { pl.in[d] = (const T*)cin[d]; pl.out[d] = (T*)cout[d]; }
         const dim3 gt((unsigned)ntiles);
-        if (vi) k_radix_scatter<T, D, false><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, pl);
-        else k_radix_scatter<T, D, true><<<gt, kBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, pl);
+        if (vi) k_radix_scatter<T, D, false><<<gt, kScatBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, pl);
+        else k_radix_scatter<T, D, true><<<gt, kScatBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, pl);
     };
     if (dim == 1) go(std::integral_constant<int, 1>{});
     else if (dim == 2) go(std::integral_constant<int, 2>{});
