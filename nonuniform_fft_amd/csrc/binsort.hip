@@ -21,7 +21,7 @@ namespace {
 constexpr int kBlock = 256;                 // threads per workgroup (4 wavefronts)
 constexpr int kItems = 16;                  // keys per thread per sort tile
 constexpr int kTile = kBlock * kItems;      // keys per sort tile
-constexpr int kScatBlock = 512;            // threads per scatter workgroup (8 wavefronts)
+constexpr int kScatBlock = 1024;           // threads per scatter workgroup (16 wavefronts)
 constexpr int kScatItems = kTile / kScatBlock;  // keys per thread in the scatter
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
