@@ -138,6 +138,12 @@ STEP_CASES = [
     Workload("st", 1, (1000,), 50_001, 1e-5, "f32", seed=37),
     Workload("st", 1, (777,), 30_000, 1e-12, "f64", seed=38),
     Workload("st", 1, (4096,), 40_000, 1e-6, "f32", dist="box", seed=39),
+    # fine grids smaller than one padded bin, which then wraps onto the grid more than once
+    Workload("st", 3, (3, 4, 2), 2_000, 1e-5, "f32", seed=131),
+    Workload("st", 3, (4, 3, 5), 2_000, 1e-2, "f32", seed=132),
+    Workload("st", 3, (4, 4, 4), 1_000, 1e-9, "f64", seed=133),
+    Workload("st", 2, (5, 7), 2_000, 1e-12, "f64", seed=134),
+    Workload("st", 1, (5,), 2_000, 1e-6, "f32", seed=135),
 ]
 
 
