@@ -93,6 +93,33 @@ __device__ __forceinline__ bool tile_fast(const int* origin, const int* p, const
     return ok;
 }
 
+// e^x in fp64 for x in [-64, 0], the range of the ES kernel's exponent beta (sqrt(1 - z^2) - 1).
+// Cody-Waite reduction x = k ln2 + r, |r| <= ln2 / 2, with ln2 split into LN2_HI (its first 32
+// significant bits, so k LN2_HI is exact) and LN2_LO = ln2 - LN2_HI; e^r from its Taylor series
+// to degree 12 (truncation error below 2.3e-16 relative on that interval); then scaled by 2^k.
+// No special cases: the argument range rules out overflow, underflow and NaN.
+__device__ __forceinline__ double exp_es(double x) {
+    constexpr double kLog2e = 1.4426950408889634;              // 1 / ln2
+    constexpr double kLn2Hi = 0x1.62e42fee00000p-1;
+    constexpr double kLn2Lo = 0x1.a39ef35793c76p-33;
+    const double k = rint(x * kLog2e);
+    const double r = __fma_rn(-k, kLn2Lo, __fma_rn(-k, kLn2Hi, x));
+    double p = 1.0 / 479001600.0;                                // 1/12!
+    p = __fma_rn(p, r, 1.0 / 39916800.0);
+    p = __fma_rn(p, r, 1.0 / 3628800.0);
+    p = __fma_rn(p, r, 1.0 / 362880.0);
+    p = __fma_rn(p, r, 1.0 / 40320.0);
+    p = __fma_rn(p, r, 1.0 / 5040.0);
+    p = __fma_rn(p, r, 1.0 / 720.0);
+    p = __fma_rn(p, r, 1.0 / 120.0);
+    p = __fma_rn(p, r, 1.0 / 24.0);
+    p = __fma_rn(p, r, 1.0 / 6.0);
+    p = __fma_rn(p, r, 0.5);
+    p = __fma_rn(p, r, 1.0);
+    p = __fma_rn(p, r, 1.0);
+    return ldexp(p, (int)k);
+}
+
 // ES kernel weights (cuFINUFFT paper eq. (5), rescaled as in eq. (8)) of a point with folded
 // scaled coordinate t along one dimension: the support is the W cells starting at
 // l0 = ceil(t - W/2); weight q has argument z = (l0 + q - t) * 2/W.  The offset l0 - t is
@@ -111,7 +138,7 @@ __device__ __forceinline__ int es_weights(double t, T beta, T* phi) {
         if constexpr (sizeof(T) == 4)
             phi[q] = (zz <= 1.0f) ? __expf(beta * (__builtin_amdgcn_sqrtf(1.0f - zz) - 1.0f)) : 0.0f;
         else
-            phi[q] = (zz <= (T)1) ? exp(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
+            phi[q] = (zz <= (T)1) ? exp_es(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
     }
     return (int)l0d;
 }

@@ -621,7 +621,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
             if constexpr (sizeof(T) == 4)
                 phi = (zz <= 1.0f) ? __expf(beta * (__builtin_amdgcn_sqrtf(1.0f - zz) - 1.0f)) : 0.0f;
             else
-                phi = (zz <= (T)1) ? exp(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
+                phi = (zz <= (T)1) ? exp_es(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
             int l0 = (int)l0d - origin[d_];
             l0 = min(max(l0, 0), pd[d_] - W);
             if (d_ < 2) {
