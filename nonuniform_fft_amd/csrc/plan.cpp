@@ -194,16 +194,23 @@ void default_bins(nufft_plan p, int* m) {
             }
         }
     } else {
-        // the column-run kernel first (it needs m3 = 8), then the plain SM tile
+        // the column-run kernel first (it needs m3 = 8), then the plain SM tile.  fp32 SM point-patch
+        // plans first look for a tile small enough for two workgroups per CU: at N = 128^3,
+        // M = 2^24 that took 16 x 8 x 8 over 16 x 16 x 8 at w = 3 and 4 (spread 1.29 -> 0.96 ms
+        // and 1.50 -> 1.15 ms); w = 2 keeps 16 x 16 x 8, which already fits twice, and fp64 plans
+        // keep the largest tile (w = 4: 2 % slower with 16 x 8 x 8).
         const bool col = nufft::spread_uses_columns(3, p->w) && p->method == NUFFT_METHOD_SM;
-        for (int pass = col ? 0 : 1; pass < 2; ++pass) {
+        const size_t full = nufft::spread_lds_limit();
+        for (int pass = col ? 0 : 1; pass < 3; ++pass) {
+            if (pass == 1 && (p->prec != 0 || p->method != NUFFT_METHOD_SM)) continue;
+            const size_t limit = (pass == 1) ? full / 2 : full;
             for (auto& c : c3) {
-                if (pass == 1 && c[0] > 16) continue;   // the point-patch kernel keeps 16 x 16 x 8
+                if (pass >= 1 && c[0] > 16) continue;   // the point-patch kernel keeps at most 16 x 16 x 8
                 int mm[3] = {c[0], c[1], c[2]};
                 // the column kernel's fp64 bin (z pitch >= depth) also covers the interpolation tile
                 const size_t need = (pass == 0) ? nufft::spread_col_lds_bytes(p->prec, p->w, mm)
                                                 : nufft::spread_tile_bytes(p->prec, 3, p->w, mm);
-                if (need > 0 && need <= nufft::spread_lds_limit()) {
+                if (need > 0 && need <= limit) {
                     m[0] = c[0];
                     m[1] = c[1];
                     m[2] = c[2];
