@@ -314,11 +314,12 @@ int batch_buffers(nufft_plan plan, int nv, void** grid, void** cscratch) {
     const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan);
     int rc;
     if ((rc = dev_alloc(plan, plan->grid_many, gbytes * nv, "many-vector fine grids")) != NUFFT_OK) return rc;
-    if (plan->prec == 1 && plan->M > 0 &&
+    // (1D fp64 spreading reads the strengths through the permutation and needs no gather scratch)
+    if (plan->prec == 1 && plan->dim >= 2 && plan->M > 0 &&
         (rc = dev_alloc(plan, plan->c_many, (size_t)plan->M * 16 * nv, "many-vector strengths")) != NUFFT_OK)
         return rc;
     *grid = plan->grid_many.p;
-    *cscratch = plan->prec == 1 ? plan->c_many.p : plan->sort_tmp.p;
+    *cscratch = (plan->prec == 1 && plan->dim >= 2) ? plan->c_many.p : plan->sort_tmp.p;
     return NUFFT_OK;
 }
 

@@ -1028,14 +1028,16 @@ size_t spread_col_lds_bytes(int prec, int w, const int* m) {
 
 hipError_t launch_spread(int prec, int method, const GeomArgs& g_in, const void* c_in, void* grid,
                          hipStream_t st, bool columns, void* c_scratch) {
-    // fp64 plans put the strengths in sorted order first, with a streaming gather: their
-    // spreading kernels run two wavefronts per SIMD and cannot hide the dependent perm -> c
-    // loads of large point sets (fp32 plans hide them, and the extra pass would cost more)
+    // fp64 plans in 2D and 3D put the strengths in sorted order first, with a streaming gather:
+    // their spreading kernels run two wavefronts per SIMD and cannot hide the dependent
+    // perm -> c loads of large point sets.  fp32 plans and the 1D kernel (one lane per point,
+    // its next point requested one iteration ahead) hide them, and the extra pass would cost
+    // more (1D fp64, N = 2^20, M = 2^24: spread 0.65 ms with the pass, 0.39 ms without).
     GeomArgs g = g_in;
     const void* c = c_in;
     if (method == NUFFT_METHOD_GM) {
         g.cperm = nullptr;   // the points are in the caller's order
-    } else if (prec == 1 && g.M > 0) {
+    } else if (prec == 1 && g.M > 0 && g.dim >= 2) {
         k_gather_c<<<dim3((unsigned)((g.M + 255) / 256), (unsigned)g.nv), 256, 0, st>>>(g.perm, (const cplx<double>*)c_in,
                                                                    (cplx<double>*)c_scratch, g.M);
         hipError_t e = hipGetLastError();
