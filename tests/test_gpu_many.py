@@ -33,6 +33,7 @@ def orc():
 
 CASES = [
     Workload("mv", 1, (1000,), 30_001, 1e-6, "f32", seed=81),
+    Workload("mv", 1, (777,), 20_000, 1e-12, "f64", seed=87),          # 1D fp64: strengths via perm
     Workload("mv", 2, (48, 40), 20_000, 1e-12, "f64", seed=82),
     Workload("mv", 3, (24, 20, 18), 30_000, 1e-5, "f32", seed=83),      # column-run spreading
     Workload("mv", 3, (20, 16, 12), 10_000, 1e-9, "f64", seed=84),      # fp64 column runs + gather
