@@ -6,13 +6,14 @@
 //
 // gfx950 design: the permutation is a least-significant-digit radix sort on the bin key, at
 // most 8 bits per pass, the key's bits spread evenly over the passes (fewer digits per pass
-// give longer runs per digit in the scatter, so fuller memory transactions).  Each pass is (1) a per-workgroup digit histogram in LDS (integer LDS
-// atomics), (2) an exclusive scan over digit-major histograms, (3) a stable scatter that ranks
-// equal digits inside a wavefront with 64-bit ballots and across the four wavefronts of a
-// workgroup through LDS counters, then reorders the tile by digit one array at a time through
-// a single LDS buffer (so several workgroups fit per CU) and writes each digit's run to
-// consecutive addresses, with neighbouring tiles kept on one XCD.  Every pass is stable, so points keep their original order
-// inside a bin and the permutation is deterministic.
+// give longer runs per digit in the scatter, so fuller memory transactions).  Each pass is
+// (1) a per-workgroup digit histogram in LDS (integer LDS atomics), (2) an exclusive scan over
+// digit-major histograms, (3) a stable scatter that ranks equal digits inside a wavefront with
+// 64-bit ballots and across the sixteen wavefronts of a workgroup through LDS counters, then
+// reorders the tile by digit one array at a time through a single LDS buffer (so two
+// workgroups fit per CU) and writes each digit's run to consecutive addresses, with
+// neighbouring tiles kept on one XCD.  Every pass is stable, so points keep their original
+// order inside a bin and the permutation is deterministic.
 #include "nufft_internal.h"
 
 namespace nufft {
@@ -232,9 +233,9 @@ struct Payload {
 // travel with the keys, so the last pass leaves the coordinates in sorted order without a
 // random gather (the first pass reads them in the caller's order, coalesced).
 //
-// Each wavefront ranks its own contiguous chunk of the tile (kItems rounds of 64 keys) with
+// Each wavefront ranks its own contiguous chunk of the tile (kScatItems rounds of 64 keys) with
 // ballots and wavefront-private digit counters, so ranking needs no workgroup barrier; the
-// per-digit counts of the four chunks are then combined into tile offsets, and keys, values
+// per-digit counts of the chunks are then combined into tile offsets, and keys, values
 // and coordinates are reordered by digit through one LDS buffer in turn, each digit's run
 // written to consecutive addresses.
 // IDV: the values are the keys' positions (the first pass), so none are read.
