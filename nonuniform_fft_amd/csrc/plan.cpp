@@ -194,15 +194,15 @@ void default_bins(nufft_plan p, int* m) {
             }
         }
     } else {
-        // the column-run kernel first (it needs m3 = 8), then the plain SM tile.  fp32 SM point-patch
+        // the column-run kernel first (it needs m3 = 8), then the plain SM tile.  SM point-patch
         // plans first look for a tile small enough for two workgroups per CU: at N = 128^3,
-        // M = 2^24 that took 16 x 8 x 8 over 16 x 16 x 8 at w = 3 and 4 (spread 1.29 -> 0.96 ms
-        // and 1.50 -> 1.15 ms); w = 2 keeps 16 x 16 x 8, which already fits twice, and fp64 plans
-        // keep the largest tile (w = 4: 2 % slower with 16 x 8 x 8).
+        // M = 2^24 that took 16 x 8 x 8 over 16 x 16 x 8 at w = 3 and 4 (fp32 spread 1.29 -> 0.96
+        // ms and 1.50 -> 1.15 ms; fp64, with its two-workgroup build, 1.94 -> 1.72 ms and
+        // 2.26 -> 2.13 ms); w = 2 keeps 16 x 16 x 8, which already fits twice.
         const bool col = nufft::spread_uses_columns(3, p->w) && p->method == NUFFT_METHOD_SM;
         const size_t full = nufft::spread_lds_limit();
         for (int pass = col ? 0 : 1; pass < 3; ++pass) {
-            if (pass == 1 && (p->prec != 0 || p->method != NUFFT_METHOD_SM)) continue;
+            if (pass == 1 && p->method != NUFFT_METHOD_SM) continue;
             const size_t limit = (pass == 1) ? full / 2 : full;
             for (auto& c : c3) {
                 if (pass >= 1 && c[0] > 16) continue;   // the point-patch kernel keeps at most 16 x 16 x 8
