@@ -184,6 +184,7 @@ struct nufft_plan_s {
 
     // plan-owned device memory
     nufft::DevBuf grid;                 // fine grid, n^d complex
+    nufft::DevBuf grid2;                // the FFT's output grid (out-of-place transforms)
     nufft::DevBuf pcorr;                // correction factors p_1 | p_2 | p_3 in precision T
     nufft::DevBuf fft_work;
 
@@ -216,6 +217,7 @@ struct nufft_plan_s {
 
     // many-vector batches: nv fine grids, and (fp64) the strengths gathered in sorted order
     nufft::DevBuf grid_many;
+    nufft::DevBuf grid_many2;
     nufft::DevBuf c_many;
 
     // rocFFT

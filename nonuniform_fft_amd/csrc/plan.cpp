@@ -251,16 +251,18 @@ void record(nufft_plan p, int i) {
     if (p->opts.timing && p->ev_ok) (void)hipEventRecord(p->ev[i], p->stream);
 }
 
-int fft_exec(nufft_plan plan, rocfft_plan fp, void* data) {
-    void* in[1] = {data};
-    rocfft_status s = rocfft_execute(fp, in, nullptr, plan->fft_info);
+int fft_exec(nufft_plan plan, rocfft_plan fp, void* src, void* dst) {
+    void* in[1] = {src};
+    void* out[1] = {dst};
+    rocfft_status s = rocfft_execute(fp, in, out, plan->fft_info);
     if (s != rocfft_status_success) return fail(plan, NUFFT_ERR_FFT, "rocfft_execute failed");
     return NUFFT_OK;
 }
 
-// rocFFT plan for one direction (forward for type 1, backward for type 2), in place,
-// unnormalised, over nv contiguous fine grids; the work buffer is shared by all plans and
-// grown when needed.
+// rocFFT plan for one direction (forward for type 1, backward for type 2), unnormalised, over
+// nv contiguous fine grids, out of place into a second grid buffer (the input grid is scratch;
+// 256^3 fp32: 0.164 ms against 0.193 in place, 512^3 fp64: 3.38 against 3.83 ms); the work
+// buffer is shared by all plans and grown when needed.
 int make_fft_plan(nufft_plan plan, int direction, int nv = 1) {
     rocfft_plan& slot = (nv == 1) ? ((direction == 1) ? plan->fft_fwd : plan->fft_bwd)
                                   : plan->fft_many[direction - 1];
@@ -276,7 +278,7 @@ int make_fft_plan(nufft_plan plan, int direction, int nv = 1) {
     rocfft_transform_type tt = (direction == 1) ? rocfft_transform_type_complex_forward
                                                 : rocfft_transform_type_complex_inverse;
     rocfft_plan fp = nullptr;
-    if (rocfft_plan_create(&fp, rocfft_placement_inplace, tt, fprec, (size_t)plan->dim, lengths, (size_t)nv,
+    if (rocfft_plan_create(&fp, rocfft_placement_notinplace, tt, fprec, (size_t)plan->dim, lengths, (size_t)nv,
                            nullptr) != rocfft_status_success)
         return fail(plan, NUFFT_ERR_FFT, "rocfft_plan_create failed");
     slot = fp;
@@ -303,22 +305,26 @@ int make_fft_plan(nufft_plan plan, int direction, int nv = 1) {
 // [8..11] the type 2 steps (pad, FFT, interp), [5..6] the sort.
 enum { EV_T1 = 0, EV_SORT0 = 5, EV_SORT1 = 6, EV_T2 = 8 };
 
-// Fine grids (and fp64 gather scratch) for one batch of nv vectors: the plan's own buffers for
-// nv = 1, the many-vector buffers otherwise.
-int batch_buffers(nufft_plan plan, int nv, void** grid, void** cscratch) {
+// Fine grids (spreading / FFT input and FFT output) and fp64 gather scratch for one batch of nv
+// vectors: the plan's own buffers for nv = 1, the many-vector buffers otherwise.
+int batch_buffers(nufft_plan plan, int nv, void** grid, void** grid2, void** cscratch) {
+    const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan);
+    int rc;
     if (nv == 1) {
+        if ((rc = dev_alloc(plan, plan->grid2, gbytes, "FFT output grid")) != NUFFT_OK) return rc;
         *grid = plan->grid.p;
+        *grid2 = plan->grid2.p;
         *cscratch = plan->sort_tmp.p;
         return NUFFT_OK;
     }
-    const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan);
-    int rc;
     if ((rc = dev_alloc(plan, plan->grid_many, gbytes * nv, "many-vector fine grids")) != NUFFT_OK) return rc;
+    if ((rc = dev_alloc(plan, plan->grid_many2, gbytes * nv, "many-vector FFT output grids")) != NUFFT_OK) return rc;
     // (1D fp64 spreading reads the strengths through the permutation and needs no gather scratch)
     if (plan->prec == 1 && plan->dim >= 2 && plan->M > 0 &&
         (rc = dev_alloc(plan, plan->c_many, (size_t)plan->M * 16 * nv, "many-vector strengths")) != NUFFT_OK)
         return rc;
     *grid = plan->grid_many.p;
+    *grid2 = plan->grid_many2.p;
     *cscratch = (plan->prec == 1 && plan->dim >= 2) ? plan->c_many.p : plan->sort_tmp.p;
     return NUFFT_OK;
 }
@@ -327,8 +333,8 @@ int batch_buffers(nufft_plan plan, int nv, void** grid, void** cscratch) {
 int run_type1(nufft_plan plan, const void* c, void* f, int nv = 1) {
     int rc;
     if ((rc = make_fft_plan(plan, 1, nv)) != NUFFT_OK) return rc;
-    void *grid, *cs;
-    if ((rc = batch_buffers(plan, nv, &grid, &cs)) != NUFFT_OK) return rc;
+    void *grid, *grid2, *cs;
+    if ((rc = batch_buffers(plan, nv, &grid, &grid2, &cs)) != NUFFT_OK) return rc;
     nufft::GeomArgs g = geom(plan);
     g.nv = nv;
     const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan) * nv;
@@ -337,9 +343,9 @@ int run_type1(nufft_plan plan, const void* c, void* f, int nv = 1) {
     record(plan, EV_T1 + 1);
     NUFFT_HIP(nufft::launch_spread(plan->prec, plan->method, g, c, grid, plan->stream, plan->colw > 0, cs));
     record(plan, EV_T1 + 2);
-    if ((rc = fft_exec(plan, nv == 1 ? plan->fft_fwd : plan->fft_many[0], grid)) != NUFFT_OK) return rc;
+    if ((rc = fft_exec(plan, nv == 1 ? plan->fft_fwd : plan->fft_many[0], grid, grid2)) != NUFFT_OK) return rc;
     record(plan, EV_T1 + 3);
-    NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, grid, f,
+    NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, grid2, f,
                                        plan->stream, nv));
     record(plan, EV_T1 + 4);
     plan->stage_recorded |= 1;
@@ -350,17 +356,17 @@ int run_type1(nufft_plan plan, const void* c, void* f, int nv = 1) {
 int run_type2(nufft_plan plan, void* c, const void* f, int nv = 1) {
     int rc;
     if ((rc = make_fft_plan(plan, 2, nv)) != NUFFT_OK) return rc;
-    void *grid, *cs;
-    if ((rc = batch_buffers(plan, nv, &grid, &cs)) != NUFFT_OK) return rc;
+    void *grid, *grid2, *cs;
+    if ((rc = batch_buffers(plan, nv, &grid, &grid2, &cs)) != NUFFT_OK) return rc;
     nufft::GeomArgs g = geom(plan);
     g.nv = nv;
     record(plan, EV_T2 + 0);
     NUFFT_HIP(nufft::launch_precorrect_pad(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, f, grid,
                                            plan->stream, nv));
     record(plan, EV_T2 + 1);
-    if ((rc = fft_exec(plan, nv == 1 ? plan->fft_bwd : plan->fft_many[1], grid)) != NUFFT_OK) return rc;
+    if ((rc = fft_exec(plan, nv == 1 ? plan->fft_bwd : plan->fft_many[1], grid, grid2)) != NUFFT_OK) return rc;
     record(plan, EV_T2 + 2);
-    NUFFT_HIP(nufft::launch_interp(plan->prec, plan->method, g, grid, c, plan->stream));
+    NUFFT_HIP(nufft::launch_interp(plan->prec, plan->method, g, grid2, c, plan->stream));
     record(plan, EV_T2 + 3);
     plan->stage_recorded |= 2;
     return NUFFT_OK;
@@ -372,7 +378,7 @@ int run_many(nufft_plan plan, int type, int nvec, void* c, void* f) {
     const size_t fbytes = (size_t)mode_count(plan) * 2 * real_size(plan);
     int b = plan->opts.max_batch > 0 ? plan->opts.max_batch : 16;
     if (plan->opts.max_batch <= 0) {
-        const size_t per = (size_t)grid_cells(plan) * 2 * real_size(plan) + (plan->prec == 1 ? cbytes : 0);
+        const size_t per = (size_t)grid_cells(plan) * 4 * real_size(plan) + (plan->prec == 1 ? cbytes : 0);
         while (b > 1 && (size_t)b * per > (size_t(2) << 30)) --b;
     }
     for (int v0 = 0; v0 < nvec; v0 += b) {
@@ -449,7 +455,7 @@ int nufft_destroy(nufft_plan plan) {
     if (plan->fft_info) rocfft_execution_info_destroy(plan->fft_info);
     if (plan->t3_spread) nufft_destroy(plan->t3_spread);
     if (plan->t3_eval) nufft_destroy(plan->t3_eval);
-    for (DevBuf* b : {&plan->grid, &plan->pcorr, &plan->fft_work, &plan->xs, &plan->perm, &plan->counts,
+    for (DevBuf* b : {&plan->grid, &plan->grid2, &plan->grid_many2, &plan->pcorr, &plan->fft_work, &plan->xs, &plan->perm, &plan->counts,
                       &plan->offsets, &plan->sub, &plan->sort_tmp, &plan->grid_many, &plan->c_many, &plan->t3_part,
                       &plan->t3_y, &plan->t3_theta, &plan->t3_pre, &plan->t3_post, &plan->t3_cp, &plan->t3_cin,
                       &plan->t3_tab})
