@@ -143,7 +143,8 @@ int nufft_setpts_type3(nufft_plan plan, int64_t M, const void* x, const void* y,
  *   type 1: reads c (M complex), writes f (prod N complex).
  *   type 2: reads f, writes c.
  *   type 3: reads c (M complex), writes f (K complex).
- * Asynchronous on the plan's stream.  NUFFT_ERR_BAD_STATE before a successful setpts.
+ * Asynchronous on the plan's stream.  NUFFT_ERR_BAD_STATE before a successful setpts.  The
+ * first call allocates a second fine grid, the output of the out-of-place FFT.
  */
 int nufft_execute(nufft_plan plan, void* c, void* f);
 
@@ -163,7 +164,8 @@ int nufft_execute_adjoint(nufft_plan plan, void* c, void* f);
  * values, f nvec*prod(N), both vector-major).  Vectors run in batches: every step of a batch is
  * one launch over all its vectors (blockIdx.y = vector) into a batch of fine grids, and the FFT
  * is one batched rocFFT call.  The batch size is opts.max_batch, or automatic (at most 16
- * vectors and about 2 GiB of batch grids); batch grids are plan-owned and kept for later calls.
+ * vectors and about 2 GiB of batch grids, two per vector); batch grids are plan-owned and kept
+ * for later calls.
  * Per-stage times (opts.timing) cover the last batch.  Errors as nufft_execute, plus
  * NUFFT_ERR_BAD_ARG for nvec < 1.
  */
