@@ -166,7 +166,7 @@ int nufft_execute_adjoint(nufft_plan plan, void* c, void* f);
  * is one batched rocFFT call.  The batch size is opts.max_batch, or automatic (at most 16
  * vectors and about 2 GiB of batch grids, two per vector); batch grids are plan-owned and kept
  * for later calls.
- * Per-stage times (opts.timing) cover the last batch.  Errors as nufft_execute, plus
+ * Per-stage times (opts.timing) count each batch as one call.  Errors as nufft_execute, plus
  * NUFFT_ERR_BAD_ARG for nvec < 1.
  */
 int nufft_execute_many(nufft_plan plan, int nvec, void* c, void* f);
@@ -200,11 +200,14 @@ int nufft_get_info(nufft_plan plan, int64_t* info_i, double* info_d);
 
 /*
  * Per-step times (ms) when opts.timing = 1, written to ms[0..7] in host memory:
- *   ms[0] sort (last setpts),
+ *   ms[0] sort (setpts),
  *   ms[1] spread, ms[2] type 1 FFT, ms[3] deconvolve + truncate, ms[4] grid clear
- *         (last type 1 execution),
- *   ms[5] interp, ms[6] type 2 FFT, ms[7] precorrect + pad (last type 2 execution).
- * A direction never executed reports zeros.  Synchronises the plan's stream.
+ *         (type 1 executions),
+ *   ms[5] interp, ms[6] type 2 FFT, ms[7] precorrect + pad (type 2 executions).
+ * Each is the average over the calls recorded since the previous nufft_get_stage_times (the
+ * last 16 when there were more; each batch of a many-vector call counts as one); a stage not
+ * run since then keeps its previous value, zero if never run.  The plan records events on its
+ * stream and never waits for them except here: this call synchronises the plan's stream.
  */
 int nufft_get_stage_times(nufft_plan plan, double* ms);
 

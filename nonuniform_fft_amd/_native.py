@@ -322,7 +322,8 @@ class Plan:
 
     def stage_times(self):
         """ms per step (needs timing=True): sort, spread, type-1 FFT, deconvolve, clear,
-        interp, type-2 FFT, precorrect+pad (zeros for a direction not run)."""
+        interp, type-2 FFT, precorrect+pad, each averaged over the calls since the previous
+        read (the last 16 at most; zeros for a direction never run)."""
         ms = (ctypes.c_double * 8)()
         self._check(self._lib.nufft_get_stage_times(self._h, ms))
         keys = ["sort", "spread", "fft1", "deconv", "clear", "interp", "fft2", "pad"]

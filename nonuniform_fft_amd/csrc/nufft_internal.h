@@ -228,10 +228,16 @@ struct nufft_plan_s {
     rocfft_execution_info fft_info = nullptr;
 
     // timing
-    hipEvent_t ev[16] = {};
+    // stage timing (opts.timing): a ring of event sets, one set per step (a setpts, or an
+    // execute of a direction already recorded in the current set), read without host syncs
+    // until nufft_get_stage_times averages the steps recorded since its last call
+    static constexpr int kEvRing = 16;
+    hipEvent_t ev[kEvRing][16] = {};
+    unsigned char ev_rec[kEvRing] = {};   // bits: 1 type 1 stages, 2 type 2 stages, 4 sort
+    int ev_cur = 0;
+    int ev_n = 0;                         // sets used since the last readout (<= kEvRing)
     bool ev_ok = false;
     double stage_ms[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int stage_recorded = 0;             // bit 0: type 1 steps recorded, bit 1: type 2 steps
 };
 
 namespace nufft {

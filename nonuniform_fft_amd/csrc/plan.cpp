@@ -248,7 +248,22 @@ nufft::GeomArgs geom(const nufft_plan p) {
 }
 
 void record(nufft_plan p, int i) {
-    if (p->opts.timing && p->ev_ok) (void)hipEventRecord(p->ev[i], p->stream);
+    if (p->opts.timing && p->ev_ok) (void)hipEventRecord(p->ev[p->ev_cur][i], p->stream);
+}
+
+// Opens the event set for a stage group (bit: 1 type 1, 2 type 2, 4 sort): a new set when the
+// group starts a step (the sort) or when the current set already holds this group.
+void begin_group(nufft_plan p, unsigned char bit) {
+    if (!p->opts.timing || !p->ev_ok) return;
+    if (p->ev_n == 0 || bit == 4 || (p->ev_rec[p->ev_cur] & bit)) {
+        p->ev_cur = (p->ev_cur + 1) % nufft_plan_s::kEvRing;
+        p->ev_rec[p->ev_cur] = 0;
+        p->ev_n = std::min(p->ev_n + 1, nufft_plan_s::kEvRing);
+    }
+}
+
+void end_group(nufft_plan p, unsigned char bit) {
+    if (p->opts.timing && p->ev_ok) p->ev_rec[p->ev_cur] |= bit;
 }
 
 int fft_exec(nufft_plan plan, rocfft_plan fp, void* src, void* dst) {
@@ -338,6 +353,7 @@ int run_type1(nufft_plan plan, const void* c, void* f, int nv = 1) {
     nufft::GeomArgs g = geom(plan);
     g.nv = nv;
     const size_t gbytes = (size_t)grid_cells(plan) * 2 * real_size(plan) * nv;
+    begin_group(plan, 1);
     record(plan, EV_T1 + 0);
     NUFFT_HIP(nufft::launch_fill_zero(grid, gbytes, plan->stream));
     record(plan, EV_T1 + 1);
@@ -348,7 +364,7 @@ int run_type1(nufft_plan plan, const void* c, void* f, int nv = 1) {
     NUFFT_HIP(nufft::launch_deconvolve(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, grid2, f,
                                        plan->stream, nv));
     record(plan, EV_T1 + 4);
-    plan->stage_recorded |= 1;
+    end_group(plan, 1);
     return NUFFT_OK;
 }
 
@@ -360,6 +376,7 @@ int run_type2(nufft_plan plan, void* c, const void* f, int nv = 1) {
     if ((rc = batch_buffers(plan, nv, &grid, &grid2, &cs)) != NUFFT_OK) return rc;
     nufft::GeomArgs g = geom(plan);
     g.nv = nv;
+    begin_group(plan, 2);
     record(plan, EV_T2 + 0);
     NUFFT_HIP(nufft::launch_precorrect_pad(plan->prec, plan->dim, plan->N, plan->n, plan->pcorr.p, f, grid,
                                            plan->stream, nv));
@@ -368,7 +385,7 @@ int run_type2(nufft_plan plan, void* c, const void* f, int nv = 1) {
     record(plan, EV_T2 + 2);
     NUFFT_HIP(nufft::launch_interp(plan->prec, plan->method, g, grid2, c, plan->stream));
     record(plan, EV_T2 + 3);
-    plan->stage_recorded |= 2;
+    end_group(plan, 2);
     return NUFFT_OK;
 }
 
@@ -461,7 +478,8 @@ int nufft_destroy(nufft_plan plan) {
                       &plan->t3_tab})
         dev_free(plan, *b);
     if (plan->ev_ok)
-        for (auto& e : plan->ev) (void)hipEventDestroy(e);
+        for (auto& set : plan->ev)
+            for (auto& e : set) (void)hipEventDestroy(e);
     delete plan;
     return NUFFT_OK;
 }
@@ -620,8 +638,9 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
     }
     if (plan->opts.timing) {
         plan->ev_ok = true;
-        for (auto& e : plan->ev)
-            if (hipEventCreate(&e) != hipSuccess) plan->ev_ok = false;
+        for (auto& set : plan->ev)
+            for (auto& e : set)
+                if (hipEventCreate(&e) != hipSuccess) plan->ev_ok = false;
     }
     *out = plan;
     return status;
@@ -652,6 +671,7 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     int64_t* nsub_dev = (int64_t*)tail;
     int* bad_dev = (int*)(tail + 64);
 
+    begin_group(plan, 4);
     record(plan, EV_SORT0);
     NUFFT_HIP(hipMemsetAsync(bad_dev, 0, sizeof(int), plan->stream));
     nufft::SortArgs a{};
@@ -680,13 +700,9 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
         NUFFT_HIP(hipStreamSynchronize(plan->stream));
         if (host_bad) return fail(plan, NUFFT_ERR_POINTS, "a coordinate is not finite or outside [-3pi, 3pi)");
         record(plan, EV_SORT1);
+        end_group(plan, 4);
         plan->M = M;
         plan->nsub = 0;
-        if (plan->opts.timing && plan->ev_ok) {
-            NUFFT_HIP(hipEventSynchronize(plan->ev[EV_SORT1]));
-            float ms = 0;
-            if (hipEventElapsedTime(&ms, plan->ev[EV_SORT0], plan->ev[EV_SORT1]) == hipSuccess) plan->stage_ms[0] = ms;
-        }
         return NUFFT_OK;
     }
     NUFFT_HIP(nufft::launch_sort(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p,
@@ -706,13 +722,9 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
                                                    (const int32_t*)plan->offsets.p, plan->sort_tmp.p,
                                                    (int32_t*)plan->sub.p, plan->stream));
     record(plan, EV_SORT1);
+    end_group(plan, 4);
     plan->M = M;
     plan->nsub = host_nsub;
-    if (plan->opts.timing && plan->ev_ok) {
-        NUFFT_HIP(hipEventSynchronize(plan->ev[EV_SORT1]));
-        float ms = 0;
-        if (hipEventElapsedTime(&ms, plan->ev[EV_SORT0], plan->ev[EV_SORT1]) == hipSuccess) plan->stage_ms[0] = ms;
-    }
     return NUFFT_OK;
 }
 
@@ -911,21 +923,35 @@ int nufft_get_stage_times(nufft_plan plan, double* ms) {
     if (!plan || !ms) return NUFFT_ERR_BAD_ARG;
     if (!plan->opts.timing || !plan->ev_ok) return fail(plan, NUFFT_ERR_BAD_STATE, "timing not enabled");
     NUFFT_HIP(hipStreamSynchronize(plan->stream));
-    auto span = [&](int a, int b) {
-        float t = 0;
-        return (hipEventElapsedTime(&t, plan->ev[a], plan->ev[b]) == hipSuccess) ? (double)t : 0.0;
-    };
-    if (plan->stage_recorded & 1) {
-        plan->stage_ms[4] = span(EV_T1 + 0, EV_T1 + 1);
-        plan->stage_ms[1] = span(EV_T1 + 1, EV_T1 + 2);
-        plan->stage_ms[2] = span(EV_T1 + 2, EV_T1 + 3);
-        plan->stage_ms[3] = span(EV_T1 + 3, EV_T1 + 4);
+    // average each stage over the event sets recorded since the last readout
+    double sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < plan->ev_n; ++k) {
+        const int set = (plan->ev_cur - k + nufft_plan_s::kEvRing) % nufft_plan_s::kEvRing;
+        const unsigned char rec = plan->ev_rec[set];
+        auto add = [&](int stage, int a, int b) {
+            float t = 0;
+            if (hipEventElapsedTime(&t, plan->ev[set][a], plan->ev[set][b]) == hipSuccess) {
+                sum[stage] += t;
+                ++cnt[stage];
+            }
+        };
+        if (rec & 4) add(0, EV_SORT0, EV_SORT1);
+        if (rec & 1) {
+            add(4, EV_T1 + 0, EV_T1 + 1);
+            add(1, EV_T1 + 1, EV_T1 + 2);
+            add(2, EV_T1 + 2, EV_T1 + 3);
+            add(3, EV_T1 + 3, EV_T1 + 4);
+        }
+        if (rec & 2) {
+            add(7, EV_T2 + 0, EV_T2 + 1);
+            add(6, EV_T2 + 1, EV_T2 + 2);
+            add(5, EV_T2 + 2, EV_T2 + 3);
+        }
     }
-    if (plan->stage_recorded & 2) {
-        plan->stage_ms[7] = span(EV_T2 + 0, EV_T2 + 1);
-        plan->stage_ms[6] = span(EV_T2 + 1, EV_T2 + 2);
-        plan->stage_ms[5] = span(EV_T2 + 2, EV_T2 + 3);
-    }
+    for (int i = 0; i < 8; ++i)
+        if (cnt[i] > 0) plan->stage_ms[i] = sum[i] / cnt[i];
+    plan->ev_n = 0;   // the next stage group opens a new set
     for (int i = 0; i < 8; ++i) ms[i] = plan->stage_ms[i];
     return NUFFT_OK;
 }
