@@ -237,6 +237,7 @@ struct nufft_plan_s {
     int ev_cur = 0;
     int ev_n = 0;                         // sets used since the last readout (<= kEvRing)
     bool ev_ok = false;
+    void* host_tail = nullptr;            // pinned 128 B: setpts reads the subproblem count and bad-point flag here
     double stage_ms[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 };
 

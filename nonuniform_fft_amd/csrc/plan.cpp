@@ -477,6 +477,7 @@ int nufft_destroy(nufft_plan plan) {
                       &plan->t3_y, &plan->t3_theta, &plan->t3_pre, &plan->t3_post, &plan->t3_cp, &plan->t3_cin,
                       &plan->t3_tab})
         dev_free(plan, *b);
+    if (plan->host_tail) (void)hipHostFree(plan->host_tail);
     if (plan->ev_ok)
         for (auto& set : plan->ev)
             for (auto& e : set) (void)hipEventDestroy(e);
@@ -668,6 +669,7 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
         return rc;
     // two small result slots at the end of the scratch: int64 subproblem count, int bad-point flag
     char* tail = (char*)plan->sort_tmp.p + (plan->sort_tmp.bytes - 256);
+    if (!plan->host_tail) NUFFT_HIP(hipHostMalloc(&plan->host_tail, 128, hipHostMallocDefault));
     int64_t* nsub_dev = (int64_t*)tail;
     int* bad_dev = (int*)(tail + 64);
 
@@ -695,9 +697,9 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
         // no sort and no binning: the points stay in the caller's order and the bin counts read zero
         NUFFT_HIP(nufft::launch_fill_zero(plan->counts.p, (size_t)plan->nbins * sizeof(int32_t), plan->stream));
         NUFFT_HIP(nufft::launch_identity_order(a, (int32_t*)plan->perm.p, plan->xs.p, bad_dev, plan->stream));
-        int host_bad = 0;
-        NUFFT_HIP(hipMemcpyAsync(&host_bad, bad_dev, sizeof(int), hipMemcpyDeviceToHost, plan->stream));
+        NUFFT_HIP(hipMemcpyAsync(plan->host_tail, tail, 128, hipMemcpyDeviceToHost, plan->stream));
         NUFFT_HIP(hipStreamSynchronize(plan->stream));
+        const int host_bad = *(const int*)((const char*)plan->host_tail + 64);
         if (host_bad) return fail(plan, NUFFT_ERR_POINTS, "a coordinate is not finite or outside [-3pi, 3pi)");
         record(plan, EV_SORT1);
         end_group(plan, 4);
@@ -708,11 +710,11 @@ int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const
     NUFFT_HIP(nufft::launch_sort(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p,
                                  (int32_t*)plan->offsets.p, plan->xs.p, plan->sort_tmp.p,
                                  plan->sort_tmp.bytes - 256, nsub_dev, bad_dev, plan->stream));
-    int64_t host_nsub = 0;
-    int host_bad = 0;
-    NUFFT_HIP(hipMemcpyAsync(&host_nsub, nsub_dev, sizeof(int64_t), hipMemcpyDeviceToHost, plan->stream));
-    NUFFT_HIP(hipMemcpyAsync(&host_bad, bad_dev, sizeof(int), hipMemcpyDeviceToHost, plan->stream));
+    // one read of both result slots into pinned memory
+    NUFFT_HIP(hipMemcpyAsync(plan->host_tail, tail, 128, hipMemcpyDeviceToHost, plan->stream));
     NUFFT_HIP(hipStreamSynchronize(plan->stream));
+    const int64_t host_nsub = *(const int64_t*)plan->host_tail;
+    const int host_bad = *(const int*)((const char*)plan->host_tail + 64);
     if (host_bad) return fail(plan, NUFFT_ERR_POINTS, "a coordinate is not finite or outside [-3pi, 3pi)");
     if ((rc = dev_alloc(plan, plan->sub, (size_t)std::max<int64_t>(host_nsub, 1) * 3 * sizeof(int32_t),
                         "subproblem list")) != NUFFT_OK)
