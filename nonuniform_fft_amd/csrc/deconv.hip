@@ -40,7 +40,7 @@ __global__ void __launch_bounds__(kBlock) k_deconvolve(int N1, int N2, int N3, i
 }
 
 template <typename T, int DIM>
-__global__ void __launch_bounds__(kBlock) k_precorrect_pad(int N1, int N2, int N3, int n1, int n2, int n3,
+__global__ void __launch_bounds__(kBlock) k_precorrect_pad(int N1, int N2, int N3, int n1, int n2, int n3, FastDiv fd1, FastDiv fd2,
                                                            const T* __restrict__ p,
                                                            const cplx<T>* __restrict__ f,
                                                            cplx<T>* __restrict__ fhat) {
@@ -50,10 +50,19 @@ __global__ void __launch_bounds__(kBlock) k_precorrect_pad(int N1, int N2, int N
     const int64_t total = (int64_t)n1 * n2 * n3;
     const int64_t cell = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (cell >= total) return;
-    const int l1 = (int)(cell % n1);
-    const int64_t r = cell / n1;
-    const int l2 = (int)(r % n2);
-    const int l3 = (int)(r / n2);
+    int l1, l2, l3;
+    if (total < (int64_t(1) << 31)) {   // 32-bit multiply-high division (fd = reciprocals of n1, n2)
+        const int c32 = (int)cell;
+        const int r = fast_div(c32, fd1);
+        l1 = c32 - r * n1;
+        l3 = fast_div(r, fd2);
+        l2 = r - l3 * n2;
+    } else {
+        l1 = (int)(cell % n1);
+        const int64_t r = cell / n1;
+        l2 = (int)(r % n2);
+        l3 = (int)(r / n2);
+    }
     // mode k of cell l: k = l on the nonnegative part of I_N, k = l - n on the negative part
     auto mode_index = [](int l, int N, int n) -> int {
         if (l < N - N / 2) return l + N / 2;
@@ -100,11 +109,11 @@ hipError_t launch_precorrect_pad(int prec, int dim, const int64_t* N, const int6
     int64_t total = n[0] * n[1] * (int64_t)n3;
     dim3 g((unsigned)((total + kBlock - 1) / kBlock), (unsigned)nv);
     if (prec == 0) {
-        if (dim <= 2) k_precorrect_pad<float, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const float*)pcorr, (const cplx<float>*)f, (cplx<float>*)fhat);
-        else k_precorrect_pad<float, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, (const float*)pcorr, (const cplx<float>*)f, (cplx<float>*)fhat);
+        if (dim <= 2) k_precorrect_pad<float, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, make_fastdiv((int)n[0]), make_fastdiv((int)n[1]), (const float*)pcorr, (const cplx<float>*)f, (cplx<float>*)fhat);
+        else k_precorrect_pad<float, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, make_fastdiv((int)n[0]), make_fastdiv((int)n[1]), (const float*)pcorr, (const cplx<float>*)f, (cplx<float>*)fhat);
     } else {
-        if (dim <= 2) k_precorrect_pad<double, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, (const double*)pcorr, (const cplx<double>*)f, (cplx<double>*)fhat);
-        else k_precorrect_pad<double, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, (const double*)pcorr, (const cplx<double>*)f, (cplx<double>*)fhat);
+        if (dim <= 2) k_precorrect_pad<double, 2><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], 1, (int)n[0], (int)n[1], 1, make_fastdiv((int)n[0]), make_fastdiv((int)n[1]), (const double*)pcorr, (const cplx<double>*)f, (cplx<double>*)fhat);
+        else k_precorrect_pad<double, 3><<<g, kBlock, 0, st>>>((int)N[0], (int)N[1], N3, (int)n[0], (int)n[1], n3, make_fastdiv((int)n[0]), make_fastdiv((int)n[1]), (const double*)pcorr, (const cplx<double>*)f, (cplx<double>*)fhat);
     }
     return hipGetLastError();
 }
