@@ -78,12 +78,14 @@ __global__ void __launch_bounds__(kInterpBlock) k_interp_gm(GeomArgs g, const cp
 }
 
 // 3D: 768 lanes.  fp64 tiles leave room for one workgroup per CU (three wavefronts per SIMD);
-// fp32 tiles for two (six per SIMD), which measured faster than 512 or 1024 lanes.
-template <typename T, int DIM>
-constexpr int kInterpSmBlock = (DIM == 3) ? 768 : 512;
+// fp32 tiles for two (six per SIMD), which measured faster than 512 or 1024 lanes.  fp64 up to
+// w = 12 takes 1024 lanes (at most 128 VGPRs, a few spilled at w = 10): 3D 256^3 fp64 w = 10
+// interpolation 37.4 -> 36.3 ms.
+template <typename T, int DIM, int W>
+constexpr int kInterpSmBlock = (DIM == 3) ? ((sizeof(T) == 8 && W <= 12) ? 1024 : 768) : 512;
 
 template <typename T, int DIM, int W>
-__global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs g, const cplx<T>* __restrict__ grid,
+__global__ void __launch_bounds__((kInterpSmBlock<T, DIM, W>)) k_interp_sm(GeomArgs g, const cplx<T>* __restrict__ grid,
                                                               cplx<T>* __restrict__ c, int p1, int p2,
                                                               int p3) {
     // vector blockIdx.y of a many-vector launch (strides in complex values)
@@ -119,8 +121,8 @@ __global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs
     const int pd[3] = {p1, p2, p3};
     auto copy = [&](auto fast) {
         constexpr bool FAST = decltype(fast)::value;
-        CellWalk cw(threadIdx.x, kInterpSmBlock<T, DIM>, p1, p2);
-        for (int k = threadIdx.x; k < P; k += (kInterpSmBlock<T, DIM>), cw.next()) {
+        CellWalk cw(threadIdx.x, kInterpSmBlock<T, DIM, W>, p1, p2);
+        for (int k = threadIdx.x; k < P; k += (kInterpSmBlock<T, DIM, W>), cw.next()) {
             const int g1 = wrap_pad<FAST>(origin[0] + cw.s1, g.n[0]);
             const int g2 = (DIM >= 2) ? wrap_pad<FAST>(origin[1] + cw.s2, g.n[1]) : 0;
             const int g3 = (DIM == 3) ? wrap_pad<FAST>(origin[2] + cw.s3, g.n[2]) : 0;
@@ -131,16 +133,16 @@ __global__ void __launch_bounds__((kInterpSmBlock<T, DIM>)) k_interp_sm(GeomArgs
     else copy(std::false_type{});
     __syncthreads();
     const T beta = (T)g.beta;
-    for (int i = threadIdx.x; i < len; i += (kInterpSmBlock<T, DIM>)) {
+    for (int i = threadIdx.x; i < len; i += (kInterpSmBlock<T, DIM, W>)) {
         const int64_t j = (int64_t)start + i;
         T xc[DIM];
 #pragma unroll
         for (int d = 0; d < DIM; ++d) xc[d] = xn[d];
         const int32_t oc = on;
-        if (i + (kInterpSmBlock<T, DIM>) < len) {
+        if (i + (kInterpSmBlock<T, DIM, W>) < len) {
 #pragma unroll
-            for (int d = 0; d < DIM; ++d) xn[d] = ((const T*)g.xs[d])[j + (kInterpSmBlock<T, DIM>)];
-            on = g.perm[j + (kInterpSmBlock<T, DIM>)];
+            for (int d = 0; d < DIM; ++d) xn[d] = ((const T*)g.xs[d])[j + (kInterpSmBlock<T, DIM, W>)];
+            on = g.perm[j + (kInterpSmBlock<T, DIM, W>)];
         }
         T ker[DIM][W];
         int l0[3] = {0, 0, 0};
@@ -210,7 +212,7 @@ hipError_t interp_w(int method, const GeomArgs& g, const void* grid, void* c, hi
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_interp_sm<T, DIM, W><<<dim3((unsigned)g.nsub, (unsigned)g.nv), (kInterpSmBlock<T, DIM>), lds, st>>>(
+    k_interp_sm<T, DIM, W><<<dim3((unsigned)g.nsub, (unsigned)g.nv), (kInterpSmBlock<T, DIM, W>), lds, st>>>(
         g, (const cplx<T>*)grid, (cplx<T>*)c, p1, p2, p3);
     return hipGetLastError();
 }
