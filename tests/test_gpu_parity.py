@@ -416,6 +416,28 @@ def test_repeated_execute_and_resetpts(nf, orc):
     p.destroy()
 
 
+def test_stage_times_average_and_reset(nf):
+    """Stage times average the calls since the previous read (the last 16 when there are
+    more); a stage not run since then keeps its value, a direction never run reads zero."""
+    import torch
+    wl = Workload("tm", 2, (64, 48), 20_000, 1e-5, "f32", seed=141)
+    inp = make_inputs(wl, want_f=False)
+    p = nf.Plan(1, wl.N, wl.eps, wl.precision, timing=True)
+    c = to_dev(inp["c"])
+    f = torch.empty(tuple(reversed(wl.N)), dtype=cdtype(wl.precision), device=dev())
+    p.setpts(*[to_dev(x) for x in inp["X"]])
+    p.execute(c, f)
+    st1 = p.stage_times()
+    assert st1["sort"] > 0 and st1["spread"] > 0 and st1["fft1"] > 0
+    assert st1["interp"] == 0 and st1["fft2"] == 0
+    for _ in range(20):   # more executes than the event ring holds
+        p.execute(c, f)
+    st2 = p.stage_times()
+    assert st2["sort"] == st1["sort"]
+    assert st2["spread"] > 0 and st2["deconv"] > 0
+    p.destroy()
+
+
 @pytest.mark.parametrize("wl", [Workload("adj", 3, (24, 20, 18), 40_000, 1e-5, "f32", seed=71),
                                 Workload("adj", 2, (64, 48), 20_000, 1e-12, "f64", seed=72)],
                          ids=["3d_f32", "2d_f64"])
