@@ -78,11 +78,13 @@ __global__ void __launch_bounds__(kInterpBlock) k_interp_gm(GeomArgs g, const cp
 }
 
 // 3D: 768 lanes.  fp64 tiles leave room for one workgroup per CU (three wavefronts per SIMD);
-// fp32 tiles for two (six per SIMD), which measured faster than 512 or 1024 lanes.  fp64 up to
-// w = 12 takes 1024 lanes (at most 128 VGPRs, a few spilled at w = 10): 3D 256^3 fp64 w = 10
-// interpolation 37.4 -> 36.3 ms.
+// fp32 tiles for two (six per SIMD), which measured faster than 512 or 1024 lanes at w = 6.
+// fp64 up to w = 12 takes 1024 lanes (at most 128 VGPRs, a few spilled at w = 10): 3D 256^3
+// fp64 w = 10 interpolation 37.4 -> 36.3 ms.  fp32 below w = 5, whose small tiles fit four
+// times, takes 512 lanes (32 wavefronts per CU instead of 24): 3D 128^3 w = 3 0.377 -> 0.358 ms.
 template <typename T, int DIM, int W>
-constexpr int kInterpSmBlock = (DIM == 3) ? ((sizeof(T) == 8 && W <= 12) ? 1024 : 768) : 512;
+constexpr int kInterpSmBlock =
+    (DIM == 3) ? ((sizeof(T) == 8 && W <= 12) ? 1024 : (sizeof(T) == 4 && W < 5) ? 512 : 768) : 512;
 
 template <typename T, int DIM, int W>
 __global__ void __launch_bounds__((kInterpSmBlock<T, DIM, W>)) k_interp_sm(GeomArgs g, const cplx<T>* __restrict__ grid,
