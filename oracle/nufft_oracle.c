@@ -15,9 +15,10 @@
  * Everything is fp64, IEEE round-to-nearest, compiled without FP contraction
  * and without fast-math.  Loops are written in the order the equations state
  * them; nothing is blocked, fused or reordered for speed.  The only
- * parallelism (OpenMP) is over independent outputs of the exact sums and over
- * point ranges of the sampled type 1 evaluation, whose partial sums are added
- * in range order; spreading, interpolation and the bin-sort are serial.  Arrays of complex
+ * parallelism (OpenMP) is over independent outputs of the exact sums, over
+ * point ranges of the sampled type 1 evaluation (partial sums added in range
+ * order), and in the parallel spreading / interpolation forms, which give the
+ * serial forms' results bit for bit (see there); the bin-sort is serial.  Arrays of complex
  * numbers are interleaved (re, im).  Grids are stored with the first index
  * fastest: cell (l1, l2, l3) sits at l1 + n1*(l2 + n2*l3).
  */
@@ -169,67 +170,165 @@ int oracle_interp(int d, const int64_t* n, int w, double beta, int64_t M,
 }
 
 /*
+ * Parallel forms of the two steps above, for large inputs.  Both give exactly
+ * the serial result, bit for bit, because every output is still summed over
+ * the same terms in the same order:
+ *  - spreading: the grid is cut along its slowest dimension into one slab per
+ *    thread; each thread walks all points in index order and adds only the
+ *    contributions whose cell lies in its own slab (so no two threads write a
+ *    cell, and each cell receives its terms in the serial order);
+ *  - interpolation: every point's sum is independent; threads take points.
+ * threads <= 0 means all available threads.
+ */
+int oracle_spread_par(int d, const int64_t* n, int w, double beta, int64_t M,
+                      const double* const* X, const double* c, double* b, int threads)
+{
+    if (d < 1 || d > 3 || w < 1 || w > 32 || M < 0) return ORACLE_BAD_ARG;
+    int64_t nn[3] = {1, 1, 1};
+    for (int i = 0; i < d; ++i) nn[i] = n[i];
+    for (int64_t j = 0; j < M; ++j)
+        for (int i = 0; i < d; ++i) {
+            double t; int64_t l;
+            if (grid_coord(X[i][j], nn[i], oracle_grid_scale(nn[i]), &t, &l) != ORACLE_OK)
+                return ORACLE_BAD_POINT;
+        }
+    int T = 1;
+#ifdef _OPENMP
+    T = threads > 0 ? threads : omp_get_max_threads();
+#endif
+    (void)threads;
+    const int slow = d - 1;
+    int wd[3] = {1, 1, 1};
+    for (int i = 0; i < d; ++i) wd[i] = w;
+#pragma omp parallel num_threads(T)
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        const int64_t lo = nn[slow] * tid / T, hi = nn[slow] * (tid + 1) / T;
+        double phi[3][32];
+        int64_t cell[3][32];
+        for (int64_t j = 0; j < M; ++j) {
+            double ts; int64_t ls;
+            grid_coord(X[slow][j], nn[slow], oracle_grid_scale(nn[slow]), &ts, &ls);
+            /* does the support along the slow dimension meet this slab? */
+            const int64_t l0 = (int64_t)ceil(ts - 0.5 * (double)w);
+            int meets = 0;
+            for (int q = 0; q < w && !meets; ++q) {
+                const int64_t cq = pmod(l0 + q, nn[slow]);
+                meets = (cq >= lo && cq < hi);
+            }
+            if (!meets) continue;
+            for (int i = 0; i < 3; ++i) { phi[i][0] = 1.0; cell[i][0] = 0; }
+            for (int i = 0; i < d; ++i) {
+                double t; int64_t l;
+                grid_coord(X[i][j], nn[i], oracle_grid_scale(nn[i]), &t, &l);
+                stencil_1d(t, nn[i], w, beta, phi[i], cell[i]);
+            }
+            double cre = c[2 * j], cim = c[2 * j + 1];
+            for (int q3 = 0; q3 < wd[2]; ++q3)
+                for (int q2 = 0; q2 < wd[1]; ++q2)
+                    for (int q1 = 0; q1 < wd[0]; ++q1) {
+                        const int64_t cs = (slow == 2) ? cell[2][q3] : (slow == 1) ? cell[1][q2] : cell[0][q1];
+                        if (cs < lo || cs >= hi) continue;
+                        double k = phi[0][q1] * phi[1][q2] * phi[2][q3];
+                        int64_t idx = cell[0][q1] + nn[0] * (cell[1][q2] + nn[1] * cell[2][q3]);
+                        b[2 * idx] += cre * k;
+                        b[2 * idx + 1] += cim * k;
+                    }
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_interp_par(int d, const int64_t* n, int w, double beta, int64_t M,
+                      const double* const* X, const double* b, double* c, int threads)
+{
+    if (d < 1 || d > 3 || w < 1 || w > 32 || M < 0) return ORACLE_BAD_ARG;
+    int64_t nn[3] = {1, 1, 1};
+    for (int i = 0; i < d; ++i) nn[i] = n[i];
+    for (int64_t j = 0; j < M; ++j)
+        for (int i = 0; i < d; ++i) {
+            double t; int64_t l;
+            if (grid_coord(X[i][j], nn[i], oracle_grid_scale(nn[i]), &t, &l) != ORACLE_OK)
+                return ORACLE_BAD_POINT;
+        }
+    int T = 1;
+#ifdef _OPENMP
+    T = threads > 0 ? threads : omp_get_max_threads();
+#endif
+    (void)threads;
+    int wd[3] = {1, 1, 1};
+    for (int i = 0; i < d; ++i) wd[i] = w;
+#pragma omp parallel for num_threads(T) schedule(static)
+    for (int64_t j = 0; j < M; ++j) {
+        double phi[3][32];
+        int64_t cell[3][32];
+        for (int i = 0; i < 3; ++i) { phi[i][0] = 1.0; cell[i][0] = 0; }
+        for (int i = 0; i < d; ++i) {
+            double t; int64_t l;
+            grid_coord(X[i][j], nn[i], oracle_grid_scale(nn[i]), &t, &l);
+            stencil_1d(t, nn[i], w, beta, phi[i], cell[i]);
+        }
+        double sre = 0.0, sim = 0.0;
+        for (int q3 = 0; q3 < wd[2]; ++q3)
+            for (int q2 = 0; q2 < wd[1]; ++q2)
+                for (int q1 = 0; q1 < wd[0]; ++q1) {
+                    double k = phi[0][q1] * phi[1][q2] * phi[2][q3];
+                    int64_t idx = cell[0][q1] + nn[0] * (cell[1][q2] + nn[1] * cell[2][q3]);
+                    sre += b[2 * idx] * k;
+                    sim += b[2 * idx + 1] * k;
+                }
+        c[2 * j] = sre;
+        c[2 * j + 1] = sim;
+    }
+    return ORACLE_OK;
+}
+
+/*
  * Bin-sort of the points (Sec. III-A, GM-sort and SM step 1).
  *
  * The fine grid is cut into bins of m1 x m2 (x m3) cells, ordered with the x
  * index fastest.  Point j lies in the bin holding its cell l_i = floor(t_i).
  * Outputs: bin[j]; counts[b] = number of points in bin b; perm = the points
- * listed bin by bin (a stable counting sort: the list is read out in bin
- * order).  Inside a bin the order is the original index, or, when w_col > 0
- * (2D and 3D), the x-y block of the point's kernel support first, then (3D)
- * the z start of the support, then the original index.  The support of a point
- * starts at l0_i = ceil(t_i - w/2); relative to its bin's padded origin
- * o_i = b_i m_i - floor(w/2) that start is c_i = l0_i - o_i in [0, m_i].
- * Starts are grouped in blocks of s x s (s = col_step >= 1): the block is
- * (c_1 / s, c_2 / s), numbered (c_2 / s) ceil((m1 + 1) / s) + c_1 / s, and the
- * in-bin key is block (m3 + 1) + c_3 in 3D, the block in 2D.  This ordering is
- * not from the pages: in 3D it is the order the column-run kernels consume,
- * stated here so the permutation can be checked exactly (the 2D form is kept
- * for block orders in 2D; the library's 2D plans use the original index).
+ * listed bin by bin, which is how the page reads the list out "in bin
+ * ordering".  The page leaves the order inside a bin open; the reading taken
+ * here is the stable one, increasing original index, so perm is the stable
+ * counting sort of bin[] (a library may order a bin's points differently as
+ * long as each bin keeps exactly its own points).
  */
 int oracle_binsort(int d, const int64_t* n, const int64_t* m, int64_t M, const double* const* X,
-                   int w_col, int col_step, int64_t* bin, int64_t* counts, int64_t* perm)
+                   int64_t* bin, int64_t* counts, int64_t* perm)
 {
-    if (d < 1 || d > 3 || M < 0 || col_step < 1) return ORACLE_BAD_ARG;
+    if (d < 1 || d > 3 || M < 0) return ORACLE_BAD_ARG;
     int64_t nb[3] = {1, 1, 1};
     for (int i = 0; i < d; ++i) {
         if (n[i] < 1 || m[i] < 1) return ORACLE_BAD_ARG;
         nb[i] = (n[i] + m[i] - 1) / m[i];
     }
-    int use_col = (w_col > 0 && d >= 2);
-    int64_t ncx = (m[0] + col_step) / col_step, ncy = (m[1] + col_step) / col_step;
-    int64_t ncol = use_col ? ncx * ncy * (d == 3 ? m[2] + 1 : 1) : 1;
     int64_t nbins = nb[0] * nb[1] * nb[2];
-    int64_t nkeys = nbins * ncol;
-    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
-    int64_t* next = (int64_t*)calloc((size_t)(nkeys > 0 ? nkeys : 1), sizeof(int64_t));
-    if (!key || !next) { free(key); free(next); return ORACLE_BAD_ARG; }
+    int64_t* next = (int64_t*)calloc((size_t)(nbins > 0 ? nbins : 1), sizeof(int64_t));
+    if (!next) return ORACLE_BAD_ARG;
     for (int64_t b = 0; b < nbins; ++b) counts[b] = 0;
     for (int64_t j = 0; j < M; ++j) {
-        int64_t bi[3] = {0, 0, 0}, lo[3] = {0, 0, 0};
+        int64_t bi[3] = {0, 0, 0};
         for (int i = 0; i < d; ++i) {
             double t; int64_t l;
             if (grid_coord(X[i][j], n[i], oracle_grid_scale(n[i]), &t, &l) != ORACLE_OK) {
-                free(key); free(next);
+                free(next);
                 return ORACLE_BAD_POINT;
             }
             bi[i] = l / m[i];
-            if (use_col) lo[i] = (int64_t)ceil(t - 0.5 * (double)w_col) - (bi[i] * m[i] - w_col / 2);
         }
         bin[j] = bi[0] + nb[0] * (bi[1] + nb[1] * bi[2]);
         counts[bin[j]] += 1;
-        if (!use_col)
-            key[j] = bin[j];
-        else if (d == 3)
-            key[j] = bin[j] * ncol + ((lo[1] / col_step) * ncx + lo[0] / col_step) * (m[2] + 1) + lo[2];
-        else
-            key[j] = bin[j] * ncol + (lo[1] / col_step) * ncx + lo[0] / col_step;
-        next[key[j]] += 1;
     }
+    /* exclusive prefix sum of the counts: where each bin's run starts */
     int64_t run = 0;
-    for (int64_t k = 0; k < nkeys; ++k) { int64_t c = next[k]; next[k] = run; run += c; }
-    for (int64_t j = 0; j < M; ++j) perm[next[key[j]]++] = j;
-    free(key);
+    for (int64_t b = 0; b < nbins; ++b) { next[b] = run; run += counts[b]; }
+    /* read the points out in bin order, ascending j inside a bin */
+    for (int64_t j = 0; j < M; ++j) perm[next[bin[j]]++] = j;
     free(next);
     return ORACLE_OK;
 }

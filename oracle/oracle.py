@@ -73,7 +73,11 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = [I, P, I, D, L, P, P, P]
             fn.restype = I
-        lib.oracle_binsort.argtypes = [I, P, P, L, P, I, I, P, P, P]
+        for name in ("oracle_spread_par", "oracle_interp_par"):
+            fn = getattr(lib, name)
+            fn.argtypes = [I, P, I, D, L, P, P, P, I]
+            fn.restype = I
+        lib.oracle_binsort.argtypes = [I, P, P, L, P, P, P, P]
         lib.oracle_binsort.restype = I
         lib.oracle_subproblems.argtypes = [L, P, L, P]
         lib.oracle_subproblems.restype = L
@@ -217,7 +221,13 @@ def _check(rc: int, what: str):
 # Steps of the method
 # ----------------------------------------------------------------------------------------------
 
-def spread(X, c, n: Sequence[int], w: int, beta: float) -> np.ndarray:
+# Threads of the parallel spreading / interpolation forms (0 = all host cores, 1 = the plain serial
+# loops).  The parallel forms return the serial results bit for bit (slab-owned spreading, one
+# independent sum per point); the CPU-baseline timing sets 1 for its serial leg.
+THREADS = 0
+
+
+def spread(X, c, n: Sequence[int], w: int, beta: float, threads: Optional[int] = None) -> np.ndarray:
     """Type 1 step 1, eq. (7).  Returns b with shape (n3, n2, n1) (n1 fastest), complex128."""
     lib = _load()
     d = len(n)
@@ -226,11 +236,16 @@ def spread(X, c, n: Sequence[int], w: int, beta: float) -> np.ndarray:
     M = xs[0].size
     b = np.zeros(int(np.prod(n)), dtype=np.complex128)
     nn = _i64(n)
-    _check(lib.oracle_spread(d, _ptr(nn), w, beta, M, xa, _ptr(cc), _ptr(b)), "spread")
+    th = THREADS if threads is None else threads
+    if th == 1:
+        rc = lib.oracle_spread(d, _ptr(nn), w, beta, M, xa, _ptr(cc), _ptr(b))
+    else:
+        rc = lib.oracle_spread_par(d, _ptr(nn), w, beta, M, xa, _ptr(cc), _ptr(b), th)
+    _check(rc, "spread")
     return b.reshape(tuple(reversed(n)))
 
 
-def interp(X, b, w: int, beta: float) -> np.ndarray:
+def interp(X, b, w: int, beta: float, threads: Optional[int] = None) -> np.ndarray:
     """Type 2 step 3 (interpolation sum after eq. (12)).  b has shape (n3, n2, n1)."""
     lib = _load()
     b = np.asarray(b)
@@ -241,7 +256,12 @@ def interp(X, b, w: int, beta: float) -> np.ndarray:
     M = xs[0].size
     c = np.zeros(M, dtype=np.complex128)
     nn = _i64(n)
-    _check(lib.oracle_interp(d, _ptr(nn), w, beta, M, xa, _ptr(bb), _ptr(c)), "interp")
+    th = THREADS if threads is None else threads
+    if th == 1:
+        rc = lib.oracle_interp(d, _ptr(nn), w, beta, M, xa, _ptr(bb), _ptr(c))
+    else:
+        rc = lib.oracle_interp_par(d, _ptr(nn), w, beta, M, xa, _ptr(bb), _ptr(c), th)
+    _check(rc, "interp")
     return c
 
 
@@ -440,21 +460,18 @@ class Type3Params:
                 self.gamma.append(1.0)
 
 
-def nufft_type3(X, c, S, eps: float, sigma: float = 2.0, coord_dtype=np.float64) -> np.ndarray:
-    """Type 3 by the steps above: f_k ~ sum_j c_j exp(+i s_k . x_j), k = 1..K.  The scaled
-    coordinates y = (x - C) / gamma and theta = ((s - D) gamma) h are computed in fp64 and then
-    stored in coord_dtype (a single-precision transform keeps them in single precision)."""
+def nufft_type3(X, c, S, eps: float, sigma: float = 2.0) -> np.ndarray:
+    """Type 3 by the steps above, all in fp64: f_k ~ sum_j c_j exp(+i s_k . x_j), k = 1..K."""
     prm = Type3Params(X, S, eps, sigma)
     xs = [np.asarray(x, dtype=np.float64) for x in X]
     ss = [np.asarray(s, dtype=np.float64) for s in S]
-    y = [((x - Ci) / g).astype(coord_dtype).astype(np.float64) for x, Ci, g in zip(xs, prm.C, prm.gamma)]
+    y = [(x - Ci) / g for x, Ci, g in zip(xs, prm.C, prm.gamma)]
     pre = np.zeros(xs[0].size)
     for x, Ci, Di in zip(xs, prm.C, prm.D):
         pre = pre + Di * (x - Ci)
     cp = np.asarray(c, dtype=np.complex128) * np.exp(1j * pre)
     b = spread(y, cp, prm.n, prm.w, prm.beta)
-    theta = [((s - Di) * g * hi).astype(coord_dtype).astype(np.float64)
-             for s, Di, g, hi in zip(ss, prm.D, prm.gamma, prm.h)]
+    theta = [(s - Di) * g * hi for s, Di, g, hi in zip(ss, prm.D, prm.gamma, prm.h)]
     cin = nufft_type2(theta, b, prm.n, eps, sigma)
     out = cin.astype(np.complex128)
     for s, Ci, Di, g, hi, ni in zip(ss, prm.C, prm.D, prm.gamma, prm.h, prm.n):
@@ -485,10 +502,9 @@ def direct_type3(X, c, S, sel: Optional[Sequence[int]] = None) -> np.ndarray:
     return out
 
 
-def binsort(X, n: Sequence[int], m: Sequence[int], w_col: int = 0, col_step: int = 1):
-    """Returns (bin_of_point, counts, perm) as int64 arrays; see the C routine.  With w_col > 0
-    (2D, 3D) the points of a bin are ordered by the col_step x col_step block of the x-y column
-    where their kernel support starts, then (3D) by the z start of the support."""
+def binsort(X, n: Sequence[int], m: Sequence[int]):
+    """Returns (bin_of_point, counts, perm) as int64 arrays: bins x-fastest (Sec. III-A), perm the
+    points read out bin by bin, increasing original index inside a bin (see the C routine)."""
     lib = _load()
     d = len(n)
     xs, xa = _coords(X)
@@ -499,8 +515,7 @@ def binsort(X, n: Sequence[int], m: Sequence[int], w_col: int = 0, col_step: int
     counts = np.zeros(nbins, dtype=np.int64)
     perm = np.zeros(M, dtype=np.int64)
     nn, mm = _i64(n), _i64(m)
-    _check(lib.oracle_binsort(d, _ptr(nn), _ptr(mm), M, xa, int(w_col), int(col_step), _ptr(binv), _ptr(counts),
-                              _ptr(perm)), "binsort")
+    _check(lib.oracle_binsort(d, _ptr(nn), _ptr(mm), M, xa, _ptr(binv), _ptr(counts), _ptr(perm)), "binsort")
     return binv, counts, perm
 
 

@@ -1,14 +1,19 @@
 """Full-size parity: every benchmark configuration at its real size, run through the C ABI in
 the launch configuration the benchmark times (one plan: setpts, type 1, adjoint type 2).
 
-The oracle cannot form these transforms whole in seconds, so outputs are compared on samples
-it computes one by one:
+Whole outputs are compared with the oracle NUFFT (eqs. (7)-(12), relative l2 over all modes and
+all points, cuFINUFFT page Sec. IV-C) for every configuration whose oracle grid fits in seconds:
+the oracle's spreading and interpolation run in their parallel forms, which equal the serial
+loops bit for bit.  The 256^3 fp64 configuration (2^27 points, w = 10: 1.3e11 cell updates per
+transform) is compared on samples the oracle computes one by one:
   * type 1: chosen modes, by eq. (9) at those frequencies with eq. (7) inserted (the oracle's
-    type1_at) -- the same approximation as the library, to 1e-5 (fp32) / 1e-10 (fp64);
-  * type 2: chosen points, interpolated from the oracle's full fine grid (eqs. (11), (12));
-  * both against the exact sums (eqs. (1), (3)) at a few outputs, within 10 eps.
+    type1_at) -- the same approximation as the library;
+  * type 2: 4096 chosen points, interpolated from the oracle's full fine grid (eqs. (11), (12)).
+Every configuration is also checked against the exact sums (eqs. (1), (3)) at a few outputs,
+within 10 eps.
 """
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -59,22 +64,24 @@ def _sample_points(M, count, rng):
 
 
 CONFIGS = [
-    ("2d_n1024_m4m_f32_e5", 48, 48),
-    ("2d_n1024_m4m_f64_e12", 24, 48),
-    ("3d_n128_m16m_f32_e2", 32, 48),
-    ("3d_n128_m16m_f32_e5", 24, 48),
-    ("3d_n128_m16m_f32_e5_cluster", 24, 48),
-    ("3d_n256_m134m_f64_e9", 8, 24),
-    ("1d_n1m_m16m_f32_e6", 48, 48),
-    ("1d_n1m_m16m_f64_e6", 48, 48),
+    # name, whole outputs?, sampled modes, sampled points
+    ("2d_n1024_m4m_f32_e5", True, 0, 0),
+    ("2d_n1024_m4m_f64_e12", True, 0, 0),
+    ("3d_n128_m16m_f32_e2", True, 0, 0),
+    ("3d_n128_m16m_f32_e5", True, 0, 0),
+    ("3d_n128_m16m_f32_e5_cluster", True, 0, 0),
+    ("3d_n256_m134m_f64_e9", False, 12, 4096),
+    ("1d_n1m_m16m_f32_e6", True, 0, 0),
+    ("1d_n1m_m16m_f64_e6", True, 0, 0),
 ]
 
 
-@pytest.mark.parametrize("name,nmodes,npts", CONFIGS, ids=[c[0] for c in CONFIGS])
-def test_full_size_config(nf, orc, name, nmodes, npts):
+@pytest.mark.parametrize("name,whole,nmodes,npts", CONFIGS, ids=[c[0] for c in CONFIGS])
+def test_full_size_config(nf, orc, name, whole, nmodes, npts):
     wl = WORKLOADS[name]
     print(f"full-size {name}: N={wl.N} M={wl.M} {wl.precision} eps={wl.eps} {wl.dist}", flush=True)
     sys.stdout.flush()
+    t0 = time.perf_counter()
     inp = make_inputs(wl)
     X, c, f = inp["X"], inp["c"], inp["f"]
     cd = cdtype(wl.precision)
@@ -93,22 +100,35 @@ def test_full_size_config(nf, orc, name, nmodes, npts):
     del Xd, c_d, f_d, f_out, c_out
     plan.destroy()
     torch.cuda.empty_cache()
-
-    rng = np.random.default_rng(7)
-    sel_k = _sample_modes(wl.N, nmodes, rng)
-    sel_j = _sample_points(wl.M, npts, rng)
+    print(f"  inputs + GPU pair: {time.perf_counter() - t0:.1f} s", flush=True)
     tol = tol_for(wl.precision)
+    rng = np.random.default_rng(7)
 
-    # type 1 at chosen modes vs the oracle's same approximation
-    ref1 = orc.nufft_type1_at(X, c, wl.N, wl.eps, sel_k)
-    e1 = orc.rel_l2(f_gpu[sel_k], ref1)
-    print(f"  type1 vs oracle at {len(sel_k)} modes: {e1:.2e}", flush=True)
+    if whole:
+        t1 = time.perf_counter()
+        ref1 = orc.nufft_type1(X, c, wl.N, wl.eps).ravel()
+        e1 = orc.rel_l2(f_gpu, ref1)
+        print(f"  type1 vs oracle, all {f_gpu.size} modes: {e1:.2e} ({time.perf_counter() - t1:.1f} s)", flush=True)
+        del ref1
+        t1 = time.perf_counter()
+        ref2 = orc.nufft_type2(X, f, wl.N, wl.eps)
+        e2 = orc.rel_l2(c_gpu, ref2)
+        print(f"  type2 vs oracle, all {c_gpu.size} points: {e2:.2e} ({time.perf_counter() - t1:.1f} s)", flush=True)
+        del ref2
+        sel_k = _sample_modes(wl.N, 4, rng)
+        sel_j = _sample_points(wl.M, 4, rng)
+    else:
+        sel_k = _sample_modes(wl.N, nmodes, rng)
+        sel_j = _sample_points(wl.M, npts, rng)
+        t1 = time.perf_counter()
+        ref1 = orc.nufft_type1_at(X, c, wl.N, wl.eps, sel_k)
+        e1 = orc.rel_l2(f_gpu[sel_k], ref1)
+        print(f"  type1 vs oracle at {len(sel_k)} modes: {e1:.2e} ({time.perf_counter() - t1:.1f} s)", flush=True)
+        t1 = time.perf_counter()
+        ref2 = orc.nufft_type2_at(X, f, wl.N, wl.eps, sel_j)
+        e2 = orc.rel_l2(c_gpu[sel_j], ref2)
+        print(f"  type2 vs oracle at {len(sel_j)} points: {e2:.2e} ({time.perf_counter() - t1:.1f} s)", flush=True)
     assert e1 <= tol, e1
-
-    # type 2 at chosen points vs the oracle's fine grid
-    ref2 = orc.nufft_type2_at(X, f, wl.N, wl.eps, sel_j)
-    e2 = orc.rel_l2(c_gpu[sel_j], ref2)
-    print(f"  type2 vs oracle at {len(sel_j)} points: {e2:.2e}", flush=True)
     assert e2 <= tol, e2
 
     # a few outputs against the exact sums, within 10 eps

@@ -56,6 +56,57 @@ SORT_CASES = [
 ]
 
 
+def _grid_t(x, n):
+    """t = (x + pi) n / (2 pi) in fp64 as two rounded operations, folded once into [0, n) (the
+    documented coordinate rule of nufft_get_sort); returns (t, l)."""
+    s = np.float64(n) / (2.0 * np.float64(math.pi))
+    t = (np.asarray(x, dtype=np.float64) + np.float64(math.pi)) * s
+    l = np.floor(t)
+    hi, lo = l >= n, l < 0
+    t = np.where(hi, t - n, np.where(lo, t + n, t))
+    l = np.where(hi, l - n, np.where(lo, l + n, l))
+    return t, l.astype(np.int64)
+
+
+def _documented_inbin_key(X, info):
+    """The in-bin key nufft_get_sort documents for plans with a column order (w, s): the block
+    (c2 // s) ceil((m1 + 1) / s) + c1 // s of the support start c_i = ceil(t_i - w/2) - (b_i m_i -
+    floor(w/2)), then the z start c3.  Computed here from the header's description alone."""
+    w, step = info["colw"], info["colstep"]
+    m, n = info["bins"], info["n"]
+    c = []
+    for i in range(3):
+        t, l = _grid_t(X[i], n[i])
+        b = l // m[i]
+        c.append(np.ceil(t - 0.5 * w).astype(np.int64) - (b * m[i] - w // 2))
+    ncx = -(-(m[0] + 1) // step)
+    return ((c[1] // step) * ncx + c[0] // step) * (m[2] + 1) + c[2]
+
+
+def _check_sort(info, X, perm, counts, sub, orc):
+    """Counts and subproblem rows bit-exact against the oracle; every bin's slice of the
+    permutation holds exactly the oracle's points of that bin; the order inside a bin is the
+    documented one (increasing original index, or for column-order plans the documented key then
+    the original index).  Several in-bin orders are valid; the oracle fixes only the set."""
+    _, ocounts, operm = orc.binsort(X, info["n"], info["bins"])
+    np.testing.assert_array_equal(counts, ocounts)
+    osub = orc.subproblems(ocounts, info["cap"])
+    np.testing.assert_array_equal(sub, osub)
+    off = np.concatenate([[0], np.cumsum(ocounts)])
+    assert perm.size == operm.size
+    for b in np.nonzero(ocounts)[0]:
+        a, e = off[b], off[b + 1]
+        np.testing.assert_array_equal(np.sort(perm[a:e]), operm[a:e])
+    # in-bin order
+    if info["colw"] > 0:
+        key = _documented_inbin_key(X, info)[perm]
+    else:
+        key = np.zeros(perm.size, dtype=np.int64)
+    binpos = np.repeat(np.arange(ocounts.size), ocounts)
+    order = np.lexsort((perm, key, binpos))
+    np.testing.assert_array_equal(order, np.arange(perm.size))
+
+
 @pytest.mark.parametrize("name,wl", SORT_CASES, ids=[c[0] for c in SORT_CASES])
 @pytest.mark.parametrize("cap", [0, 37])
 def test_binsort_bit_exact(nf, orc, name, wl, cap):
@@ -66,34 +117,33 @@ def test_binsort_bit_exact(nf, orc, name, wl, cap):
     p.setpts(*[to_dev(x) for x in X])
     info = p.info()
     perm, counts, sub = [t.cpu().numpy().astype(np.int64) for t in p.get_sort()]
-    _, ocounts, operm = orc.binsort(X, info["n"], info["bins"], w_col=info["colw"],
-                                    col_step=info["colstep"])
-    np.testing.assert_array_equal(counts, ocounts)
-    np.testing.assert_array_equal(perm, operm)
     if cap > 0:
         assert info["cap"] == cap
-    osub = orc.subproblems(ocounts, info["cap"])
-    np.testing.assert_array_equal(sub, osub)
+    _check_sort(info, X, perm, counts, sub, orc)
     p.destroy()
 
 
 def test_binsort_boundary_points(nf, orc):
-    """Coordinates at -pi, just below pi, values that round to pi in fp32, and the fold range."""
+    """Coordinates at -pi, just below pi, values that round to pi in fp32, the fold range
+    [-3 pi, -pi) and [pi, 3 pi), and nextafter(-pi, -inf), whose folded t rounds to n."""
     N = (32, 24)
     xs = np.array([-math.pi, np.nextafter(math.pi, 0), math.pi - 1e-9, 0.0, 1e-30, -1e-30,
-                   -2.9 * math.pi, 2.5 * math.pi, math.pi, -math.pi + 1e-7])
-    ys = np.array([0.1, -0.2, math.pi - 1e-12, -math.pi, 3.0, -3.0, 0.0, 0.0, 1.0, 2.9])
+                   -2.9 * math.pi, 2.5 * math.pi, math.pi, -math.pi + 1e-7, np.nextafter(-math.pi, -4.0),
+                   3 * math.pi - 1e-9, -3 * math.pi])
+    ys = np.array([0.1, -0.2, math.pi - 1e-12, -math.pi, 3.0, -3.0, 0.0, 0.0, 1.0, 2.9, 0.5, -1.5,
+                   np.nextafter(-math.pi, -4.0)])
     for prec, dt in (("f32", np.float32), ("f64", np.float64)):
-        X = [xs.astype(dt), ys.astype(dt)]
-        p = nf.Plan(1, N, 1e-6, prec)
-        p.setpts(*[to_dev(x) for x in X])
-        info = p.info()
-        perm, counts, _ = [t.cpu().numpy().astype(np.int64) for t in p.get_sort()]
-        _, ocounts, operm = orc.binsort(X, info["n"], info["bins"], w_col=info["colw"],
-                                        col_step=info["colstep"])
-        np.testing.assert_array_equal(counts, ocounts)
-        np.testing.assert_array_equal(perm, operm)
-        p.destroy()
+        for N3 in (None, 20):
+            X = [xs.astype(dt), ys.astype(dt)]
+            NN = N if N3 is None else N + (N3,)
+            if N3 is not None:
+                X.append(np.roll(xs, 3).astype(dt))
+            p = nf.Plan(1, NN, 1e-6, prec)
+            p.setpts(*[to_dev(x) for x in X])
+            info = p.info()
+            perm, counts, sub = [t.cpu().numpy().astype(np.int64) for t in p.get_sort()]
+            _check_sort(info, X, perm, counts, sub, orc)
+            p.destroy()
 
 
 def test_setpts_rejects_bad_points(nf):

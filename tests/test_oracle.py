@@ -219,9 +219,18 @@ def test_spread_and_interp_match_bruteforce(oracle_mod, n, w):
     beta = 2.30 * w
     M = 23
     X = _uniform_points(rng, len(n), M)
-    # include points at the ends of the periodic box
+    # include points at the ends of the periodic box, and points in the folded ranges
+    # [pi, 3 pi) and [-3 pi, -pi), which the method maps back by one period (values off the grid
+    # points: where t - w/2 is an integer the support is a tie of two equal endpoint weights,
+    # and which end a rounding picks is not fixed by eq. (8))
     X[0][0] = -math.pi
     X[0][1] = math.pi - 1e-13
+    X[0][2] = math.pi + 1e-3
+    X[0][3] = 2.5 * math.pi + 0.01
+    X[0][4] = -2.2 * math.pi
+    X[0][5] = np.nextafter(-math.pi, -4.0)
+    X[-1][6] = 3 * math.pi - 1e-9
+    X[-1][7] = -3 * math.pi + 0.013
     c = _rand_complex(rng, M)
     P = _brute_psi_per(X, n, w, beta)
     b = oracle_mod.spread(X, c, n, w, beta)
@@ -544,44 +553,55 @@ def test_points_out_of_range_rejected(oracle_mod):
         oracle_mod.spread([np.array([np.nan]), np.array([0.0])], np.array([1 + 0j]), (16, 16), 4, 9.2)
 
 
-@pytest.mark.parametrize("step", [1, 2, 3, 4])
-def test_bins_column_order_within_bins(oracle_mod, step):
-    """3D column order: perm is numpy's stable lexsort by (bin, support-column block, z start), the
-    block of a point being (c_2 // s) ceil((m1 + 1) / s) + c_1 // s with c = l0 - o, l0 the
-    kernel-support start (computed here in extended precision), o the bin's padded origin and s
-    the step."""
-    n = (32, 24, 20)
-    m = (8, 8, 4)
-    w = 6
-    rng = _rng(12)
-    X = [rng.uniform(-math.pi, math.pi, 4000) for _ in range(3)]
-    binv, counts, perm = oracle_mod.binsort(X, n, m, w_col=w, col_step=step)
-    binv0, counts0, perm0 = oracle_mod.binsort(X, n, m)
-    np.testing.assert_array_equal(binv, binv0)
-    np.testing.assert_array_equal(counts, counts0)
-    nb0, nb1 = (n[0] + m[0] - 1) // m[0], (n[1] + m[1] - 1) // m[1]
-    bidx = [binv % nb0, (binv // nb0) % nb1, binv // (nb0 * nb1)]
-    lo = []
+def test_bins_fold_range_cell_interval(oracle_mod):
+    """Coordinates in [pi, 3 pi) and [-3 pi, -pi) fall in the bin of their image in [-pi, pi):
+    with u = (x + pi) n / (2 pi) in extended precision and reduced mod n, the bin's cells contain
+    u (to 1e-9 cells), and the point lands where the same point shifted by a period lands."""
+    n = (40, 24, 18)
+    m = (16, 8, 8)
+    rng = _rng(13)
+    M = 3000
+    X = []
     for i in range(3):
-        t = (np.longdouble(X[i]) + np.longdouble(math.pi)) * n[i] / (2 * np.longdouble(math.pi))
-        l0 = np.ceil(t - w / 2).astype(np.int64)
-        lo.append(l0 - (bidx[i] * m[i] - w // 2))
+        base = rng.uniform(-math.pi, math.pi, M)
+        shift = rng.integers(-1, 2, M) * 2 * math.pi
+        X.append(np.clip(base + shift, -3 * math.pi, np.nextafter(3 * math.pi, 0)))
+    X[0][:4] = [math.pi, -3 * math.pi, np.nextafter(-math.pi, -4.0), 3 * math.pi - 1e-12]
+    binv, counts, perm = oracle_mod.binsort(X, n, m)
+    nb = [(ni + mi - 1) // mi for ni, mi in zip(n, m)]
+    bidx = [binv % nb[0], (binv // nb[0]) % nb[1], binv // (nb[0] * nb[1])]
     for i in range(3):
-        assert lo[i].min() >= 0 and lo[i].max() <= m[i]
-    ncx = -(-(m[0] + 1) // step)
-    col = (lo[1] // step) * ncx + lo[0] // step
-    expect = np.lexsort((np.arange(4000), lo[2], col, binv))
-    np.testing.assert_array_equal(perm, expect)
-    # 2D: the block of the support start, then the original index
-    b2, _, p2 = oracle_mod.binsort(X[:2], n[:2], m[:2], w_col=w, col_step=step)
-    nb0 = (n[0] + m[0] - 1) // m[0]
-    lo2 = []
-    for i in range(2):
-        t = (np.longdouble(X[i]) + np.longdouble(math.pi)) * n[i] / (2 * np.longdouble(math.pi))
-        bi = b2 % nb0 if i == 0 else b2 // nb0
-        lo2.append(np.ceil(t - w / 2).astype(np.int64) - (bi * m[i] - w // 2))
-    col2 = (lo2[1] // step) * ncx + lo2[0] // step
-    np.testing.assert_array_equal(p2, np.lexsort((np.arange(4000), col2, b2)))
-    # 1D ignores the column order
-    _, _, p1 = oracle_mod.binsort(X[:1], n[:1], m[:1], w_col=w)
-    np.testing.assert_array_equal(p1, np.argsort(oracle_mod.binsort(X[:1], n[:1], m[:1])[0], kind="stable"))
+        u = (np.longdouble(X[i]) + np.longdouble(math.pi)) * n[i] / (2 * np.longdouble(math.pi))
+        u = u - n[i] * np.floor(u / n[i])
+        lo = bidx[i] * m[i]
+        hi = np.minimum(lo + m[i], n[i])
+        near_top = u > n[i] - 1e-9        # images that round onto the period's end
+        ok = ((u >= lo - 1e-9) & (u < hi + 1e-9)) | (near_top & (hi == n[i]))
+        assert ok.all(), i
+    np.testing.assert_array_equal(perm, np.argsort(binv, kind="stable"))
+    np.testing.assert_array_equal(counts, np.bincount(binv, minlength=int(np.prod(nb))))
+
+
+@pytest.mark.parametrize("n,w,dist", [((64,), 7, "u"), ((5,), 7, "u"), ((30, 20), 6, "u"), ((7, 9), 13, "u"),
+                                      ((16, 12, 10), 6, "u"), ((12, 8, 6), 10, "u"), ((4, 4, 4), 5, "u"),
+                                      ((32, 24, 20), 6, "box")])
+def test_parallel_spread_interp_equal_serial(oracle_mod, n, w, dist):
+    """The parallel spreading (slab-owned) and interpolation (point-parallel) forms return the
+    serial loops' results bit for bit, on grids larger and smaller than the kernel, with folded
+    coordinates, for any thread count."""
+    rng = _rng(17)
+    d = len(n)
+    M = 2500
+    if dist == "box":
+        X = [rng.uniform(0.0, 0.5, M) for _ in range(d)]
+    else:
+        X = [rng.uniform(-math.pi, math.pi, M) for _ in range(d)]
+        X[0][:3] = [2.5 * math.pi, -2.9 * math.pi, np.nextafter(-math.pi, -4.0)]
+    c = _rand_complex(rng, M)
+    beta = 2.30 * w
+    ref = oracle_mod.spread(X, c, n, w, beta, threads=1)
+    g = _rand_complex(rng, tuple(reversed(n)))
+    ref2 = oracle_mod.interp(X, g, w, beta, threads=1)
+    for th in (2, 3, 7, 0):
+        np.testing.assert_array_equal(oracle_mod.spread(X, c, n, w, beta, threads=th), ref)
+        np.testing.assert_array_equal(oracle_mod.interp(X, g, w, beta, threads=th), ref2)
