@@ -110,8 +110,10 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
  * Set the nonuniform points (Sec. III-A bin-sort and subproblems).
  *   M        number of points, 0 <= M <= 2^31 - 1.
  *   x, y, z  device arrays of M coordinates (z is NULL for dim 2; y and z for dim 1).  Values must be
- *            finite and in [-3pi, 3pi) (one periodic fold is applied), else
- *            NUFFT_ERR_POINTS and the plan keeps no points.
+ *            finite and within one period of [-pi, pi), i.e. about [-3pi, 3pi) (one periodic
+ *            fold is applied); exactly, t = (x + pi) n / (2 pi) (two rounded fp64 operations)
+ *            must satisfy -n <= floor(t) < 2n, so values at the very ends of that range may be
+ *            rejected by rounding.  Otherwise NUFFT_ERR_POINTS and the plan keeps no points.
  * The library copies what it needs (sorted coordinates, permutation); the caller
  * may reuse x, y, z once the stream has passed this call.  Blocks the host until
  * the sort is done (one small device-to-host read of the subproblem count).

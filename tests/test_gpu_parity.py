@@ -129,7 +129,7 @@ def test_binsort_boundary_points(nf, orc):
     N = (32, 24)
     xs = np.array([-math.pi, np.nextafter(math.pi, 0), math.pi - 1e-9, 0.0, 1e-30, -1e-30,
                    -2.9 * math.pi, 2.5 * math.pi, math.pi, -math.pi + 1e-7, np.nextafter(-math.pi, -4.0),
-                   3 * math.pi - 1e-9, -3 * math.pi])
+                   3 * math.pi - 1e-9, -3 * math.pi + 1e-9])
     ys = np.array([0.1, -0.2, math.pi - 1e-12, -math.pi, 3.0, -3.0, 0.0, 0.0, 1.0, 2.9, 0.5, -1.5,
                    np.nextafter(-math.pi, -4.0)])
     for prec, dt in (("f32", np.float32), ("f64", np.float64)):
@@ -148,7 +148,8 @@ def test_binsort_boundary_points(nf, orc):
 
 def test_setpts_rejects_bad_points(nf):
     p = nf.Plan(1, (16, 16), 1e-5, "f32")
-    for bad in (np.nan, np.inf, 20.0, -10.0):
+    # -3 pi itself scales to t = -n minus a rounding, below the accepted floor(t) >= -n
+    for bad in (np.nan, np.inf, 20.0, -10.0, -3 * math.pi):
         x = np.array([0.0, bad, 1.0], np.float32)
         y = np.zeros(3, np.float32)
         with pytest.raises(nf.NufftError) as ei:
