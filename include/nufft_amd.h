@@ -248,6 +248,18 @@ int nufft_precorrect_pad(nufft_plan plan, const void* f, void* fhat);
  */
 int nufft_get_sort(nufft_plan plan, int32_t* perm, int32_t* counts, int32_t* subproblems);
 
+/*
+ * Number of kernel-support starts that any spreading or interpolation launch on this plan (or,
+ * for a type 3 plan, its inner plans) found outside the padded tile of the point's subproblem
+ * since the plan was created, written to *count (host).  The bin-sort places every point so
+ * that its support starts inside its bin's padded tile (the bin holds floor(t) and the support
+ * starts at ceil(t - w/2), Sec. III-A with the kernel of eq. (8)); the kernels check this and
+ * clamp a start that is outside, counting it here instead of accessing memory out of bounds.
+ * A nonzero count means results are wrong.  Synchronises the plan's stream.
+ * NUFFT_ERR_BAD_ARG for a NULL plan or count.
+ */
+int nufft_get_range_errors(nufft_plan plan, int64_t* count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,7 @@ SIGNATURES = {
     "nufft_deconvolve": (_I, [_P, _P, _P]),
     "nufft_precorrect_pad": (_I, [_P, _P, _P]),
     "nufft_get_sort": (_I, [_P, _P, _P, _P]),
+    "nufft_get_range_errors": (_I, [_P, ctypes.POINTER(_L)]),
 }
 
 NUFFT_OK = 0
@@ -319,6 +320,13 @@ class Plan:
             self._h, ctypes.c_void_p(perm.data_ptr() if perm.numel() else 0),
             ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(sub.data_ptr() if sub.numel() else 0)))
         return perm, counts, sub
+
+    def range_errors(self) -> int:
+        """Kernel-support starts found outside their padded tile since plan creation (0 when the
+        sort and the kernels agree; see nufft_get_range_errors)."""
+        v = ctypes.c_int64()
+        self._check(self._lib.nufft_get_range_errors(self._h, ctypes.byref(v)))
+        return int(v.value)
 
     def stage_times(self):
         """ms per step (needs timing=True): sort, spread, type-1 FFT, deconvolve, clear,

@@ -153,8 +153,7 @@ __global__ void __launch_bounds__((kInterpSmBlock<T, DIM, W>)) k_interp_sm(GeomA
             double t = grid_t((double)xc[d], g.s[d]);
             int l;
             fold_t(t, g.n[d], l);
-            int v = es_weights<T, W>(t, beta, ker[d]) - origin[d];
-            l0[d] = min(max(v, 0), pd[d] - W);
+            l0[d] = checked_start(es_weights<T, W>(t, beta, ker[d]) - origin[d], pd[d] - W, g.range_err);
         }
         T are = 0, aim = 0;
         if constexpr (DIM == 1) {

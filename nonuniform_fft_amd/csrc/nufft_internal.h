@@ -145,6 +145,18 @@ __device__ __forceinline__ int es_weights(double t, T beta, T* phi) {
 
 template <typename T> struct cplx { T re, im; };
 
+// A kernel-support start l0 inside a padded tile must lie in [0, hi]; the bin-sort and the
+// kernels place every point so that it does.  A start outside is counted in *err (a plan-owned
+// counter the tests read back) and clamped, so a disagreement shows up as a count instead of
+// as an out-of-bounds access.
+__device__ __forceinline__ int checked_start(int l0, int hi, unsigned int* err) {
+    if (l0 < 0 || l0 > hi) {
+        atomicAdd(err, 1u);
+        l0 = min(max(l0, 0), hi);
+    }
+    return l0;
+}
+
 // ------------------------------------------------------------------------------------------------
 // Plan
 // ------------------------------------------------------------------------------------------------
@@ -196,6 +208,7 @@ struct nufft_plan_s {
     nufft::DevBuf counts;               // int32[nbins]
     nufft::DevBuf offsets;              // int32[nbins + 1]
     nufft::DevBuf sub;                  // int32[3 * nsub] (bin, start, len)
+    nufft::DevBuf range_err;            // unsigned int: stencil starts found outside their tile
     nufft::DevBuf sort_tmp;             // radix-sort scratch
     size_t sort_tmp_cap = 0;
     size_t pts_cap = 0;                 // capacity (points) of xs / perm
@@ -319,6 +332,9 @@ struct GeomArgs {
     // grid + v gvs (strides in complex values; nv = 1 for a single transform)
     int nv;
     int64_t cvs, gvs;
+    // count of stencil starts found outside their subproblem's padded tile (clamped; the sort and
+    // the kernels agree on every bin, so this stays 0)
+    unsigned int* range_err;
 };
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // columns: the points of each bin are in column order (3D), so the column-run kernel may run.

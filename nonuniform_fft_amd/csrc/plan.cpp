@@ -244,6 +244,7 @@ nufft::GeomArgs geom(const nufft_plan p) {
     g.nv = 1;
     g.cvs = std::max<int64_t>(p->M, 0);
     g.gvs = grid_cells(p);
+    g.range_err = (unsigned int*)p->range_err.p;
     return g;
 }
 
@@ -473,7 +474,8 @@ int nufft_destroy(nufft_plan plan) {
     if (plan->t3_spread) nufft_destroy(plan->t3_spread);
     if (plan->t3_eval) nufft_destroy(plan->t3_eval);
     for (DevBuf* b : {&plan->grid, &plan->grid2, &plan->grid_many2, &plan->pcorr, &plan->fft_work, &plan->xs, &plan->perm, &plan->counts,
-                      &plan->offsets, &plan->sub, &plan->sort_tmp, &plan->grid_many, &plan->c_many, &plan->t3_part,
+                      &plan->offsets, &plan->sub, &plan->range_err, &plan->sort_tmp, &plan->grid_many, &plan->c_many,
+                      &plan->t3_part,
                       &plan->t3_y, &plan->t3_theta, &plan->t3_pre, &plan->t3_post, &plan->t3_cp, &plan->t3_cin,
                       &plan->t3_tab})
         dev_free(plan, *b);
@@ -627,6 +629,20 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
         }
         if (e != hipSuccess) {
             hip_fail(plan, e, "hipMemcpy correction factors");
+            nufft_destroy(plan);
+            return NUFFT_ERR_HIP;
+        }
+    }
+
+    // counter of kernel-support starts found outside their padded tile (nufft_get_range_errors)
+    if ((rc = dev_alloc(plan, plan->range_err, 256, "range-error counter")) != NUFFT_OK) {
+        nufft_destroy(plan);
+        return rc;
+    }
+    {
+        hipError_t e = hipMemset(plan->range_err.p, 0, 256);
+        if (e != hipSuccess) {
+            hip_fail(plan, e, "hipMemset range-error counter");
             nufft_destroy(plan);
             return NUFFT_ERR_HIP;
         }
@@ -1031,6 +1047,30 @@ int nufft_get_sort(nufft_plan plan, int32_t* perm, int32_t* counts, int32_t* sub
     if (subproblems && plan->nsub > 0)
         NUFFT_HIP(hipMemcpyAsync(subproblems, plan->sub.p, sizeof(int32_t) * 3 * plan->nsub,
                                  hipMemcpyDeviceToDevice, plan->stream));
+    return NUFFT_OK;
+}
+
+int nufft_get_range_errors(nufft_plan plan, int64_t* count) {
+    if (!plan || !count) return NUFFT_ERR_BAD_ARG;
+    *count = 0;
+    if (plan->type == 3) {
+        // the transform's spreading and evaluation run in its inner plans
+        for (nufft_plan q : {plan->t3_spread, plan->t3_eval}) {
+            int64_t v = 0;
+            if (q) {
+                int rc = nufft_get_range_errors(q, &v);
+                if (rc != NUFFT_OK) return fail(plan, rc, q->last_error);
+            }
+            *count += v;
+        }
+        return NUFFT_OK;
+    }
+    unsigned int v = 0;
+    if (plan->range_err.p) {
+        NUFFT_HIP(hipMemcpyAsync(&v, plan->range_err.p, sizeof(v), hipMemcpyDeviceToHost, plan->stream));
+        NUFFT_HIP(hipStreamSynchronize(plan->stream));
+    }
+    *count = (int64_t)v;
     return NUFFT_OK;
 }
 

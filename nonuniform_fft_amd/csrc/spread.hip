@@ -124,8 +124,7 @@ k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c, cplx<T>* __restrict__ gri
             int l;
             fold_t(tt, g.n[i], l);
             T ker[W];
-            int l0 = es_weights<T, W>(tt, beta, ker) - origin[i];
-            l0 = min(max(l0, 0), pd[i] - W);
+            const int l0 = checked_start(es_weights<T, W>(tt, beta, ker) - origin[i], pd[i] - W, g.range_err);
             if (i < 2) {
 #pragma unroll
                 for (int q = 0; q < W; ++q) st->kxy[p][i][q] = ker[q];
@@ -402,8 +401,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
             int l;
             fold_t(tt, g.n[si], l);
             T ker[W];
-            l0 = es_weights<T, W>(tt, beta, ker) - origin[si];
-            l0 = min(max(l0, 0), pd[si] - W);
+            l0 = checked_start(es_weights<T, W>(tt, beta, ker) - origin[si], pd[si] - W, g.range_err);
             if (si < 2) {
                 // x or y: the block index, and the weights placed in the block's window
                 const int blk = l0 / S;
@@ -625,8 +623,9 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
                 phi = (zz <= 1.0f) ? __expf(beta * (__builtin_amdgcn_sqrtf(1.0f - zz) - 1.0f)) : 0.0f;
             else
                 phi = (zz <= (T)1) ? exp_es(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
-            int l0 = (int)l0d - origin[d_];
-            l0 = min(max(l0, 0), pd[d_] - W);
+            // the start is checked once per (point, dimension), by its q = 0 item
+            const int l0 = (q_ == 0) ? checked_start((int)l0d - origin[d_], pd[d_] - W, g.range_err)
+                                     : min(max((int)l0d - origin[d_], 0), pd[d_] - W);
             if (d_ < 2) {
                 const int blk = l0 / S;
                 const int off = l0 - blk * S;
@@ -834,8 +833,7 @@ __global__ void __launch_bounds__(kSpread1Block) k_spread_sm1(GeomArgs g, const 
         int l;
         fold_t(t, g.n[0], l);
         T ker[W];
-        int l0 = es_weights<T, W>(t, beta, ker) - origin;
-        l0 = min(max(l0, 0), p1 - W);
+        const int l0 = checked_start(es_weights<T, W>(t, beta, ker) - origin, p1 - W, g.range_err);
 #pragma unroll
         for (int q = 0; q < W; ++q) {
             atomicAdd(tre + l0 + q, (double)(cv.re * ker[q]));

@@ -95,6 +95,7 @@ def test_full_size_config(nf, orc, name, whole, nmodes, npts):
     plan.execute(c_d, f_out)
     plan.execute_adjoint(c_out, f_d)
     torch.cuda.synchronize()
+    assert plan.range_errors() == 0
     f_gpu = f_out.cpu().numpy().ravel()
     c_gpu = c_out.cpu().numpy()
     del Xd, c_d, f_d, f_out, c_out

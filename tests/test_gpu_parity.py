@@ -129,7 +129,7 @@ def test_binsort_boundary_points(nf, orc):
     N = (32, 24)
     xs = np.array([-math.pi, np.nextafter(math.pi, 0), math.pi - 1e-9, 0.0, 1e-30, -1e-30,
                    -2.9 * math.pi, 2.5 * math.pi, math.pi, -math.pi + 1e-7, np.nextafter(-math.pi, -4.0),
-                   3 * math.pi - 1e-9, -3 * math.pi + 1e-9])
+                   3 * math.pi - 1e-5, -3 * math.pi + 1e-5])
     ys = np.array([0.1, -0.2, math.pi - 1e-12, -math.pi, 3.0, -3.0, 0.0, 0.0, 1.0, 2.9, 0.5, -1.5,
                    np.nextafter(-math.pi, -4.0)])
     for prec, dt in (("f32", np.float32), ("f64", np.float64)):
@@ -143,6 +143,15 @@ def test_binsort_boundary_points(nf, orc):
             info = p.info()
             perm, counts, sub = [t.cpu().numpy().astype(np.int64) for t in p.get_sort()]
             _check_sort(info, X, perm, counts, sub, orc)
+            # the points at the period's ends (folded t rounding onto n) keep their stencils
+            # inside their tiles in both directions
+            cd = cdtype(prec)
+            f = torch.empty(tuple(reversed(NN)), dtype=cd, device=dev())
+            cc = torch.empty(len(xs), dtype=cd, device=dev())
+            p.execute(torch.ones(len(xs), dtype=cd, device=dev()), f)
+            p.execute_adjoint(cc, f)
+            torch.cuda.synchronize()
+            assert p.range_errors() == 0
             p.destroy()
 
 
@@ -220,6 +229,7 @@ def test_spread_step(nf, orc, wl, method):
     ref = orc.spread(inp["X"], inp["c"], p.n, p.w, p.beta)
     err = orc.rel_l2(grid.cpu().numpy(), ref.ravel())
     assert err <= _step_tol(wl.precision, fp32_atomics=(method in (1, 3))), err
+    assert p.range_errors() == 0
     p.destroy()
 
 
@@ -239,6 +249,7 @@ def test_interp_step(nf, orc, wl, method):
     ref = orc.interp(inp["X"], g.reshape(tuple(reversed(p.n))), p.w, p.beta)
     err = orc.rel_l2(c.cpu().numpy(), ref)
     assert err <= _step_tol(wl.precision), err
+    assert p.range_errors() == 0
     p.destroy()
 
 
