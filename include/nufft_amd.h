@@ -122,6 +122,29 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
 int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z);
 
 /*
+ * nufft_setpts without allocating anything, for callers that cannot allocate memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  No hipMalloc, hipFree
+ * or pinned-host allocation happens in this call.  (It still reads the subproblem count back to
+ * the host and waits for the plan's stream, as nufft_setpts does.)  Results are those of
+ * nufft_setpts on the same points.
+ *   Scratch: the sort's temporaries (key and value ping-pong buffers, digit histograms, scans and
+ *   two result slots: about 16 + dim * sizeof(real) bytes per point plus a little per bin, e.g.
+ *   29 bytes per point in 3D fp32) live in one file-scope device array of
+ *   NUFFT_NOALLOC_SCRATCH_BYTES bytes per GPU, loaded with the library and held until the process
+ *   ends.  A point set that needs more is rejected with NUFFT_ERR_ALLOC (3D fp32: up to about
+ *   2.2 million points; 3D fp64: about 1.6 million).
+ *   Plan buffers: the sorted coordinates, permutation, bin counts and offsets and the subproblem
+ *   list are the plan's own and are not grown here: an earlier nufft_setpts on this plan with at
+ *   least M points (and at least as many subproblems) must have sized them, else NUFFT_ERR_ALLOC.
+ *   Concurrency: every call on one GPU uses that GPU's one scratch array, which keeps the last
+ *   call's contents; calls that overlap in time on one GPU (from other threads or on other
+ *   streams) race, and the caller must serialise them.
+ * Errors: those of nufft_setpts, plus NUFFT_ERR_ALLOC as above (the plan then keeps no points).
+ */
+#define NUFFT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int nufft_setpts_noalloc(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z);
+
+/*
  * Type 3 points: M sources (x, y, z: device arrays, any finite values) and K targets (s, t, u:
  * device arrays of K frequencies, any finite values); unused dimensions NULL.  nufft_execute
  * then maps c (M complex) to f (K complex), f_k ~ sum_j c_j exp(+i (s_k x_j + t_k y_j + u_k z_j)).

@@ -31,6 +31,7 @@ SIGNATURES = {
     "nufft_plan_create": (_I, [_I, _I, ctypes.POINTER(_L), _D, _I, _P, ctypes.POINTER(NufftOpts),
                                ctypes.POINTER(_P)]),
     "nufft_setpts": (_I, [_P, _L, _P, _P, _P]),
+    "nufft_setpts_noalloc": (_I, [_P, _L, _P, _P, _P]),
     "nufft_setpts_type3": (_I, [_P, _L, _P, _P, _P, _L, _P, _P, _P]),
     "nufft_execute": (_I, [_P, _P, _P]),
     "nufft_execute_adjoint": (_I, [_P, _P, _P]),

@@ -367,6 +367,13 @@ __global__ void __launch_bounds__(kScatBlock) k_radix_scatter(const int32_t* __r
         emit([&](int r, int p) { bt[p] = cvs[r][d]; }, [&](int64_t o, int i) { pl.out[d][o] = bt[i]; });
 }
 
+// Clears n 32-bit words (small flags and counters: a kernel rather than a memset, so that a
+// captured stream records no memset node).
+__global__ void k_zero_words(uint32_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 __global__ void k_iota(int32_t* __restrict__ v, int64_t M) {
     int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j < M) v[j] = (int32_t)j;
@@ -471,6 +478,12 @@ hipError_t scatter_dim(int dim, const int32_t* ki, const int32_t* vi, int32_t* k
 
 size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec) { return layout(M, nbins, dim, prec).end; }
 
+hipError_t launch_zero_words(void* p, int64_t nwords, hipStream_t st) {
+    if (nwords <= 0) return hipSuccess;
+    k_zero_words<<<dim3((unsigned)cdiv(nwords, kBlock)), kBlock, 0, st>>>((uint32_t*)p, nwords);
+    return hipGetLastError();
+}
+
 hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int32_t* offsets,
                        void* xs_out, void* scratch, size_t scratch_bytes, int64_t* nsub_dev,
                        int* bad_dev, hipStream_t st) {
@@ -544,14 +557,13 @@ hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int
         k_bin_offsets<<<dim3((unsigned)cdiv(M + 1, kBlock)), kBlock, 0, st>>>(ki, M, a.nbins,
                                                                                make_fastdiv(std::max(a.ncol, 1)), offsets);
     } else {
-        if ((e = hipMemsetAsync(offsets, 0, sizeof(int32_t) * (a.nbins + 1), st)) != hipSuccess)
-            return e;
+        if ((e = launch_zero_words(offsets, (int64_t)a.nbins + 1, st)) != hipSuccess) return e;
     }
     k_counts_nsub<<<dim3((unsigned)cdiv(a.nbins, kBlock)), kBlock, 0, st>>>(offsets, a.nbins, a.cap,
                                                                           counts, nsp);
     if ((e = exclusive_scan(nsp, first, a.nbins, stmp, st)) != hipSuccess) return e;
     // total number of subproblems = first[nbins]; widen to int64 for the host read-back
-    if ((e = hipMemsetAsync(nsub_dev, 0, sizeof(int64_t), st)) != hipSuccess) return e;
+    if ((e = launch_zero_words(nsub_dev, 2, st)) != hipSuccess) return e;
     if ((e = hipMemcpyAsync(nsub_dev, first + a.nbins, sizeof(int32_t), hipMemcpyDeviceToDevice,
                             st)) != hipSuccess)
         return e;

@@ -297,6 +297,8 @@ struct SortArgs {
 };
 // Bytes of scratch the sort needs for M points and the plan's bin count.
 size_t sort_scratch_bytes(int64_t M, int nbins, int dim, int prec);
+// Clears nwords 32-bit words with a kernel (no memset node when the stream is captured).
+hipError_t launch_zero_words(void* p, int64_t nwords, hipStream_t st);
 // Runs bin index + radix sort + counts/offsets + subproblem counts.  Writes perm, counts,
 // offsets and the coordinates in sorted order (xs_out: dim arrays of M, plan precision);
 // writes the number of subproblems into *nsub_dev (device int64) and a nonzero value into

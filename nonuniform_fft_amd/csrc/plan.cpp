@@ -436,6 +436,157 @@ int check_points(nufft_plan p) {
     return NUFFT_OK;
 }
 
+// ------------------------------------------------------------------------------------------------
+// setpts (bin-sort and subproblems) with the plan's own scratch, or without allocating
+// ------------------------------------------------------------------------------------------------
+
+// Device scratch of nufft_setpts_noalloc: the sort's temporaries (key / value ping-pong buffers,
+// digit histograms, scans and the two result slots).  One array per GPU, loaded with the library's
+// code and held until the process ends.  In host code `scratch` is only a handle for
+// hipGetSymbolAddress: the device address of each GPU's copy is looked up once per device, with
+// that device current, and kept in g_scratch_ptr.
+constexpr size_t kNoallocScratchBytes = NUFFT_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t noalloc_scratch(int device, void** out) {
+    *out = nullptr;
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != device) (void)hipSetDevice(cur);
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
+// noalloc: sort in the device array above, read the result slots into host stack memory, and
+// require the plan's point buffers (sized by an earlier nufft_setpts) to be large enough.
+int setpts_impl(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z, bool noalloc) {
+    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
+    if (plan->type == 3) return fail(plan, NUFFT_ERR_BAD_ARG, "a type 3 plan takes nufft_setpts_type3");
+    if (M < 0 || M > INT32_MAX) return fail(plan, NUFFT_ERR_BAD_ARG, "M out of range [0, 2^31-1]");
+    const void* X[3] = {x, y, z};
+    if (M > 0)
+        for (int i = 0; i < plan->dim; ++i)
+            if (!X[i]) return fail(plan, NUFFT_ERR_BAD_ARG, "null coordinate array");
+    plan->M = -1;
+    plan->nsub = 0;
+    const size_t rs = real_size(plan);
+    const size_t Mm = (size_t)std::max<int64_t>(M, 1);
+    int rc;
+    const size_t sort_bytes = nufft::sort_scratch_bytes(M, (int)plan->nbins, plan->dim, plan->prec) + 256;
+    char* scr = nullptr;        // sort scratch: the plan's, or the device array
+    size_t scr_bytes = 0;
+    if (noalloc) {
+        if (sort_bytes > kNoallocScratchBytes)
+            return fail(plan, NUFFT_ERR_ALLOC, "nufft_setpts_noalloc: sorting " + std::to_string(M) + " points needs " +
+                                                   std::to_string(sort_bytes) + " bytes of scratch, more than the " +
+                                                   std::to_string(kNoallocScratchBytes) + "-byte no-allocation scratch");
+        if ((size_t)M > plan->pts_cap || plan->counts.bytes < (size_t)plan->nbins * sizeof(int32_t) ||
+            plan->offsets.bytes < (size_t)(plan->nbins + 1) * sizeof(int32_t) || !plan->sort_tmp.p)
+            return fail(plan, NUFFT_ERR_ALLOC, "nufft_setpts_noalloc: the plan's point buffers hold fewer than " +
+                                                   std::to_string(M) +
+                                                   " points; size them with nufft_setpts on at least as many points");
+        void* p = nullptr;
+        NUFFT_HIP(noalloc_scratch(plan->device, &p));
+        scr = (char*)p;
+        scr_bytes = sort_bytes;
+    } else {
+        if ((rc = dev_alloc(plan, plan->xs, Mm * plan->dim * rs, "sorted coordinates")) != NUFFT_OK ||
+            (rc = dev_alloc(plan, plan->perm, Mm * sizeof(int32_t), "permutation")) != NUFFT_OK ||
+            (rc = dev_alloc(plan, plan->counts, (size_t)plan->nbins * sizeof(int32_t), "bin counts")) != NUFFT_OK ||
+            (rc = dev_alloc(plan, plan->offsets, (size_t)(plan->nbins + 1) * sizeof(int32_t), "bin offsets")) != NUFFT_OK ||
+            (rc = dev_alloc(plan, plan->sort_tmp, sort_bytes, "sort scratch")) != NUFFT_OK)
+            return rc;
+        // points the buffers hold (they only grow); the sort scratch also holds the gathered
+        // strengths of fp64 executes, at least M complex values
+        plan->pts_cap = std::min(plan->xs.bytes / (plan->dim * rs), plan->perm.bytes / sizeof(int32_t));
+        if (!plan->host_tail) NUFFT_HIP(hipHostMalloc(&plan->host_tail, 128, hipHostMallocDefault));
+        scr = (char*)plan->sort_tmp.p;
+        scr_bytes = plan->sort_tmp.bytes;
+    }
+    // two small result slots at the end of the scratch: int64 subproblem count, int bad-point flag,
+    // read back into pinned memory (or, without allocation, into host stack memory)
+    char* tail = scr + (scr_bytes - 256);
+    int64_t* nsub_dev = (int64_t*)tail;
+    int* bad_dev = (int*)(tail + 64);
+    alignas(64) unsigned char stack_tail[128];
+    unsigned char* host_tail = noalloc ? stack_tail : (unsigned char*)plan->host_tail;
+
+    begin_group(plan, 4);
+    record(plan, EV_SORT0);
+    NUFFT_HIP(nufft::launch_zero_words(bad_dev, 1, plan->stream));
+    nufft::SortArgs a{};
+    a.dim = plan->dim;
+    a.prec = plan->prec;
+    a.M = M;
+    for (int i = 0; i < 3; ++i) {
+        a.x[i] = i < plan->dim ? X[i] : nullptr;
+        a.n[i] = (int)plan->n[i];
+        a.s[i] = plan->s[i];
+        a.m[i] = plan->m[i];
+        a.nb[i] = plan->nb[i];
+    }
+    a.nbins = (int)plan->nbins;
+    a.nbits = plan->nbits;
+    a.cap = plan->cap;
+    a.colw = plan->colw;
+    a.colstep = plan->colstep;
+    a.ncol = plan->ncol;
+    if (plan->method == NUFFT_METHOD_GM) {
+        // no sort and no binning: the points stay in the caller's order and the bin counts read zero
+        NUFFT_HIP(nufft::launch_fill_zero(plan->counts.p, (size_t)plan->nbins * sizeof(int32_t), plan->stream));
+        NUFFT_HIP(nufft::launch_identity_order(a, (int32_t*)plan->perm.p, plan->xs.p, bad_dev, plan->stream));
+        NUFFT_HIP(hipMemcpyAsync(host_tail, tail, 128, hipMemcpyDeviceToHost, plan->stream));
+        NUFFT_HIP(hipStreamSynchronize(plan->stream));
+        const int host_bad = *(const int*)(host_tail + 64);
+        if (host_bad) return fail(plan, NUFFT_ERR_POINTS, "a coordinate is not finite or outside [-3pi, 3pi)");
+        record(plan, EV_SORT1);
+        end_group(plan, 4);
+        plan->M = M;
+        plan->nsub = 0;
+        return NUFFT_OK;
+    }
+    NUFFT_HIP(nufft::launch_sort(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p, (int32_t*)plan->offsets.p,
+                                 plan->xs.p, scr, scr_bytes - 256, nsub_dev, bad_dev, plan->stream));
+    // one read of both result slots
+    NUFFT_HIP(hipMemcpyAsync(host_tail, tail, 128, hipMemcpyDeviceToHost, plan->stream));
+    NUFFT_HIP(hipStreamSynchronize(plan->stream));
+    const int64_t host_nsub = *(const int64_t*)host_tail;
+    const int host_bad = *(const int*)(host_tail + 64);
+    if (host_bad) return fail(plan, NUFFT_ERR_POINTS, "a coordinate is not finite or outside [-3pi, 3pi)");
+    const size_t sub_bytes = (size_t)std::max<int64_t>(host_nsub, 1) * 3 * sizeof(int32_t);
+    if (noalloc) {
+        if (plan->sub.bytes < sub_bytes)
+            return fail(plan, NUFFT_ERR_ALLOC, "nufft_setpts_noalloc: the plan's subproblem list holds fewer than " +
+                                                   std::to_string(host_nsub) +
+                                                   " subproblems; size it with nufft_setpts on a point set with as many");
+    } else if ((rc = dev_alloc(plan, plan->sub, sub_bytes, "subproblem list")) != NUFFT_OK) {
+        return rc;
+    }
+    NUFFT_HIP(nufft::launch_build_subproblems_from(M, (int)plan->nbins, plan->dim, plan->prec, plan->cap,
+                                                   (const int32_t*)plan->counts.p, (const int32_t*)plan->offsets.p,
+                                                   scr, (int32_t*)plan->sub.p, plan->stream));
+    record(plan, EV_SORT1);
+    end_group(plan, 4);
+    plan->M = M;
+    plan->nsub = host_nsub;
+    return NUFFT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -664,86 +815,11 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
 }
 
 int nufft_setpts(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z) {
-    if (check_plan(plan) != NUFFT_OK) return NUFFT_ERR_BAD_ARG;
-    if (plan->type == 3) return fail(plan, NUFFT_ERR_BAD_ARG, "a type 3 plan takes nufft_setpts_type3");
-    if (M < 0 || M > INT32_MAX) return fail(plan, NUFFT_ERR_BAD_ARG, "M out of range [0, 2^31-1]");
-    const void* X[3] = {x, y, z};
-    if (M > 0)
-        for (int i = 0; i < plan->dim; ++i)
-            if (!X[i]) return fail(plan, NUFFT_ERR_BAD_ARG, "null coordinate array");
-    plan->M = -1;
-    plan->nsub = 0;
-    const size_t rs = real_size(plan);
-    const size_t Mm = (size_t)std::max<int64_t>(M, 1);
-    int rc;
-    size_t sort_bytes = nufft::sort_scratch_bytes(M, (int)plan->nbins, plan->dim, plan->prec) + 256;
-    if ((rc = dev_alloc(plan, plan->xs, Mm * plan->dim * rs, "sorted coordinates")) != NUFFT_OK ||
-        (rc = dev_alloc(plan, plan->perm, Mm * sizeof(int32_t), "permutation")) != NUFFT_OK ||
-        (rc = dev_alloc(plan, plan->counts, (size_t)plan->nbins * sizeof(int32_t), "bin counts")) != NUFFT_OK ||
-        (rc = dev_alloc(plan, plan->offsets, (size_t)(plan->nbins + 1) * sizeof(int32_t), "bin offsets")) != NUFFT_OK ||
-        (rc = dev_alloc(plan, plan->sort_tmp, sort_bytes, "sort scratch")) != NUFFT_OK)
-        return rc;
-    // two small result slots at the end of the scratch: int64 subproblem count, int bad-point flag
-    char* tail = (char*)plan->sort_tmp.p + (plan->sort_tmp.bytes - 256);
-    if (!plan->host_tail) NUFFT_HIP(hipHostMalloc(&plan->host_tail, 128, hipHostMallocDefault));
-    int64_t* nsub_dev = (int64_t*)tail;
-    int* bad_dev = (int*)(tail + 64);
+    return setpts_impl(plan, M, x, y, z, false);
+}
 
-    begin_group(plan, 4);
-    record(plan, EV_SORT0);
-    NUFFT_HIP(hipMemsetAsync(bad_dev, 0, sizeof(int), plan->stream));
-    nufft::SortArgs a{};
-    a.dim = plan->dim;
-    a.prec = plan->prec;
-    a.M = M;
-    for (int i = 0; i < 3; ++i) {
-        a.x[i] = i < plan->dim ? X[i] : nullptr;
-        a.n[i] = (int)plan->n[i];
-        a.s[i] = plan->s[i];
-        a.m[i] = plan->m[i];
-        a.nb[i] = plan->nb[i];
-    }
-    a.nbins = (int)plan->nbins;
-    a.nbits = plan->nbits;
-    a.cap = plan->cap;
-    a.colw = plan->colw;
-    a.colstep = plan->colstep;
-    a.ncol = plan->ncol;
-    if (plan->method == NUFFT_METHOD_GM) {
-        // no sort and no binning: the points stay in the caller's order and the bin counts read zero
-        NUFFT_HIP(nufft::launch_fill_zero(plan->counts.p, (size_t)plan->nbins * sizeof(int32_t), plan->stream));
-        NUFFT_HIP(nufft::launch_identity_order(a, (int32_t*)plan->perm.p, plan->xs.p, bad_dev, plan->stream));
-        NUFFT_HIP(hipMemcpyAsync(plan->host_tail, tail, 128, hipMemcpyDeviceToHost, plan->stream));
-        NUFFT_HIP(hipStreamSynchronize(plan->stream));
-        const int host_bad = *(const int*)((const char*)plan->host_tail + 64);
-        if (host_bad) return fail(plan, NUFFT_ERR_POINTS, "a coordinate is not finite or outside [-3pi, 3pi)");
-        record(plan, EV_SORT1);
-        end_group(plan, 4);
-        plan->M = M;
-        plan->nsub = 0;
-        return NUFFT_OK;
-    }
-    NUFFT_HIP(nufft::launch_sort(a, (int32_t*)plan->perm.p, (int32_t*)plan->counts.p,
-                                 (int32_t*)plan->offsets.p, plan->xs.p, plan->sort_tmp.p,
-                                 plan->sort_tmp.bytes - 256, nsub_dev, bad_dev, plan->stream));
-    // one read of both result slots into pinned memory
-    NUFFT_HIP(hipMemcpyAsync(plan->host_tail, tail, 128, hipMemcpyDeviceToHost, plan->stream));
-    NUFFT_HIP(hipStreamSynchronize(plan->stream));
-    const int64_t host_nsub = *(const int64_t*)plan->host_tail;
-    const int host_bad = *(const int*)((const char*)plan->host_tail + 64);
-    if (host_bad) return fail(plan, NUFFT_ERR_POINTS, "a coordinate is not finite or outside [-3pi, 3pi)");
-    if ((rc = dev_alloc(plan, plan->sub, (size_t)std::max<int64_t>(host_nsub, 1) * 3 * sizeof(int32_t),
-                        "subproblem list")) != NUFFT_OK)
-        return rc;
-    NUFFT_HIP(nufft::launch_build_subproblems_from(M, (int)plan->nbins, plan->dim, plan->prec, plan->cap,
-                                                   (const int32_t*)plan->counts.p,
-                                                   (const int32_t*)plan->offsets.p, plan->sort_tmp.p,
-                                                   (int32_t*)plan->sub.p, plan->stream));
-    record(plan, EV_SORT1);
-    end_group(plan, 4);
-    plan->M = M;
-    plan->nsub = host_nsub;
-    return NUFFT_OK;
+int nufft_setpts_noalloc(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z) {
+    return setpts_impl(plan, M, x, y, z, true);
 }
 
 int nufft_setpts_type3(nufft_plan plan, int64_t M, const void* x, const void* y, const void* z, int64_t K,
