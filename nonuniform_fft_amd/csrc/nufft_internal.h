@@ -120,6 +120,17 @@ __device__ __forceinline__ double exp_es(double x) {
     return ldexp(p, (int)k);
 }
 
+// sqrt(x) for x in [0, 1] in fp64: the hardware square root (about 2^-23 relative error) refined
+// by one Newton step s + (x - s^2) / (2 s), which squares the relative error (below 1e-15 here);
+// x = 0 gives 0.  The refinement's reciprocal may be approximate: its error only scales the
+// already small correction.
+__device__ __forceinline__ double sqrt_unit(double x) {
+    const double s = __builtin_amdgcn_sqrt(x);
+    const double e = __fma_rn(-s, s, x);
+    const double r = __builtin_amdgcn_rcp(s);
+    return (x > 0.0) ? __fma_rn(e, 0.5 * r, s) : 0.0;
+}
+
 // ES kernel weights (cuFINUFFT paper eq. (5), rescaled as in eq. (8)) of a point with folded
 // scaled coordinate t along one dimension: the support is the W cells starting at
 // l0 = ceil(t - W/2); weight q has argument z = (l0 + q - t) * 2/W.  The offset l0 - t is
@@ -138,7 +149,7 @@ __device__ __forceinline__ int es_weights(double t, T beta, T* phi) {
         if constexpr (sizeof(T) == 4)
             phi[q] = (zz <= 1.0f) ? __expf(beta * (__builtin_amdgcn_sqrtf(1.0f - zz) - 1.0f)) : 0.0f;
         else
-            phi[q] = (zz <= (T)1) ? exp_es(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
+            phi[q] = (zz <= (T)1) ? exp_es(beta * (sqrt_unit((T)1 - zz) - (T)1)) : (T)0;
     }
     return (int)l0d;
 }

@@ -572,18 +572,29 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
     const int npieces = (per + PIECE - 1) / PIECE;    // the same for every wavefront
     const T beta = (T)g.beta;
 
-    // this thread's staging items: (slice, point, dimension, q), and their raw inputs (the
-    // strengths arrive in sorted order)
+    // this thread's staging items: (slice, point, dimension, q), the same in every piece, so they
+    // are decoded once and kept packed (q | d << 5 | p << 7 | s << 11, or -1 past the last item);
+    // and their raw inputs (the strengths arrive in sorted order)
+    static_assert(W < 32 && PIECE < 16 && SLICES < 64, "item fields");
     T xr[IT], crr[IT], cri[IT];
-    auto item_point = [&](int it, int k, int& s_, int& p_, int& d_, int& q_) -> int64_t {
+    int item[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
         const int i = threadIdx.x + it * BLOCK;
-        if (i >= ITEMS) return -1;
-        q_ = i % W;
-        int r = i / W;
-        d_ = r % 3;
-        r /= 3;
-        p_ = r % PIECE;
-        s_ = r / PIECE;
+        if (i >= ITEMS) {
+            item[it] = -1;
+        } else {
+            const int q = i % W, r = i / W;
+            item[it] = q | ((r % 3) << 5) | (((r / 3) % PIECE) << 7) | ((r / 3 / PIECE) << 11);
+        }
+    }
+    auto item_point = [&](int it, int k, int& s_, int& p_, int& d_, int& q_) -> int64_t {
+        const int v = item[it];
+        if (v < 0) return -1;
+        q_ = v & 31;
+        d_ = (v >> 5) & 3;
+        p_ = (v >> 7) & 15;
+        s_ = v >> 11;
         const int ps = s_ * per + k * PIECE + p_;              // point index in the subproblem
         if (k * PIECE + p_ >= per || ps >= len) return -1;
         return (int64_t)start + ps;
@@ -622,7 +633,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col_wg(GeomArgs g,
             if constexpr (sizeof(T) == 4)
                 phi = (zz <= 1.0f) ? __expf(beta * (__builtin_amdgcn_sqrtf(1.0f - zz) - 1.0f)) : 0.0f;
             else
-                phi = (zz <= (T)1) ? exp_es(beta * (sqrt((T)1 - zz) - (T)1)) : (T)0;
+                phi = (zz <= (T)1) ? exp_es(beta * (sqrt_unit((T)1 - zz) - (T)1)) : (T)0;
             // the start is checked once per (point, dimension), by its q = 0 item
             const int l0 = (q_ == 0) ? checked_start((int)l0d - origin[d_], pd[d_] - W, g.range_err)
                                      : min(max((int)l0d - origin[d_], 0), pd[d_] - W);
