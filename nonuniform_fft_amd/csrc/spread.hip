@@ -234,8 +234,10 @@ struct ColCfg {
 template <typename T, int W>
 struct ColStage {
     using C = ColCfg<T, W>;
-    T kz[C::kPiece][C::kWZ];
-    cplx<T> cv[C::kPiece];
+    // a point's z weights then its strength, in one 16-byte-aligned row: every lane reads the
+    // row from one address
+    static constexpr int kRow = (W + 2 + 3) & ~3;
+    T kzc[C::kPiece][kRow];
     // x and y weights placed in the point's block window (zero elsewhere); the odd row pitch puts
     // the staging lanes' stores on distinct banks
     T kx[C::kPiece][C::kB | 1];
@@ -251,6 +253,13 @@ struct IntC {
 __device__ __forceinline__ int uniform_copy(int v) {
     int r;
     asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
+    return r;
+}
+
+// A copy of a per-lane value that the optimizer cannot split into scalar and vector parts.
+__device__ __forceinline__ uint32_t vector_copy(uint32_t v) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
     return r;
 }
 
@@ -411,11 +420,14 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
                 for (int q = 0; q < B; ++q) win[q] = (T)0;
 #pragma unroll
                 for (int q = 0; q < W; ++q) win[off + q] = ker[q];
-                if (si == 0) ws->cv[sp] = cr;
+                if (si == 0) {
+                    ws->kzc[sp][W] = cr.re;
+                    ws->kzc[sp][W + 1] = cr.im;
+                }
                 l0 = blk;
             } else {
 #pragma unroll
-                for (int q = 0; q < W; ++q) ws->kz[sp][q] = ker[q];
+                for (int q = 0; q < W; ++q) ws->kzc[sp][q] = ker[q];
             }
         }
         // lane 3 sp packs the point's x block | y block << 8 | z start << 16
@@ -439,12 +451,29 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
         // start covers a whole group, whose points then cost only their loads and 2 w FMAs.
         auto group = [&](auto z0c, int p, int kp) -> int {
             constexpr int Z0 = decltype(z0c)::value;
+            using LT = __attribute__((address_space(3))) const T;
+            constexpr uint32_t kRowBytes = (uint32_t)sizeof(ws->kx[0]);
+            // this lane's x and y weight addresses as whole vector registers, advanced one staged
+            // point at a time (left to itself the compiler re-adds the stage base on every point)
+            uint32_t ax = vector_copy((uint32_t)(uintptr_t)(LT*)&ws->kx[p][q1]);
+            uint32_t ay = vector_copy((uint32_t)(uintptr_t)(LT*)&ws->ky[p][q2]);
+            // lane of the next point's key, kept in a scalar register
+            int kl = uniform_copy(3 * p + 3);
             ColPt<T, W> A;
-            do {
-                A.load(*ws, p, q1, q2);
+            while (true) {
+#pragma unroll
+                for (int q = 0; q < W; ++q) A.kz[q] = ws->kzc[p][q];
+                A.cv.re = ws->kzc[p][W];
+                A.cv.im = ws->kzc[p][W + 1];
+                A.kx = *(LT*)(uintptr_t)ax;
+                A.ky = *(LT*)(uintptr_t)ay;
                 A.template add<Z, Z0>(are, aim);
                 ++p;
-            } while (p < np && __builtin_amdgcn_readlane(key, 3 * p) == kp);
+                ax += kRowBytes;
+                ay += kRowBytes;
+                if (p >= np || __builtin_amdgcn_readlane(key, kl) != kp) break;
+                kl = uniform_copy(kl + 3);
+            }
             return p;
         };
         int p = 0;
