@@ -24,12 +24,25 @@ namespace {
 constexpr int kSpreadBlock = 1024;   // 16 wavefronts: one workgroup keeps a CU busy on its own
 constexpr int kGmBlock = 128;
 
-// Points staged per round: about 24 KB of LDS for kernel weights, local offsets and strengths.
+// One staged point of the point-patch kernel: its x and y weights, strength, the tile offset of
+// its stencil start (l0x + l0y pc + l0z pp) and, in 3D, its z weights widened to fp64.  Records
+// of 20 or 22 words put the x (or y) weights of up to 16 neighbouring points on distinct banks.
 template <typename T, int DIM, int W>
-struct SmCfg {
+struct SmRec {
     static constexpr int kWP = (W + 3) & ~3;                      // padded row of T weights (16 B aligned)
     static constexpr int kWD = (W + 1) & ~1;                      // padded row of fp64 z weights
-    static constexpr int kPerPoint = 2 * kWP * (int)sizeof(T) + (DIM == 3 ? kWD * 8 : 0) + 16 + 2 * (int)sizeof(T);
+    T kx[kWP];
+    T ky[kWP];
+    cplx<T> cv;
+    int base;
+    int pad_;
+    double kz[DIM == 3 ? kWD : 1];
+};
+
+// Points staged per round: about 24 KB of LDS.
+template <typename T, int DIM, int W>
+struct SmCfg {
+    static constexpr int kPerPoint = (int)sizeof(SmRec<T, DIM, W>);
     static constexpr int kRaw = 24576 / kPerPoint;
     static constexpr int kChunk = kRaw >= 256 ? 256 : (kRaw < 32 ? 32 : (kRaw & ~31));
 };
@@ -38,11 +51,15 @@ template <typename T, int DIM, int W>
 struct Stage {
     using C = SmCfg<T, DIM, W>;
     static constexpr int CH = C::kChunk;
-    int4 l0[CH];                                   // local stencil start per dimension
-    cplx<T> cv[CH];                                // strength
-    T kxy[CH][2][C::kWP];                          // x and y weights
-    double kz[DIM == 3 ? CH : 1][C::kWD];          // z weights, widened once
+    SmRec<T, DIM, W> rec[CH];
 };
+
+// A copy of a per-lane value that the optimizer cannot split into scalar and vector parts.
+__device__ __forceinline__ uint32_t vector_copy(uint32_t v) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
 
 // LDS tile of a padded bin: separate fp64 planes for real and imaginary parts, row pitch pc with
 // pc = W (mod 16), so the w x w patch of one point's x-y stencil covers the 16 bank pairs evenly.
@@ -89,75 +106,94 @@ k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c, cplx<T>* __restrict__ gri
     const int pd[3] = {p1, p2, p3};
     for (int k = threadIdx.x; k < 2 * PL; k += kSpreadBlock) tre[k] = 0.0;
 
-    // this thread's fixed slot (q1, q2) of the x-y stencil patch
+    // this thread's fixed slot (q1, q2) of the x-y stencil patch, and its tile offset
     const int t = threadIdx.x;
     const int p_first = t / WW;
     const int slot = t - p_first * WW;
     const int q2 = slot / W;
     const int q1 = slot - q2 * W;
+    const int qoff = q1 + q2 * pc;
     const bool active = p_first < PPP;
 
     const T beta = (T)g.beta;
-    // staging thread (point sp, dimension si): its raw coordinate and strength for the next
-    // chunk are requested while the current chunk is accumulated
-    const int sp = threadIdx.x / DIM, si = threadIdx.x - (threadIdx.x / DIM) * DIM;
+    // staging thread (point sp, dimension si < DIM; in 3D four lanes per point, the fourth idle,
+    // so that a point's lanes sit in one aligned quad): its raw coordinate and strength for the
+    // next chunk are requested while the current chunk is accumulated
+    constexpr int SPW = (DIM == 3) ? 4 : DIM;
+    static_assert(SPW * CH <= kSpreadBlock, "one staging lane per point and dimension");
+    const int sp = threadIdx.x / SPW, si = threadIdx.x - (threadIdx.x / SPW) * SPW;
+    const int spitch = (si == 0) ? 1 : (si == 1 ? pc : pp);
     T xr = (T)0;
     cplx<T> cr;
     cr.re = (T)0;
     cr.im = (T)0;
     auto fetch = [&](int c0) {
-        if (threadIdx.x < min(CH, len - c0) * DIM) {
+        if (si < DIM && sp < min(CH, len - c0)) {
             const int64_t j = (int64_t)start + c0 + sp;
             xr = ((const T*)g.xs[si])[j];
             if (si == 0) cr = c[g.cperm ? g.cperm[j] : j];
         }
     };
+    using Rec = SmRec<T, DIM, W>;
+    using LRec = __attribute__((address_space(3))) const Rec;
+    using LT = __attribute__((address_space(3))) const T;
+    constexpr uint32_t kStep = (uint32_t)(PPP * sizeof(Rec));
     fetch(0);
     for (int c0 = 0; c0 < len; c0 += CH) {
         const int np = min(CH, len - c0);
         __syncthreads();   // previous chunk consumed (and tile zeroed on the first round)
-        // stage kernel weights: one thread per (point, dimension)
-        if (threadIdx.x < np * DIM) {
-            const int p = sp;
-            const int i = si;
-            double tt = grid_t((double)xr, g.s[i]);
+        // stage kernel weights: one thread per (point, dimension); the point's lanes add up the
+        // tile offset of its stencil start
+        int part = 0;
+        if (si < DIM && sp < np) {
+            Rec& r = st->rec[sp];
+            double tt = grid_t((double)xr, g.s[si]);
             int l;
-            fold_t(tt, g.n[i], l);
+            fold_t(tt, g.n[si], l);
             T ker[W];
-            const int l0 = checked_start(es_weights<T, W>(tt, beta, ker) - origin[i], pd[i] - W, g.range_err);
-            if (i < 2) {
+            const int l0 = checked_start(es_weights<T, W>(tt, beta, ker) - origin[si], pd[si] - W, g.range_err);
+            if (si == 0) {
 #pragma unroll
-                for (int q = 0; q < W; ++q) st->kxy[p][i][q] = ker[q];
+                for (int q = 0; q < W; ++q) r.kx[q] = ker[q];
+                r.cv = cr;
+            } else if (si == 1) {
+#pragma unroll
+                for (int q = 0; q < W; ++q) r.ky[q] = ker[q];
             } else {
 #pragma unroll
-                for (int q = 0; q < W; ++q) st->kz[DIM == 3 ? p : 0][q] = (double)ker[q];
+                for (int q = 0; q < W; ++q) r.kz[DIM == 3 ? q : 0] = (double)ker[q];
             }
-            if (i == 0) {
-                st->l0[p].x = l0;
-                st->cv[p] = cr;
-            } else if (i == 1) {
-                st->l0[p].y = l0;
-            } else {
-                st->l0[p].z = l0;
-            }
+            part = l0 * spitch;
         }
+        part += __shfl_xor(part, 1);
+        if (DIM == 3) part += __shfl_xor(part, 2);
+        if (si == 0 && sp < np) st->rec[sp].base = part;
         if (c0 + CH < len) fetch(c0 + CH);
         __syncthreads();
-        if (active) {
+        if (active && p_first < np) {
+            // this item's record fields as whole vector registers, advanced PPP records at a time
+            uint32_t ar = vector_copy((uint32_t)(uintptr_t)(LRec*)&st->rec[p_first]);
+            uint32_t ax = vector_copy((uint32_t)(uintptr_t)(LT*)&st->rec[p_first].kx[q1]);
+            uint32_t ay = vector_copy((uint32_t)(uintptr_t)(LT*)&st->rec[p_first].ky[q2]);
             for (int p = p_first; p < np; p += PPP) {
                 // read everything this item needs before the first atomic, so the LDS counter
                 // waits only on these reads and the atomics then issue back to back
-                const int4 l0 = st->l0[p];
-                const cplx<T> cv = st->cv[p];
+                LRec* R = (LRec*)(uintptr_t)ar;
+                cplx<T> cv;
+                cv.re = R->cv.re;
+                cv.im = R->cv.im;
+                const int base = R->base + qoff;
                 double kz[DIM == 3 ? W : 1];
                 if (DIM == 3) {
 #pragma unroll
-                    for (int q3 = 0; q3 < W; ++q3) kz[q3] = st->kz[DIM == 3 ? p : 0][q3];
+                    for (int q3 = 0; q3 < W; ++q3) kz[q3] = R->kz[DIM == 3 ? q3 : 0];
                 }
-                const T wxy = st->kxy[p][0][q1] * st->kxy[p][1][q2];
+                const T wxy = *(LT*)(uintptr_t)ax * *(LT*)(uintptr_t)ay;
+                ar += kStep;
+                ax += kStep;
+                ay += kStep;
                 const double vre = (double)(cv.re * wxy);
                 const double vim = (double)(cv.im * wxy);
-                const int base = l0.x + q1 + (l0.y + q2) * pc + (DIM == 3 ? l0.z * pp : 0);
                 if (DIM == 2) {
                     atomicAdd(tre + base, vre);
                     atomicAdd(tim + base, vim);
@@ -253,13 +289,6 @@ struct IntC {
 __device__ __forceinline__ int uniform_copy(int v) {
     int r;
     asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
-    return r;
-}
-
-// A copy of a per-lane value that the optimizer cannot split into scalar and vector parts.
-__device__ __forceinline__ uint32_t vector_copy(uint32_t v) {
-    uint32_t r;
-    asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
     return r;
 }
 
