@@ -723,12 +723,13 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
     plan->colw = 0;
     plan->colstep = 1;
     plan->ncol = 1;
-    const size_t col_lds = nufft::spread_col_lds_bytes(plan->prec, w, plan->m);
-    const int step = nufft::spread_col_step(w);
+    // (the column step is positive only at the widths the column kernels serve, w <= 12)
+    const bool col_width = plan->method == NUFFT_METHOD_SM && nufft::spread_uses_columns(dim, w);
+    const size_t col_lds = col_width ? nufft::spread_col_lds_bytes(plan->prec, w, plan->m) : 0;
+    const int step = col_width ? nufft::spread_col_step(w) : 1;
     const int64_t ncol = (int64_t)((plan->m[0] + step) / step) * ((plan->m[1] + step) / step) *
                          (plan->m[2] + 1);
-    const bool col_fits = plan->method == NUFFT_METHOD_SM && nufft::spread_uses_columns(dim, w) &&
-                          plan->m[2] == 8 && col_lds > 0 && col_lds <= nufft::spread_lds_limit() &&
+    const bool col_fits = col_width && plan->m[2] == 8 && col_lds > 0 && col_lds <= nufft::spread_lds_limit() &&
                           plan->nbins * ncol < (int64_t(1) << 31);
     // the bins must fit the spreader this plan will run, and the interpolation tile
     if ((!col_fits && plan->method == NUFFT_METHOD_SM &&

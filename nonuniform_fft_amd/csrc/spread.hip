@@ -1098,6 +1098,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 // kernel is faster there
 bool spread_uses_columns(int dim, int w) { return dim == 3 && w >= 5 && w <= 12; }
 
+// support starts per column-block edge; defined (and at least 1) only where spread_uses_columns holds
 int spread_col_step(int w) { return col_block_edge(w) - w + 1; }
 
 size_t spread_col_lds_bytes(int prec, int w, const int* m) {

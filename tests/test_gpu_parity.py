@@ -559,6 +559,41 @@ def test_execute_adjoint_matches_oracle(nf, orc, wl):
 
 
 # ---------------------------------------------------------------------------------------------
+# The point-patch spreader (2D, and 3D outside the column widths) across kernel widths
+# ---------------------------------------------------------------------------------------------
+
+PATCH_CASES = [(2, "f32", 1e-1), (2, "f32", 1e-3), (2, "f32", 1e-6), (2, "f64", 1e-8), (2, "f64", 1e-10),
+               (2, "f64", 1e-13), (2, "f64", 1e-15), (3, "f32", 1e-1), (3, "f32", 1e-3), (3, "f64", 1e-2),
+               (3, "f64", 1e-3), (3, "f64", 1e-12), (3, "f64", 1e-13), (3, "f64", 1e-15)]
+
+
+@pytest.mark.parametrize("dim,prec,eps", PATCH_CASES, ids=[f"{d}d_{p}_{e:g}" for d, p, e in PATCH_CASES])
+def test_point_patch_widths(nf, orc, dim, prec, eps):
+    """Plans served by the point-patch spreader at kernel widths 2..16 (the staged point record's
+    padded rows change with w): the plan reports no column order, and type 1 plus the adjoint type 2
+    on the same sorted points match the oracle."""
+    N = (40, 36) if dim == 2 else (16, 14, 12)
+    wl = Workload("patch", dim, N, 8_000 if dim == 2 else 6_000, eps, prec, seed=141)
+    _announce(f"point-patch widths {dim}D {prec} eps={eps}")
+    inp = make_inputs(wl)
+    cd = cdtype(prec)
+    p = nf.Plan(1, N, eps, prec)
+    info = p.info()
+    assert info["colw"] == 0, info
+    p.setpts(*[to_dev(x) for x in inp["X"]])
+    f = torch.empty(tuple(reversed(N)), dtype=cd, device=dev())
+    c = torch.empty(wl.M, dtype=cd, device=dev())
+    p.execute(to_dev(inp["c"]), f)
+    p.execute_adjoint(c, to_dev(inp["f"]))
+    torch.cuda.synchronize()
+    assert p.range_errors() == 0
+    p.destroy()
+    e1 = orc.rel_l2(f.cpu().numpy(), orc.nufft_type1(inp["X"], inp["c"], N, eps))
+    e2 = orc.rel_l2(c.cpu().numpy(), orc.nufft_type2(inp["X"], inp["f"], N, eps))
+    assert e1 <= tol_for(prec) and e2 <= tol_for(prec), (info["w"], e1, e2)
+
+
+# ---------------------------------------------------------------------------------------------
 # The 3D column-run spreader at every kernel width it serves
 # ---------------------------------------------------------------------------------------------
 
