@@ -593,6 +593,37 @@ def test_point_patch_widths(nf, orc, dim, prec, eps):
     assert e1 <= tol_for(prec) and e2 <= tol_for(prec), (info["w"], e1, e2)
 
 
+WIDTH_METHOD_CASES = [(1, "f32", 1e-1, 2), (1, "f32", 1e-3, 2), (1, "f64", 1e-8, 2), (1, "f64", 1e-13, 2),
+                      (1, "f64", 1e-15, 2), (1, "f64", 1e-13, 1), (2, "f32", 1e-1, 1), (2, "f64", 1e-13, 1),
+                      (3, "f64", 1e-15, 1), (1, "f32", 1e-1, 3), (2, "f64", 1e-15, 3), (3, "f64", 1e-13, 3)]
+
+
+@pytest.mark.parametrize("dim,prec,eps,method", WIDTH_METHOD_CASES,
+                         ids=[f"{d}d_{p}_{e:g}_m{m}" for d, p, e, m in WIDTH_METHOD_CASES])
+def test_widths_1d_and_gm(nf, orc, dim, prec, eps, method):
+    """The kernels outside the 2D/3D point-patch and column spreaders at the extreme kernel widths:
+    the 1D SM spreader and interpolation (w = 2, 4, 9, 14, 16) and the GM-sort (method 1) and GM
+    (method 3) kernels in 1D, 2D and 3D (w = 2, 14, 16); type 1 and the adjoint type 2 match the
+    oracle."""
+    N = {1: (300,), 2: (40, 36), 3: (16, 14, 12)}[dim]
+    wl = Workload("wm", dim, N, 5_000, eps, prec, seed=151)
+    _announce(f"widths {dim}D {prec} eps={eps} method={method}")
+    inp = make_inputs(wl)
+    cd = cdtype(prec)
+    p = nf.Plan(1, N, eps, prec, method=method)
+    p.setpts(*[to_dev(x) for x in inp["X"]])
+    f = torch.empty(tuple(reversed(N)), dtype=cd, device=dev())
+    c = torch.empty(wl.M, dtype=cd, device=dev())
+    p.execute(to_dev(inp["c"]), f)
+    p.execute_adjoint(c, to_dev(inp["f"]))
+    torch.cuda.synchronize()
+    assert p.range_errors() == 0
+    p.destroy()
+    e1 = orc.rel_l2(f.cpu().numpy(), orc.nufft_type1(inp["X"], inp["c"], N, eps))
+    e2 = orc.rel_l2(c.cpu().numpy(), orc.nufft_type2(inp["X"], inp["f"], N, eps))
+    assert e1 <= tol_for(prec) and e2 <= tol_for(prec), (e1, e2)
+
+
 # ---------------------------------------------------------------------------------------------
 # The 3D column-run spreader at every kernel width it serves
 # ---------------------------------------------------------------------------------------------
