@@ -414,6 +414,33 @@ def test_empty_and_single_point(nf, orc):
         assert orc.rel_l2(f, ref) <= tol_for(prec)
 
 
+TINY_CASES = [((1,), "f32"), ((2,), "f64"), ((3,), "f32"), ((1, 1), "f64"), ((1, 5), "f32"), ((2, 3), "f64"),
+              ((1, 1, 1), "f32"), ((3, 1, 2), "f64"), ((5, 4, 1), "f32"), ((2, 2, 2), "f64")]
+
+
+@pytest.mark.parametrize("N,prec", TINY_CASES, ids=[f"{'x'.join(map(str, n))}_{p}" for n, p in TINY_CASES])
+@pytest.mark.parametrize("M", [1, 3, 500])
+def test_tiny_mode_counts(nf, orc, N, prec, M):
+    """One to five modes per dimension: the fine grid is the kernel width or just above it, the
+    padded bins wrap onto it several times, and a dimension with one mode has only k = 0; type 1
+    and the adjoint type 2 match the oracle."""
+    wl = Workload("tiny", len(N), N, M, 1e-6, prec, seed=161 + M)
+    inp = make_inputs(wl)
+    cd = cdtype(prec)
+    p = nf.Plan(1, N, 1e-6, prec)
+    p.setpts(*[to_dev(x) for x in inp["X"]])
+    f = torch.empty(tuple(reversed(N)), dtype=cd, device=dev())
+    c = torch.empty(M, dtype=cd, device=dev())
+    p.execute(to_dev(inp["c"]), f)
+    p.execute_adjoint(c, to_dev(inp["f"]))
+    torch.cuda.synchronize()
+    assert p.range_errors() == 0
+    p.destroy()
+    e1 = orc.rel_l2(f.cpu().numpy(), orc.nufft_type1(inp["X"], inp["c"], N, 1e-6))
+    e2 = orc.rel_l2(c.cpu().numpy(), orc.nufft_type2(inp["X"], inp["f"], N, 1e-6))
+    assert e1 <= tol_for(prec) and e2 <= tol_for(prec), (e1, e2)
+
+
 SIGMA_CASES = [
     Workload("sg", 1, (2000,), 40_000, 1e-6, "f32", seed=111),
     Workload("sg", 2, (100, 72), 50_001, 1e-5, "f32", seed=112),
