@@ -101,7 +101,11 @@ int nufft_default_opts(nufft_opts* opts);
  *   opts      NULL or tuning/test options.
  *   out       receives the plan.  Nothing is allocated on error.
  * Allocates the fine grid (n_i = smallest 2^a 3^b 5^c >= max(ceil(sigma N_i), w)), the
- * correction factors (eq. (10), computed on the host in fp64) and the rocFFT plan.
+ * correction factors (eq. (10), computed on the host in fp64) and the rocFFT plan.  Each N_i is
+ * at most 2^28 and the fine grid has fewer than 2^32 cells (NUFFT_ERR_BAD_ARG otherwise: rocFFT
+ * transforms of 2^32 elements or more gave wrong values on this software stack); the grid is
+ * held twice (spreading output and FFT output), so a 2048 x 2048 x 1000 fp32 grid takes 62.5 GiB,
+ * and a grid the device cannot hold fails with NUFFT_ERR_ALLOC.
  */
 int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int precision,
                       void* stream, const nufft_opts* opts, nufft_plan* out);

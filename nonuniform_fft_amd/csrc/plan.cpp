@@ -694,7 +694,9 @@ int nufft_plan_create(int type, int dim, const int64_t* N, double eps, int preci
         plan->n[i] = i < dim ? next_5smooth(std::max<int64_t>((int64_t)std::ceil(sigma * (double)N[i] - 1e-9), w)) : 1;
         plan->s[i] = (double)plan->n[i] / (2.0 * nufft::kPi);
     }
-    if (grid_cells(plan) > (int64_t(1) << 31) - 1) {
+    // fewer than 2^32 cells: rocFFT's 3D transforms of 2^32 elements returned wrong values here
+    // (a delta function's transform, 2048 x 2048 x 1024), while 2048 x 2048 x 1000 was exact
+    if (grid_cells(plan) >= (int64_t(1) << 32)) {
         nufft_destroy(plan);
         return NUFFT_ERR_BAD_ARG;
     }

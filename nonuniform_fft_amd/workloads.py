@@ -19,7 +19,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "draw_points", "draw_strengths",
-           "draw_coefficients", "scaled"]
+           "draw_coefficients", "draw_sparse_coefficients", "scaled"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -126,13 +126,29 @@ def draw_coefficients(wl: Workload, rng: np.random.Generator) -> np.ndarray:
     return f
 
 
+def draw_sparse_coefficients(wl: Workload, rng: np.random.Generator, count: int):
+    """`count` distinct flat mode positions (k1 fastest) drawn uniformly, with real and imaginary
+    parts iid N(0,1): the nonzero entries of an otherwise zero f, for grids too large to fill."""
+    total = wl.nmodes
+    picks = np.unique(rng.integers(0, total, size=4 * count))[:count]
+    while picks.size < count:
+        picks = np.unique(np.concatenate([picks, rng.integers(0, total, size=count)]))[:count]
+    vals = np.empty(picks.size, dtype=wl.complex_dtype)
+    vals.real = rng.standard_normal(picks.size)
+    vals.imag = rng.standard_normal(picks.size)
+    return picks.astype(np.int64), vals
+
+
 def make_inputs(wl: Workload, seed: Optional[int] = None, want_c: bool = True,
-                want_f: bool = True):
-    """Points, then strengths, then coefficients, from one PCG64 stream."""
+                want_f: bool = True, sparse_f: int = 0):
+    """Points, then strengths, then coefficients, from one PCG64 stream.  With sparse_f > 0 the
+    coefficients are that many nonzero modes ("f_modes", "f_vals") instead of a dense "f"."""
     rng = np.random.default_rng(wl.seed if seed is None else seed)
     out = {"X": draw_points(wl, rng)}
     if want_c:
         out["c"] = draw_strengths(wl, rng)
-    if want_f:
+    if sparse_f > 0:
+        out["f_modes"], out["f_vals"] = draw_sparse_coefficients(wl, rng, sparse_f)
+    elif want_f:
         out["f"] = draw_coefficients(wl, rng)
     return out

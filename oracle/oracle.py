@@ -404,6 +404,29 @@ def direct_type2(X, f, N: Sequence[int], sel: Optional[Sequence[int]] = None) ->
     return out
 
 
+def direct_type2_modes(X, N: Sequence[int], modes: Sequence[int], vals) -> np.ndarray:
+    """Eq. (3) summed term by term over the nonzero coefficients only: f is zero except at the
+    flat mode positions `modes` (k1 fastest, k_i in I_N of eq. (2)), where it holds `vals`.
+    Returns c at every point."""
+    d = len(N)
+    modes = np.asarray(modes, dtype=np.int64)
+    vals = np.asarray(vals, dtype=np.complex128)
+    # the mode vector of each flat position
+    ks = []
+    rest = modes.copy()
+    for i in range(d):
+        ks.append(mode_range(int(N[i]))[rest % int(N[i])].astype(np.float64))
+        rest //= int(N[i])
+    M = np.asarray(X[0]).size
+    out = np.zeros(M, dtype=np.complex128)
+    for lo in range(0, M, 4096):
+        ph = np.zeros((min(M, lo + 4096) - lo, modes.size))
+        for i in range(d):
+            ph += np.outer(np.asarray(X[i], dtype=np.float64)[lo:lo + 4096], ks[i])
+        out[lo:lo + ph.shape[0]] = np.exp(1j * ph) @ vals
+    return out
+
+
 # ----------------------------------------------------------------------------------------------
 # Bin-sort and subproblems (Sec. III-A)
 # ----------------------------------------------------------------------------------------------

@@ -44,7 +44,11 @@ def test_host_side_argument_checks():
     h = ctypes.c_void_p()
     bad = [(4, 2, N, 1e-5, 0), (0, 2, N, 1e-5, 0), (1, 4, N, 1e-5, 0), (1, 0, N, 1e-5, 0), (1, 2, N, 0.0, 0), (1, 2, N, -1.0, 0),
            (1, 2, N, float("nan"), 0), (1, 2, N, 1e-5, 2), (1, 2, None, 1e-5, 0),
-           (2, 3, (ctypes.c_int64 * 3)(16, 0, 16), 1e-5, 1)]
+           (2, 3, (ctypes.c_int64 * 3)(16, 0, 16), 1e-5, 1),
+           # a mode count above 2^28, and fine grids of 2^32 and 2^38 cells
+           (1, 1, (ctypes.c_int64 * 3)((1 << 28) + 1, 1, 1), 1e-5, 0),
+           (1, 3, (ctypes.c_int64 * 3)(1 << 10, 1 << 10, 1 << 9), 1e-5, 0),
+           (1, 3, (ctypes.c_int64 * 3)(1 << 12, 1 << 12, 1 << 11), 1e-5, 0)]
     for t, d, n, e, p in bad:
         assert lib.nufft_plan_create(t, d, n, e, p, None, None, ctypes.byref(h)) == -1
         assert not h.value

@@ -139,3 +139,39 @@ def test_full_size_config(nf, orc, name, whole, nmodes, npts):
     d2 = orc.rel_l2(c_gpu[jj], orc.direct_type2(X, f, wl.N, sel=jj))
     print(f"  vs exact sums: type1 {d1:.2e}  type2 {d2:.2e}  (10 eps = {10 * wl.eps:g})", flush=True)
     assert d1 <= 10 * wl.eps and d2 <= 10 * wl.eps
+
+
+def test_fine_grid_above_2_31_cells(nf, orc):
+    """The largest grid class a plan accepts: 3D fp32 with N = 1024 x 1024 x 500 modes on a
+    2048 x 2048 x 1000 fine grid, 4.19e9 cells (above 2^31, below the 2^32 limit; two 31 GiB grid
+    buffers), so every linear cell index exceeds a signed 32-bit integer somewhere in the grid.
+    Type 1 at 64 modes and type 2 at all points are compared with the exact sums (eqs. (1), (3))
+    within 10 eps; the type 2 coefficients have 16 nonzero modes, so their exact sum is cheap."""
+    from nonuniform_fft_amd.workloads import Workload
+    N = (1024, 1024, 500)
+    wl = Workload("grid_big", 3, N, 4096, 1e-5, "f32", seed=171)
+    print(f"largest grid: N={N} M={wl.M}", flush=True)
+    inp = make_inputs(wl, sparse_f=16)
+    X, c = inp["X"], inp["c"]
+    plan = nf.Plan(1, N, wl.eps, "f32")
+    assert tuple(plan.info()["n"][:3]) == (2048, 2048, 1000)
+    plan.setpts(*[to_dev(x) for x in X])
+    f_out = torch.empty(tuple(reversed(N)), dtype=torch.complex64, device=dev())
+    plan.execute(to_dev(c), f_out)
+    f_in = torch.zeros(tuple(reversed(N)), dtype=torch.complex64, device=dev())
+    f_in.view(-1)[torch.from_numpy(inp["f_modes"]).to(dev())] = to_dev(inp["f_vals"])
+    c_out = torch.empty(wl.M, dtype=torch.complex64, device=dev())
+    plan.execute_adjoint(c_out, f_in)
+    torch.cuda.synchronize()
+    assert plan.range_errors() == 0
+    rng = np.random.default_rng(9)
+    sel_k = _sample_modes(N, 64, rng)
+    f_sel = f_out.view(-1)[torch.from_numpy(sel_k).to(dev())].cpu().numpy()
+    c_gpu = c_out.cpu().numpy()
+    del f_out, f_in, c_out
+    plan.destroy()
+    torch.cuda.empty_cache()
+    d1 = orc.rel_l2(f_sel, orc.direct_type1(X, c, N, sel=sel_k))
+    d2 = orc.rel_l2(c_gpu, orc.direct_type2_modes(X, N, inp["f_modes"], inp["f_vals"]))
+    print(f"  vs exact sums: type1 at 64 modes {d1:.2e}, type2 at all points {d2:.2e}", flush=True)
+    assert d1 <= 10 * wl.eps and d2 <= 10 * wl.eps

@@ -183,6 +183,23 @@ def test_direct_selected_entries_match_full(oracle_mod):
     np.testing.assert_array_equal(oracle_mod.direct_type2(X, f, N, sel=[3, 29, 0]), full2[[3, 29, 0]])
 
 
+@pytest.mark.parametrize("N", [(7,), (6, 5), (5, 4, 6)])
+def test_direct_type2_modes_matches_dense(oracle_mod, N):
+    """The sparse form of eq. (3) equals the dense exact sum of the C oracle on an f that is zero
+    except at the listed modes (odd and even N, corner modes included)."""
+    rng = _rng(5)
+    d = len(N)
+    X = _uniform_points(rng, d, 25)
+    total = int(np.prod(N))
+    modes = np.array(sorted({0, total - 1, *rng.integers(0, total, 6).tolist()}), dtype=np.int64)
+    vals = _rand_complex(rng, modes.size)
+    f = np.zeros(total, dtype=complex)
+    f[modes] = vals
+    dense = oracle_mod.direct_type2(X, f.reshape(tuple(reversed(N))), N)
+    sparse = oracle_mod.direct_type2_modes(X, N, modes, vals)
+    assert np.max(np.abs(sparse - dense)) <= 1e-13 * np.max(np.abs(dense))
+
+
 # ---------------------------------------------------------------------------------------------
 # Spreading / interpolation against a brute-force periodic sum over the whole grid (eqs. (7), (8))
 # ---------------------------------------------------------------------------------------------
