@@ -96,7 +96,7 @@ constexpr int kInterpSmBlock =
 // and so on; lane i takes position i, so every run of R lanes holds R distinct residues until
 // the classes run out.  Which lane evaluates a point changes nothing in its result.
 //
-// Measured (3D, N = 256^3, M = 2^27, eps = 1e-9, w = 10): 36.2 -> 31.8 ms.  The same order did not
+// Measured (3D, N = 256^3, M = 2^27, eps = 1e-9, w = 10): 36.2 -> 31.4 ms.  The same order did not
 // pay for its three barriers per chunk in fp32, whose interpolation issues few LDS bytes per
 // VALU instruction (3D 128^3 w = 6: 0.78 -> 1.11 ms), nor for 2D fp64 (w = 13: 0.30 -> 0.33 ms).
 template <typename T>
