@@ -195,6 +195,9 @@ STEP_CASES = [
     Workload("st", 3, (16, 16, 16), 20_000, 1e-2, "f32", seed=34),
     Workload("st", 3, (20, 16, 12), 15_000, 1e-9, "f64", seed=35),
     Workload("st", 3, (16, 16, 16), 30_000, 1e-5, "f32", dist="box", seed=36),
+    # fp64 3D box: one bin split into subproblems of the full cap, each interpolated in two
+    # chunks of the bank-aware point order
+    Workload("st", 3, (16, 16, 16), 30_000, 1e-9, "f64", dist="box", seed=40),
     Workload("st", 1, (1000,), 50_001, 1e-5, "f32", seed=37),
     Workload("st", 1, (777,), 30_000, 1e-12, "f64", seed=38),
     Workload("st", 1, (4096,), 40_000, 1e-6, "f32", dist="box", seed=39),
