@@ -382,6 +382,7 @@ size_t spread_lds_limit();
 size_t spread_tile_bytes(int prec, int dim, int w, const int* m);
 // LDS bytes of the 3D column-run spreading kernel for bins m (0 if it cannot run: m3 > 8).
 size_t spread_col_lds_bytes(int prec, int w, const int* m);
+int spread_col_per_cu(int prec, int w);   // workgroups of the column kernel meant to share a CU
 // Whether 3D spreading with this kernel width uses the column-run kernel (needs the column order).
 bool spread_uses_columns(int dim, int w);
 int spread_col_step(int w);   // column block edge the 3D column kernel groups points by

@@ -194,16 +194,20 @@ void default_bins(nufft_plan p, int* m) {
             }
         }
     } else {
-        // the column-run kernel first (it needs m3 = 8), then the plain SM tile.  SM point-patch
-        // plans first look for a tile small enough for two workgroups per CU: at N = 128^3,
-        // M = 2^24 that took 16 x 8 x 8 over 16 x 16 x 8 at w = 3 and 4 (fp32 spread 1.29 -> 0.96
-        // ms and 1.50 -> 1.15 ms; fp64, with its two-workgroup build, 1.94 -> 1.72 ms and
-        // 2.26 -> 2.13 ms); w = 2 keeps 16 x 16 x 8, which already fits twice.
+        // the column-run kernel first (it needs m3 = 8), then the plain SM tile.  The column
+        // kernel's bins must fit as many times as its workgroups are meant to share a CU (fp32
+        // w <= 6: twice, which gives 16 x 16 x 8).  SM point-patch plans first look for a tile
+        // small enough for two workgroups per CU: at N = 128^3, M = 2^24 that took 16 x 8 x 8
+        // over 16 x 16 x 8 at w = 3 and 4 (fp32 spread 1.29 -> 0.96 ms and 1.50 -> 1.15 ms;
+        // fp64, with its two-workgroup build, 1.94 -> 1.72 ms and 2.26 -> 2.13 ms); w = 2 keeps
+        // 16 x 16 x 8, which already fits twice.
         const bool col = nufft::spread_uses_columns(3, p->w) && p->method == NUFFT_METHOD_SM;
         const size_t full = nufft::spread_lds_limit();
         for (int pass = col ? 0 : 1; pass < 3; ++pass) {
             if (pass == 1 && p->method != NUFFT_METHOD_SM) continue;
-            const size_t limit = (pass == 1) ? full / 2 : full;
+            const size_t limit = (pass == 1) ? full / 2
+                                 : (pass == 0) ? full / (size_t)nufft::spread_col_per_cu(p->prec, p->w)
+                                               : full;
             for (auto& c : c3) {
                 if (pass >= 1 && c[0] > 16) continue;   // the point-patch kernel keeps at most 16 x 16 x 8
                 int mm[3] = {c[0], c[1], c[2]};

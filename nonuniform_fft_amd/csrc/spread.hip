@@ -234,7 +234,8 @@ k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c, cplx<T>* __restrict__ gri
 //
 // The lanes of a wavefront (or of kSlotWaves wavefronts) own a B x B block of x-y columns of
 // the padded bin and keep the whole z-line of each column (8 + w cells) in registers, in the
-// transform's precision (a run's sum is added to the fp64 LDS bin when the run ends).  A
+// transform's precision (a run's sum is added to the LDS bin, also in the transform's
+// precision, when the run ends).  A
 // point whose kernel support starts at column (c1, c2) fits in the block at origin
 // (s floor(c1 / s), s floor(c2 / s)) with s = B - w + 1, so setpts orders the points of a bin
 // by that column block and a wavefront accumulates every point of a block in registers; the
@@ -244,15 +245,23 @@ k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c, cplx<T>* __restrict__ gri
 // point, so its z offset inside the line is wave-uniform: a scalar branch picks the w
 // registers it updates, and each point costs 2 w FMAs per lane.  The LDS bin is stored
 // z-fastest in separate real and imaginary planes (cell = (x + y p1) pz + z, pz odd) so a line
-// is flushed with fixed offsets and the lanes of a flush fall on distinct bank pairs.
+// is flushed with fixed offsets and the lanes of a flush fall on distinct banks.  Blocks of
+// different wavefronts overlap, so the flush is atomic.
 // Per-point weights are staged per wavefront (no workgroup barrier inside the loop).
 // ------------------------------------------------------------------------------------------
 // column block edge per kernel width: one wavefront for w <= 6, two up to 10, three above
 __host__ __device__ constexpr int col_block_edge(int w) { return w <= 6 ? 8 : (w <= 10 ? 11 : (w == 11 ? 12 : 13)); }
 
-// register budget: fp64 z-lines need twice the registers per lane, so half the wavefronts
+// fp64 z-lines need twice the registers per lane, so 768 lanes.  fp32 plans keep the bin in
+// fp32 and up to w = 6 run 768 lanes, so that two workgroups share a CU (LDS and registers):
+// 3D fp32 w = 6, N = 128^3, M = 2^24 spreads in 1.36 ms instead of 1.72 ms with one
+// 1024-lane workgroup on an fp64 bin (w = 5: 1.26 instead of 1.71 ms).
 template <typename T, int W>
-constexpr int kColBlock = (sizeof(T) == 4) ? 1024 : 768;
+constexpr int kColBlock = (sizeof(T) == 4 && W > 6) ? 1024 : 768;
+
+// workgroups of the column kernel meant to share one CU (the bins are chosen to fit)
+template <typename T, int W>
+constexpr int kColPerCu = (sizeof(T) == 4 && W <= 6) ? 2 : 1;
 
 template <typename T, int W>
 struct ColCfg {
@@ -263,7 +272,9 @@ struct ColCfg {
     static constexpr int kBlock = kColBlock<T, W>;
     static constexpr int kWaves = kBlock / 64;
     static constexpr int kSlotWaves = (kB * kB + 63) / 64;  // wavefronts sharing one slice
-    static constexpr int kPiece = (sizeof(T) == 4) ? 21 : 6;  // points staged per round (3 lanes each)
+    // points staged per round (3 lanes each); at w <= 6 the stages of 12 wavefronts and a
+    // 16 x 16 x 8 fp32 bin fit twice in the LDS (81,792 bytes at w = 6)
+    static constexpr int kPiece = (sizeof(T) == 4) ? (W <= 6 ? 19 : 21) : 6;
     static constexpr int kWZ = (sizeof(T) == 4) ? ((W + 3) & ~3) : ((W + 1) & ~1);  // 16-byte rows
 };
 
@@ -296,6 +307,46 @@ __device__ __forceinline__ int uniform_copy(int v) {
 // register line through copies at the loop head).
 __device__ __forceinline__ void zero_in_place(double& v) { asm volatile("v_mov_b64 %0, 0" : "+v"(v)); }
 __device__ __forceinline__ void zero_in_place(float& v) { asm volatile("v_mov_b32 %0, 0" : "+v"(v)); }
+
+// Adds a register z-line into an LDS bin line t[0..Z).  fp64 bins use the LDS float atomic.
+// fp32 bins use compare-and-swap: the LDS fp32 atomic add runs at a third of a lane per clock
+// per CU on this part, a read plus compare-and-swap at about 6.6 (as fast as the fp64 add).
+// The reads and swaps are issued in batches of Z/2 so their latencies overlap; a swap that
+// lost a race with another wavefront (an overlapping column block) is retried.
+template <int Z>
+__device__ __forceinline__ void lds_line_add(double* t, const float (&a)[Z]) {
+#pragma unroll
+    for (int z = 0; z < Z; ++z) atomicAdd(t + z, (double)a[z]);
+}
+template <int Z>
+__device__ __forceinline__ void lds_line_add(double* t, const double (&a)[Z]) {
+#pragma unroll
+    for (int z = 0; z < Z; ++z) atomicAdd(t + z, a[z]);
+}
+template <int Z>
+__device__ __forceinline__ void lds_line_add(float* t, const float (&a)[Z]) {
+    unsigned int* u = (unsigned int*)t;
+    constexpr int H = (Z + 1) / 2;
+#pragma unroll
+    for (int h = 0; h < Z; h += H) {
+        constexpr int n = H;
+        unsigned int want[n], got[n];
+#pragma unroll
+        for (int i = 0; i < n; ++i)
+            if (h + i < Z) want[i] = u[h + i];
+#pragma unroll
+        for (int i = 0; i < n; ++i)
+            if (h + i < Z) got[i] = atomicCAS(u + h + i, want[i], __float_as_uint(__uint_as_float(want[i]) + a[h + i]));
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+            if (h + i >= Z) continue;
+            while (got[i] != want[i]) {
+                want[i] = got[i];
+                got[i] = atomicCAS(u + h + i, want[i], __float_as_uint(__uint_as_float(want[i]) + a[h + i]));
+            }
+        }
+    }
+}
 
 // Adds the point's w z-weights times v into the register line at the wave-uniform offset Z0.
 template <int W, int Z, int Z0, typename A>
@@ -331,8 +382,8 @@ struct ColPt {
 
 // Adds a column kernel's padded bin (z fastest with pitch PZ, z extent pd[2]) to the fine grid
 // with periodic wrap (eq. (15)); consecutive lanes take consecutive x, then y, then z.
-template <typename T, int BLOCK, int PZ>
-__device__ __forceinline__ void flush_columns(const GeomArgs& g, const double* tre, const double* tim,
+template <typename T, int BLOCK, int PZ, typename TT>
+__device__ __forceinline__ void flush_columns(const GeomArgs& g, const TT* tre, const TT* tim,
                                               cplx<T>* grid, const int* origin, const int* pd, int p1, int p2) {
     const int P = p1 * p2 * pd[2];
     auto run = [&](auto fast) {
@@ -340,8 +391,8 @@ __device__ __forceinline__ void flush_columns(const GeomArgs& g, const double* t
         CellWalk cw(threadIdx.x, BLOCK, p1, p2);
         for (int k = threadIdx.x; k < P; k += BLOCK, cw.next()) {
             const int li = (cw.s1 + cw.s2 * p1) * PZ + cw.s3;
-            const double re = tre[li], im = tim[li];
-            if (re == 0.0 && im == 0.0) continue;
+            const TT re = tre[li], im = tim[li];
+            if (re == (TT)0 && im == (TT)0) continue;
             const int g1 = wrap_pad<FAST>(origin[0] + cw.s1, g.n[0]);
             const int g2 = wrap_pad<FAST>(origin[1] + cw.s2, g.n[1]);
             const int g3 = wrap_pad<FAST>(origin[2] + cw.s3, g.n[2]);
@@ -372,8 +423,8 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
     constexpr int BLOCK = C::kBlock;
     extern __shared__ __align__(16) unsigned char smem[];
     const int PL = p1 * p2 * PZ;
-    double* tre = (double*)smem;             // real and imaginary planes, cell (x + y p1) pz + z
-    double* tim = tre + PL;
+    T* tre = (T*)smem;                       // real and imaginary planes, cell (x + y p1) pz + z
+    T* tim = tre + PL;
     St* stages = (St*)(tim + PL);
 
     const int sid = blockIdx.x;
@@ -390,7 +441,7 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
         origin[2] = b2 * g.m[2] - W / 2;
     }
     const int pd[3] = {p1, p2, Z};
-    for (int k = threadIdx.x; k < 2 * PL; k += BLOCK) tre[k] = 0.0;
+    for (int k = threadIdx.x; k < 2 * PL; k += BLOCK) tre[k] = (T)0;
     __syncthreads();
 
     // the wavefront index is uniform: say so, so the slice bounds and the point loop stay scalar
@@ -511,11 +562,8 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
             const int col = kp & 0xffff;
             if (col != cur) {
                 if (cur >= 0 && live) {
-#pragma unroll
-                    for (int z = 0; z < Z; ++z) {
-                        atomicAdd(tre + cell + z, (double)are[z]);
-                        atomicAdd(tim + cell + z, (double)aim[z]);
-                    }
+                    lds_line_add<Z>(tre + cell, are);
+                    lds_line_add<Z>(tim + cell, aim);
                 }
 #pragma unroll
                 for (int z = 0; z < Z; ++z) {
@@ -545,11 +593,8 @@ __global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, co
         __builtin_amdgcn_wave_barrier();
     }
     if (cur >= 0 && live) {
-#pragma unroll
-        for (int z = 0; z < Z; ++z) {
-            atomicAdd(tre + cell + z, (double)are[z]);
-            atomicAdd(tim + cell + z, (double)aim[z]);
-        }
+        lds_line_add<Z>(tre + cell, are);
+        lds_line_add<Z>(tim + cell, aim);
     }
     __syncthreads();
     // add the padded bin to the fine grid with periodic wrap (eq. (15))
@@ -804,7 +849,8 @@ constexpr bool kWgStaging = sizeof(T) == 8;
 template <typename T, int W>
 size_t col_lds_bytes(const int* m) {
     using C = ColCfg<T, W>;
-    const size_t tile = (size_t)(m[0] + W) * (m[1] + W) * C::kPZ * 2 * sizeof(double);
+    // fp64 plans (workgroup staging) and fp32 plans keep the bin in their own precision
+    const size_t tile = (size_t)(m[0] + W) * (m[1] + W) * C::kPZ * 2 * sizeof(T);
     if constexpr (kWgStaging<T>)
         return tile + sizeof(WgStage<T, W>) * 2 * (C::kWaves / C::kSlotWaves);
     return tile + sizeof(ColStage<T, W>) * C::kWaves;
@@ -1104,6 +1150,16 @@ int spread_col_step(int w) { return col_block_edge(w) - w + 1; }
 size_t spread_col_lds_bytes(int prec, int w, const int* m) {
     if (!spread_uses_columns(3, w) || m[2] != 8) return 0;
     return col_lds_bytes_rt(prec, w, m);
+}
+
+int spread_col_per_cu(int prec, int w) {
+    switch (w) {
+#define NUFFT_CASE(WW) case WW: return prec == 0 ? kColPerCu<float, WW> : kColPerCu<double, WW>;
+        NUFFT_CASE(5) NUFFT_CASE(6) NUFFT_CASE(7) NUFFT_CASE(8) NUFFT_CASE(9) NUFFT_CASE(10)
+        NUFFT_CASE(11) NUFFT_CASE(12)
+#undef NUFFT_CASE
+        default: return 1;
+    }
 }
 
 hipError_t launch_spread(int prec, int method, const GeomArgs& g_in, const void* c_in, void* grid,
