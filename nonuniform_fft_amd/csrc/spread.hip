@@ -253,15 +253,17 @@ k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c, cplx<T>* __restrict__ gri
 __host__ __device__ constexpr int col_block_edge(int w) { return w <= 6 ? 8 : (w <= 10 ? 11 : (w == 11 ? 12 : 13)); }
 
 // fp64 z-lines need twice the registers per lane, so 768 lanes.  fp32 plans keep the bin in
-// fp32 and up to w = 6 run 768 lanes, so that two workgroups share a CU (LDS and registers):
-// 3D fp32 w = 6, N = 128^3, M = 2^24 spreads in 1.36 ms instead of 1.72 ms with one
-// 1024-lane workgroup on an fp64 bin (w = 5: 1.26 instead of 1.71 ms).
+// fp32 and up to w = 8 run 768 lanes, so that two workgroups share a CU (LDS and registers):
+// 3D fp32, N = 128^3, M = 2^24 spreads in 1.36 ms instead of 1.72 ms at w = 6 (with one
+// 1024-lane workgroup on an fp64 bin), 1.26 instead of 1.71 ms at w = 5, 2.32 instead of
+// 3.10 ms at w = 7 and 2.83 instead of 3.46 ms at w = 8.
 template <typename T, int W>
-constexpr int kColBlock = (sizeof(T) == 4 && W > 6) ? 1024 : 768;
+constexpr int kColBlock = (sizeof(T) == 4 && W > 8) ? 1024 : 768;
 
-// workgroups of the column kernel meant to share one CU (the bins are chosen to fit)
+// workgroups of the column kernel meant to share one CU (the bins are chosen to fit, and the
+// kernel is built for the registers that allow it)
 template <typename T, int W>
-constexpr int kColPerCu = (sizeof(T) == 4 && W <= 6) ? 2 : 1;
+constexpr int kColPerCu = (sizeof(T) == 4 && W <= 8) ? 2 : 1;
 
 template <typename T, int W>
 struct ColCfg {
@@ -272,9 +274,10 @@ struct ColCfg {
     static constexpr int kBlock = kColBlock<T, W>;
     static constexpr int kWaves = kBlock / 64;
     static constexpr int kSlotWaves = (kB * kB + 63) / 64;  // wavefronts sharing one slice
-    // points staged per round (3 lanes each); at w <= 6 the stages of 12 wavefronts and a
-    // 16 x 16 x 8 fp32 bin fit twice in the LDS (81,792 bytes at w = 6)
-    static constexpr int kPiece = (sizeof(T) == 4) ? (W <= 6 ? 19 : 21) : 6;
+    // points staged per round (3 lanes each), sized so that with two fp32 workgroups per CU
+    // the stages of 12 wavefronts and the bin fit twice in the LDS: 16 x 16 x 8 bins at
+    // w <= 6 (81,792 bytes at w = 6), 16 x 8 x 8 at w = 7 and 8
+    static constexpr int kPiece = (sizeof(T) == 4) ? (W <= 6 ? 19 : (W == 8 ? 16 : 21)) : 6;
     static constexpr int kWZ = (sizeof(T) == 4) ? ((W + 3) & ~3) : ((W + 1) & ~1);  // 16-byte rows
 };
 
@@ -406,7 +409,8 @@ __device__ __forceinline__ void flush_columns(const GeomArgs& g, const TT* tre, 
 }
 
 template <typename T, int W>
-__global__ void __launch_bounds__((kColBlock<T, W>)) k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
+__global__ void __launch_bounds__((kColBlock<T, W>)) __attribute__((amdgpu_waves_per_eu(kColPerCu<T, W> == 2 ? 6 : 1)))
+k_spread_col(GeomArgs g, const cplx<T>* __restrict__ c,
                                                                      cplx<T>* __restrict__ grid, int p1, int p2) {
     // vector blockIdx.y of a many-vector launch (strides in complex values)
     c += (int64_t)blockIdx.y * g.cvs;
