@@ -35,10 +35,7 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Bin keys
 // ------------------------------------------------------------------------------------------
 template <typename T, int DIM>
-__global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __restrict__ keys,
-                                                      int* __restrict__ bad) {
-    int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (j >= a.M) return;
+__device__ __forceinline__ int32_t bin_key(const SortArgs& a, int64_t j, int* __restrict__ bad) {
     int bidx[3] = {0, 0, 0};
     double tf[DIM];
     bool ok = true;
@@ -67,7 +64,36 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
         key = 0;
         atomicOr(bad, 1);
     }
-    keys[j] = key;
+    return key;
+}
+
+// The keys of one sort tile (kTile points, kItems per thread, the loads of several points in
+// flight per thread), and, when hist is given, the tile's histogram of the first radix digit
+// (the low bits0 bits), in the digit-major layout the scan and the scatter read
+// (hist[d * ntiles + tile]), so the first pass needs no histogram kernel of its own.
+template <typename T, int DIM>
+__global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __restrict__ keys,
+                                                      int* __restrict__ bad, int bits0, int64_t ntiles,
+                                                      int32_t* __restrict__ hist) {
+    __shared__ int32_t h[kRadix];
+    const int mask = (1 << bits0) - 1;
+    if (hist)
+        for (int i = threadIdx.x; i < kRadix; i += kBlock) h[i] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kTile;
+#pragma unroll 4
+    for (int r = 0; r < kItems; ++r) {
+        const int64_t j = base + (int64_t)r * kBlock + threadIdx.x;
+        if (j < a.M) {
+            const int32_t key = bin_key<T, DIM>(a, j, bad);
+            keys[j] = key;
+            if (hist) atomicAdd(&h[key & mask], 1);
+        }
+    }
+    if (hist) {
+        __syncthreads();
+        for (int d = threadIdx.x; d <= mask; d += kBlock) hist[(int64_t)d * ntiles + blockIdx.x] = h[d];
+    }
 }
 
 // Points in the caller's order (the GM method, Sec. III-A): the same inside-bin rule and point
@@ -380,13 +406,21 @@ __global__ void k_iota(int32_t* __restrict__ v, int64_t M) {
 }
 
 // offsets[b] = first sorted position whose bin is >= b (offsets[nbins] = M); key = bin * ncol + column.
+// Position i writes the bins in (bin(i - 1), bin(i)]; each thread takes kOffItems consecutive positions.
+constexpr int kOffItems = 4;
 __global__ void k_bin_offsets(const int32_t* __restrict__ skeys, int64_t M, int nbins, FastDiv ncol,
                               int32_t* __restrict__ offsets) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i > M) return;
-    int lo = (i == 0) ? 0 : fast_div(skeys[i - 1], ncol) + 1;
-    int hi = (i == M) ? nbins : fast_div(skeys[i], ncol);
-    for (int b = lo; b <= hi; ++b) offsets[b] = (int32_t)i;
+    const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * kOffItems;
+    if (i0 > M) return;
+    int prev = (i0 == 0) ? -1 : fast_div(skeys[i0 - 1], ncol);
+#pragma unroll
+    for (int k = 0; k < kOffItems; ++k) {
+        const int64_t i = i0 + k;
+        if (i > M) break;
+        const int cur = (i == M) ? nbins : fast_div(skeys[i], ncol);
+        for (int b = prev + 1; b <= cur; ++b) offsets[b] = (int32_t)i;
+        prev = cur;
+    }
 }
 
 __global__ void k_counts_nsub(const int32_t* __restrict__ offsets, int nbins, int cap,
@@ -505,14 +539,16 @@ hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int
     hipError_t e;
     const int64_t M = a.M;
     if (M > 0) {
-        dim3 g((unsigned)cdiv(M, kBlock));
+        const int passes = (a.nbits + kRadixBits - 1) / kRadixBits;
+        // the first pass's digit width (the remaining bits spread evenly over the passes, below)
+        const int bits0 = passes > 0 ? (a.nbits + passes - 1) / passes : 0;
         auto keys_kernel = [&](auto tag, auto dtag) {
             using T = decltype(tag);
-            k_bin_keys<T, decltype(dtag)::value><<<g, kBlock, 0, st>>>(a, keysA, bad_dev);
+            k_bin_keys<T, decltype(dtag)::value><<<dim3((unsigned)L.ntiles), kBlock, 0, st>>>(
+                a, keysA, bad_dev, bits0, L.ntiles, passes > 0 ? hist : nullptr);
         };
         with_type_dim(a.prec, a.dim, keys_kernel);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int passes = (a.nbits + kRadixBits - 1) / kRadixBits;
         int shift = 0;
         // values: the first pass generates the identity, the last writes the caller's perm, and
         // the passes between alternate valsA / valsB
@@ -524,7 +560,8 @@ hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int
             // the remaining bits spread evenly over the remaining passes
             const int bits = (a.nbits - shift + (passes - p) - 1) / (passes - p);
             dim3 gt((unsigned)L.ntiles);
-            k_radix_hist<<<gt, kBlock, 0, st>>>(ki, M, shift, bits, L.ntiles, hist);
+            // (the keys kernel wrote the first pass's histogram)
+            if (p > 0) k_radix_hist<<<gt, kBlock, 0, st>>>(ki, M, shift, bits, L.ntiles, hist);
             if ((e = exclusive_scan(hist, hscan, ((int64_t)1 << bits) * L.ntiles, stmp, st)) != hipSuccess)
                 return e;
             // coordinates: caller's arrays -> ... -> sorted output; the last pass writes xs_out
@@ -554,8 +591,8 @@ hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int
             k_iota<<<dim3((unsigned)cdiv(M, kBlock)), kBlock, 0, st>>>(perm, M);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        k_bin_offsets<<<dim3((unsigned)cdiv(M + 1, kBlock)), kBlock, 0, st>>>(ki, M, a.nbins,
-                                                                               make_fastdiv(std::max(a.ncol, 1)), offsets);
+        k_bin_offsets<<<dim3((unsigned)cdiv(cdiv(M + 1, kOffItems), kBlock)), kBlock, 0, st>>>(
+            ki, M, a.nbins, make_fastdiv(std::max(a.ncol, 1)), offsets);
     } else {
         if ((e = launch_zero_words(offsets, (int64_t)a.nbins + 1, st)) != hipSuccess) return e;
     }
