@@ -686,6 +686,42 @@ def test_column_kernel_widths(nf, orc, prec, eps):
     assert e1 <= tol_for(prec) and e2 <= tol_for(prec), (info["w"], e1, e2)
 
 
+@pytest.mark.parametrize("bins,dist", [(None, "box"), (None, "uniform"), ((32, 16, 8), "uniform"),
+                                       ((16, 8, 8), "box")],
+                         ids=["default_box", "default_uniform", "32x16x8_uniform", "16x8x8_box"])
+def test_column_fp32_bins(nf, orc, bins, dist):
+    """fp32 column-run plans (w = 6) keep the padded bin in fp32 and add each register z-line into
+    it by compare-and-swap, retrying a cell whose swap lost to another wavefront's overlapping
+    column block.  Every point in one 8-cell box with the full subproblem cap puts all wavefronts
+    of a workgroup on the same columns (the most retries); 32 x 16 x 8 bins fit the LDS once (one
+    workgroup per CU), the default 16 x 16 x 8 twice.  The spread step matches the oracle's spread
+    at the single-step bar, and type 1 plus the adjoint type 2 match the oracle NUFFT."""
+    N = (24, 20, 16)
+    wl = Workload("cc", 3, N, 40_000, 1e-5, "f32", dist=dist, seed=171)
+    _announce(f"column fp32 bins={bins} {dist}")
+    inp = make_inputs(wl)
+    kw = {"bins": bins} if bins else {}
+    p = nf.Plan(1, N, wl.eps, "f32", **kw)
+    info = p.info()
+    assert info["w"] == 6 and info["colw"] == 6, info
+    assert tuple(info["bins"]) == (bins or (16, 16, 8)), info
+    X = [to_dev(x) for x in inp["X"]]
+    p.setpts(*X)
+    grid = torch.empty(p.fine_cells, dtype=torch.complex64, device=dev())
+    p.spread(to_dev(inp["c"]), grid)
+    f = torch.empty(tuple(reversed(N)), dtype=torch.complex64, device=dev())
+    c = torch.empty(wl.M, dtype=torch.complex64, device=dev())
+    p.execute(to_dev(inp["c"]), f)
+    p.execute_adjoint(c, to_dev(inp["f"]))
+    torch.cuda.synchronize()
+    ref = orc.spread(inp["X"], inp["c"], p.n, p.w, p.beta)
+    assert orc.rel_l2(grid.cpu().numpy(), ref.ravel()) <= _step_tol("f32")
+    assert orc.rel_l2(f.cpu().numpy(), orc.nufft_type1(inp["X"], inp["c"], N, wl.eps)) <= tol_for("f32")
+    assert orc.rel_l2(c.cpu().numpy(), orc.nufft_type2(inp["X"], inp["f"], N, wl.eps)) <= tol_for("f32")
+    assert p.range_errors() == 0
+    p.destroy()
+
+
 @pytest.mark.parametrize("wl", [Workload("gm", 3, (24, 20, 18), 30_000, 1e-5, "f32", seed=91),
                                 Workload("gm", 2, (48, 40), 20_000, 1e-12, "f64", seed=92),
                                 Workload("gm", 3, (20, 16, 12), 10_000, 1e-9, "f64", dist="cluster", seed=93),
