@@ -75,10 +75,11 @@ template <typename T, int DIM>
 __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __restrict__ keys,
                                                       int* __restrict__ bad, int bits0, int64_t ntiles,
                                                       int32_t* __restrict__ hist) {
-    __shared__ int32_t h[kRadix];
+    __shared__ int32_t h[kBlock / 64][kRadix];   // one copy per wavefront
     const int mask = (1 << bits0) - 1;
+    const int wv = threadIdx.x >> 6;
     if (hist)
-        for (int i = threadIdx.x; i < kRadix; i += kBlock) h[i] = 0;
+        for (int i = threadIdx.x; i < kRadix * (kBlock / 64); i += kBlock) (&h[0][0])[i] = 0;
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kTile;
 #pragma unroll 4
@@ -87,12 +88,17 @@ __global__ void __launch_bounds__(kBlock) k_bin_keys(SortArgs a, int32_t* __rest
         if (j < a.M) {
             const int32_t key = bin_key<T, DIM>(a, j, bad);
             keys[j] = key;
-            if (hist) atomicAdd(&h[key & mask], 1);
+            if (hist) atomicAdd(&h[wv][key & mask], 1);
         }
     }
     if (hist) {
         __syncthreads();
-        for (int d = threadIdx.x; d <= mask; d += kBlock) hist[(int64_t)d * ntiles + blockIdx.x] = h[d];
+        for (int d = threadIdx.x; d <= mask; d += kBlock) {
+            int32_t t = 0;
+#pragma unroll
+            for (int w = 0; w < kBlock / 64; ++w) t += h[w][d];
+            hist[(int64_t)d * ntiles + blockIdx.x] = t;
+        }
     }
 }
 
@@ -187,6 +193,46 @@ __global__ void k_scan_total(const int32_t* __restrict__ in, int32_t* __restrict
     if (threadIdx.x == 0 && blockIdx.x == 0) out[n] = (n > 0) ? out[n - 1] + in[n - 1] : 0;
 }
 
+// Per-digit scan of a radix pass's tile histograms, one workgroup per digit: offs[d * ntiles + t]
+// = the digit's count in tiles before t, totals[d] = the digit's count.  The scatter adds the
+// exclusive scan of the totals (digits before d), so one launch replaces a scan of the whole
+// digit-major array.
+__global__ void __launch_bounds__(kBlock) k_digit_scan(const int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ offs, int64_t ntiles,
+                                                        int32_t* __restrict__ totals) {
+    const int64_t row = (int64_t)blockIdx.x * ntiles;
+    int32_t carry = 0;
+    for (int64_t b = 0; b < ntiles; b += kScanTile) {
+        const int64_t base = b + (int64_t)threadIdx.x * kScanItems;
+        int32_t v[kScanItems];
+        int32_t sum = 0;
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) {
+            v[i] = (base + i < ntiles) ? hist[row + base + i] : 0;
+            sum += v[i];
+        }
+        int32_t tot;
+        int32_t run = carry + block_excl_scan(sum, &tot);
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) {
+            if (base + i < ntiles) offs[row + base + i] = run;
+            run += v[i];
+        }
+        carry += tot;
+    }
+    if (threadIdx.x == 0) totals[blockIdx.x] = carry;
+}
+
+// dbase[d] = the counts of the digits below d (nd <= kBlock digit totals, one workgroup).
+__global__ void __launch_bounds__(kBlock) k_digit_base(const int32_t* __restrict__ totals, int nd,
+                                                        int32_t* __restrict__ dbase) {
+    const int d = threadIdx.x;
+    const int32_t v = d < nd ? totals[d] : 0;
+    int32_t tot;
+    const int32_t ex = block_excl_scan(v, &tot);
+    if (d < nd) dbase[d] = ex;
+}
+
 // Upper bound on the scratch exclusive_scan uses for n elements: per level, the tile sums and
 // their scanned copy (t + 1 entries each).
 size_t scan_scratch_elems(int64_t n) {
@@ -236,17 +282,28 @@ __global__ void __launch_bounds__(kBlock) k_radix_hist(const int32_t* __restrict
                                                         int shift, int bits, int64_t ntiles,
                                                         int32_t* __restrict__ hist) {
     const int mask = (1 << bits) - 1;
-    __shared__ int32_t h[kRadix];
-    for (int i = threadIdx.x; i < kRadix; i += kBlock) h[i] = 0;
+    // one copy of the counters per wavefront (fewer colliding LDS atomics), summed at the end
+    __shared__ int32_t h[kBlock / 64][kRadix];
+    const int wv = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kRadix * (kBlock / 64); i += kBlock) (&h[0][0])[i] = 0;
     __syncthreads();
     int64_t base = (int64_t)blockIdx.x * kTile;
-#pragma unroll 4
+    int32_t kv[kItems];   // (keys are non-negative; -1 marks a slot past the end)
+#pragma unroll
     for (int r = 0; r < kItems; ++r) {
         int64_t idx = base + (int64_t)r * kBlock + threadIdx.x;
-        if (idx < M) atomicAdd(&h[(keys[idx] >> shift) & mask], 1);
+        kv[r] = (idx < M) ? keys[idx] : -1;
     }
+#pragma unroll
+    for (int r = 0; r < kItems; ++r)
+        if (kv[r] >= 0) atomicAdd(&h[wv][(kv[r] >> shift) & mask], 1);
     __syncthreads();
-    for (int d = threadIdx.x; d <= mask; d += kBlock) hist[(int64_t)d * ntiles + blockIdx.x] = h[d];
+    for (int d = threadIdx.x; d <= mask; d += kBlock) {
+        int32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) t += h[w][d];
+        hist[(int64_t)d * ntiles + blockIdx.x] = t;
+    }
 }
 
 template <typename T, int NP>
@@ -266,12 +323,15 @@ struct Payload {
 // written to consecutive addresses.
 // IDV: the values are the keys' positions (the first pass), so none are read.
 template <typename T, int NP, bool IDV>
-__global__ void __launch_bounds__(kScatBlock) k_radix_scatter(const int32_t* __restrict__ keys_in,
+// fp32 tiles are built for 64 VGPRs, so that two workgroups (32 wavefronts) share a CU
+__global__ void __launch_bounds__(kScatBlock) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 8 : 1)))
+k_radix_scatter(const int32_t* __restrict__ keys_in,
                                                            const int32_t* __restrict__ vals_in,
                                                            int32_t* __restrict__ keys_out,
                                                            int32_t* __restrict__ vals_out,
                                                            int64_t M, int shift, int bits, int64_t ntiles,
                                                            const int32_t* __restrict__ offs,
+                                                           const int32_t* __restrict__ dbase,
                                                            Payload<T, NP> pl) {
     const int mask = (1 << bits) - 1;
     constexpr int kWaves = kScatBlock / 64;
@@ -286,6 +346,7 @@ __global__ void __launch_bounds__(kScatBlock) k_radix_scatter(const int32_t* __r
     const int64_t tile = xcd_tile(blockIdx.x, ntiles);
     const int64_t base = tile * kTile;
     const int count = (int)min<int64_t>(kTile, M - base);
+
 
     // load this wavefront's chunk (coalesced per round)
     int32_t keys[kScatItems], vals[kScatItems];
@@ -328,7 +389,8 @@ __global__ void __launch_bounds__(kScatBlock) k_radix_scatter(const int32_t* __r
     __syncthreads();
 
     // tile offsets: digit-major exclusive scan of the tile counts (one thread per digit, the
-    // first kRadix threads), then per-wavefront offsets
+    // first kRadix threads), then per-wavefront offsets; and the run's global start: the counts
+    // of the smaller digits (scan of the digit totals) plus this digit's count in earlier tiles
     {
         static_assert(kRadix % 64 == 0 && kRadix <= kScatBlock, "one thread per digit");
         const int d = tid;
@@ -351,7 +413,8 @@ __global__ void __launch_bounds__(kScatBlock) k_radix_scatter(const int32_t* __r
             int32_t run = inc - tot;
             for (int i = 0; i < wv; ++i) run += wsum[i];
             tbase[d] = run;
-            gbase[d] = (d <= mask) ? offs[(int64_t)d * ntiles + tile] : 0;
+            // the counts of the smaller digits plus this digit's count in earlier tiles
+            gbase[d] = (d <= mask) ? dbase[d] + offs[(int64_t)d * ntiles + tile] : 0;
 #pragma unroll
             for (int i = 0; i < kWaves; ++i) {
                 cnt[i][d] = run;
@@ -447,7 +510,7 @@ __global__ void k_build_sub(int nbins, int cap, const int32_t* __restrict__ coun
 
 struct SortLayout {
     int64_t ntiles;
-    size_t keysA, valsA, keysB, valsB, coords, hist, hist_scan, scan_tmp, nsp, first, end;
+    size_t keysA, valsA, keysB, valsB, coords, hist, hist_scan, totals, dbase, scan_tmp, nsp, first, end;
 };
 
 SortLayout layout(int64_t M, int nbins, int dim, int prec) {
@@ -468,6 +531,8 @@ SortLayout layout(int64_t M, int nbins, int dim, int prec) {
     size_t nh = (size_t)kRadix * L.ntiles;
     L.hist = take(nh);
     L.hist_scan = take(nh + 1);
+    L.totals = take(kRadix);
+    L.dbase = take(kRadix);
     size_t big = std::max(nh, (size_t)nbins + 1);
     L.scan_tmp = take(scan_scratch_elems((int64_t)big) + 16);
     L.nsp = take((size_t)nbins + 1);
@@ -492,15 +557,15 @@ void with_type_dim(int prec, int dim, F&& fn) {
 // marks the first pass (values = identity).
 template <typename T>
 hipError_t scatter_dim(int dim, const int32_t* ki, const int32_t* vi, int32_t* ko, int32_t* vo, int64_t M,
-                       int shift, int bits, int ntiles, const int32_t* hscan, const void* const* cin,
-                       void* const* cout, hipStream_t st) {
+                       int shift, int bits, int ntiles, const int32_t* hscan, const int32_t* dbase,
+                       const void* const* cin, void* const* cout, hipStream_t st) {
     auto go = [&](auto dtag) {
         constexpr int D = decltype(dtag)::value;
         Payload<T, D> pl{};
         for (int d = 0; d < D; ++d) { pl.in[d] = (const T*)cin[d]; pl.out[d] = (T*)cout[d]; }
         const dim3 gt((unsigned)ntiles);
-        if (vi) k_radix_scatter<T, D, false><<<gt, kScatBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, pl);
-        else k_radix_scatter<T, D, true><<<gt, kScatBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, pl);
+        if (vi) k_radix_scatter<T, D, false><<<gt, kScatBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, dbase, pl);
+        else k_radix_scatter<T, D, true><<<gt, kScatBlock, 0, st>>>(ki, vi, ko, vo, M, shift, bits, ntiles, hscan, dbase, pl);
     };
     if (dim == 1) go(std::integral_constant<int, 1>{});
     else if (dim == 2) go(std::integral_constant<int, 2>{});
@@ -533,6 +598,8 @@ hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int
     int32_t* valsB = (int32_t*)(base + L.valsB);
     int32_t* hist = (int32_t*)(base + L.hist);
     int32_t* hscan = (int32_t*)(base + L.hist_scan);
+    int32_t* totals = (int32_t*)(base + L.totals);
+    int32_t* dbase = (int32_t*)(base + L.dbase);
     int32_t* stmp = (int32_t*)(base + L.scan_tmp);
     int32_t* nsp = (int32_t*)(base + L.nsp);
     int32_t* first = (int32_t*)(base + L.first);
@@ -562,8 +629,8 @@ hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int
             dim3 gt((unsigned)L.ntiles);
             // (the keys kernel wrote the first pass's histogram)
             if (p > 0) k_radix_hist<<<gt, kBlock, 0, st>>>(ki, M, shift, bits, L.ntiles, hist);
-            if ((e = exclusive_scan(hist, hscan, ((int64_t)1 << bits) * L.ntiles, stmp, st)) != hipSuccess)
-                return e;
+            k_digit_scan<<<dim3(1u << bits), kBlock, 0, st>>>(hist, hscan, L.ntiles, totals);
+            k_digit_base<<<1, kBlock, 0, st>>>(totals, 1 << bits, dbase);
             // coordinates: caller's arrays -> ... -> sorted output; the last pass writes xs_out
             const bool last = (p == passes - 1);
             const int32_t* vi = (p == 0) ? nullptr : vbuf[(p - 1) & 1];
@@ -576,8 +643,8 @@ hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int
                                                                      : (const void*)((char*)xs_out + (size_t)d * M * rs));
                 cout[d] = to_tmp ? (void*)(ctmp + (size_t)d * M * rs) : (void*)((char*)xs_out + (size_t)d * M * rs);
             }
-            e = a.prec == 0 ? scatter_dim<float>(a.dim, ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, cin, cout, st)
-                            : scatter_dim<double>(a.dim, ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, cin, cout, st);
+            e = a.prec == 0 ? scatter_dim<float>(a.dim, ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, dbase, cin, cout, st)
+                            : scatter_dim<double>(a.dim, ki, vi, ko, vo, M, shift, bits, L.ntiles, hscan, dbase, cin, cout, st);
             if (e != hipSuccess) return e;
             std::swap(ki, ko);
             shift += bits;
