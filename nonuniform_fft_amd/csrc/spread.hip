@@ -244,8 +244,8 @@ k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c, cplx<T>* __restrict__ gri
 // reads its own two weights and all lanes stay live in the flush.  All lanes work on the same
 // point, so its z offset inside the line is wave-uniform: a scalar branch picks the w
 // registers it updates, and each point costs 2 w FMAs per lane.  The LDS bin is stored
-// z-fastest in separate real and imaginary planes (cell = (x + y p1) pz + z, pz odd) so a line
-// is flushed with fixed offsets and the lanes of a flush fall on distinct banks.  Blocks of
+// z-fastest in separate real and imaginary planes (cell = (x + y p1) pz + z) so a line is
+// flushed with fixed offsets (an odd pz puts the lanes of a flush on distinct banks).  Blocks of
 // different wavefronts overlap, so the flush is atomic.
 // Per-point weights are staged per wavefront (no workgroup barrier inside the loop).
 // ------------------------------------------------------------------------------------------
@@ -268,7 +268,10 @@ constexpr int kColPerCu = (sizeof(T) == 4 && W <= 8) ? 2 : 1;
 template <typename T, int W>
 struct ColCfg {
     static constexpr int kZ = 8 + W;                        // z extent of the padded bin (m3 = 8)
-    static constexpr int kPZ = kZ | 1;                      // odd z pitch of the LDS bin
+    // z pitch of the LDS bin: odd, so the lanes of a line flush fall on distinct banks, except
+    // for fp32 bins up to w = 6, where the unpadded pitch leaves room for 21-point stages with two
+    // workgroups per CU (the flush is rare; w = 6 spread 1.39 -> 1.35 ms)
+    static constexpr int kPZ = (sizeof(T) == 4 && W <= 6) ? kZ : (kZ | 1);
     static constexpr int kB = col_block_edge(W);            // column block edge
     static constexpr int kS = kB - W + 1;                   // support starts per block edge
     static constexpr int kBlock = kColBlock<T, W>;
@@ -276,8 +279,8 @@ struct ColCfg {
     static constexpr int kSlotWaves = (kB * kB + 63) / 64;  // wavefronts sharing one slice
     // points staged per round (3 lanes each), sized so that with two fp32 workgroups per CU
     // the stages of 12 wavefronts and the bin fit twice in the LDS: 16 x 16 x 8 bins at
-    // w <= 6 (81,792 bytes at w = 6), 16 x 8 x 8 at w = 7 and 8
-    static constexpr int kPiece = (sizeof(T) == 4) ? (W <= 6 ? 19 : (W == 8 ? 16 : 21)) : 6;
+    // w <= 6 (80,416 bytes at w = 6), 16 x 8 x 8 at w = 7 and 8
+    static constexpr int kPiece = (sizeof(T) == 4) ? (W == 8 ? 16 : 21) : 6;
     static constexpr int kWZ = (sizeof(T) == 4) ? ((W + 3) & ~3) : ((W + 1) & ~1);  // 16-byte rows
 };
 
