@@ -322,17 +322,13 @@ struct Payload {
 // and coordinates are reordered by digit through one LDS buffer in turn, each digit's run
 // written to consecutive addresses.
 // IDV: the values are the keys' positions (the first pass), so none are read.
+// fp32 tiles are built for 64 VGPRs, so that two workgroups (32 wavefronts) share a CU.
 template <typename T, int NP, bool IDV>
-// fp32 tiles are built for 64 VGPRs, so that two workgroups (32 wavefronts) share a CU
 __global__ void __launch_bounds__(kScatBlock) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 8 : 1)))
-k_radix_scatter(const int32_t* __restrict__ keys_in,
-                                                           const int32_t* __restrict__ vals_in,
-                                                           int32_t* __restrict__ keys_out,
-                                                           int32_t* __restrict__ vals_out,
-                                                           int64_t M, int shift, int bits, int64_t ntiles,
-                                                           const int32_t* __restrict__ offs,
-                                                           const int32_t* __restrict__ dbase,
-                                                           Payload<T, NP> pl) {
+k_radix_scatter(const int32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
+                int32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int64_t M, int shift,
+                int bits, int64_t ntiles, const int32_t* __restrict__ offs,
+                const int32_t* __restrict__ dbase, Payload<T, NP> pl) {
     const int mask = (1 << bits) - 1;
     constexpr int kWaves = kScatBlock / 64;
     constexpr int kChunk = kScatItems * 64;              // keys per wavefront
@@ -346,7 +342,6 @@ k_radix_scatter(const int32_t* __restrict__ keys_in,
     const int64_t tile = xcd_tile(blockIdx.x, ntiles);
     const int64_t base = tile * kTile;
     const int count = (int)min<int64_t>(kTile, M - base);
-
 
     // load this wavefront's chunk (coalesced per round)
     int32_t keys[kScatItems], vals[kScatItems];
@@ -530,11 +525,11 @@ SortLayout layout(int64_t M, int nbins, int dim, int prec) {
     L.coords = take(Mm * (size_t)dim * (prec == 0 ? 1 : 2));
     size_t nh = (size_t)kRadix * L.ntiles;
     L.hist = take(nh);
-    L.hist_scan = take(nh + 1);
+    L.hist_scan = take(nh);
     L.totals = take(kRadix);
     L.dbase = take(kRadix);
-    size_t big = std::max(nh, (size_t)nbins + 1);
-    L.scan_tmp = take(scan_scratch_elems((int64_t)big) + 16);
+    // (the one multi-level scan left is over the bins' subproblem counts)
+    L.scan_tmp = take(scan_scratch_elems((int64_t)nbins + 1) + 16);
     L.nsp = take((size_t)nbins + 1);
     L.first = take((size_t)nbins + 2);
     L.end = off;
