@@ -463,22 +463,22 @@ __global__ void k_iota(int32_t* __restrict__ v, int64_t M) {
     if (j < M) v[j] = (int32_t)j;
 }
 
-// offsets[b] = first sorted position whose bin is >= b (offsets[nbins] = M); key = bin * ncol + column.
-// Position i writes the bins in (bin(i - 1), bin(i)]; each thread takes kOffItems consecutive positions.
-constexpr int kOffItems = 4;
-__global__ void k_bin_offsets(const int32_t* __restrict__ skeys, int64_t M, int nbins, FastDiv ncol,
+// offsets[b] = first sorted position whose bin is >= b (offsets[nbins] = M); key = bin * ncol + column,
+// so that is the first sorted key >= b * ncol: one binary search per bin.  (Writing the bins between
+// consecutive sorted keys from the keys' side makes one thread fill every empty bin of a gap, which
+// clustered points turn into a long serial tail.)
+__global__ void k_bin_offsets(const int32_t* __restrict__ skeys, int64_t M, int nbins, int ncol,
                               int32_t* __restrict__ offsets) {
-    const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * kOffItems;
-    if (i0 > M) return;
-    int prev = (i0 == 0) ? -1 : fast_div(skeys[i0 - 1], ncol);
-#pragma unroll
-    for (int k = 0; k < kOffItems; ++k) {
-        const int64_t i = i0 + k;
-        if (i > M) break;
-        const int cur = (i == M) ? nbins : fast_div(skeys[i], ncol);
-        for (int b = prev + 1; b <= cur; ++b) offsets[b] = (int32_t)i;
-        prev = cur;
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b > nbins) return;
+    const int64_t target = (int64_t)b * ncol;
+    int64_t lo = 0, hi = M;   // the answer lies in [lo, hi]
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if ((int64_t)skeys[mid] < target) lo = mid + 1;
+        else hi = mid;
     }
+    offsets[b] = (int32_t)lo;
 }
 
 __global__ void k_counts_nsub(const int32_t* __restrict__ offsets, int nbins, int cap,
@@ -653,8 +653,8 @@ hipError_t launch_sort(const SortArgs& a_in, int32_t* perm, int32_t* counts, int
             k_iota<<<dim3((unsigned)cdiv(M, kBlock)), kBlock, 0, st>>>(perm, M);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        k_bin_offsets<<<dim3((unsigned)cdiv(cdiv(M + 1, kOffItems), kBlock)), kBlock, 0, st>>>(
-            ki, M, a.nbins, make_fastdiv(std::max(a.ncol, 1)), offsets);
+        k_bin_offsets<<<dim3((unsigned)cdiv((int64_t)a.nbins + 1, kBlock)), kBlock, 0, st>>>(
+            ki, M, a.nbins, std::max(a.ncol, 1), offsets);
     } else {
         if ((e = launch_zero_words(offsets, (int64_t)a.nbins + 1, st)) != hipSuccess) return e;
     }
