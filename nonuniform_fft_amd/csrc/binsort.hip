@@ -490,17 +490,26 @@ __global__ void k_counts_nsub(const int32_t* __restrict__ offsets, int nbins, in
     nsp[b] = (c + cap - 1) / cap;
 }
 
-__global__ void k_build_sub(int nbins, int cap, const int32_t* __restrict__ counts,
+// One thread per subproblem: its bin is the last bin whose first subproblem index is at or below
+// it (a binary search over the scanned per-bin counts; empty bins share their successor's first
+// index), and it is that bin's k-th chunk of cap points.  (One thread per bin writing all its
+// chunks leaves a serial tail on bins holding many subproblems.)
+__global__ void k_build_sub(int nbins, int64_t nsub, int cap, const int32_t* __restrict__ counts,
                             const int32_t* __restrict__ offsets,
                             const int32_t* __restrict__ first, int32_t* __restrict__ sub) {
-    int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= nbins) return;
-    int32_t c = counts[b], f = first[b], o = offsets[b];
-    for (int32_t s = 0, k = 0; s < c; s += cap, ++k) {
-        sub[3 * (int64_t)(f + k) + 0] = b;
-        sub[3 * (int64_t)(f + k) + 1] = o + s;
-        sub[3 * (int64_t)(f + k) + 2] = min(cap, c - s);
+    const int64_t si = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (si >= nsub) return;
+    int lo = 0, hi = nbins - 1;
+    while (lo < hi) {
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (first[mid] <= si) lo = mid;
+        else hi = mid - 1;
     }
+    const int b = lo;
+    const int32_t k = (int32_t)(si - first[b]);
+    sub[3 * si + 0] = b;
+    sub[3 * si + 1] = offsets[b] + k * cap;
+    sub[3 * si + 2] = min(cap, counts[b] - k * cap);
 }
 
 struct SortLayout {
@@ -680,13 +689,14 @@ hipError_t launch_identity_order(const SortArgs& a, int32_t* perm, void* xs_out,
     return hipGetLastError();
 }
 
-hipError_t launch_build_subproblems_from(int64_t M, int nbins, int dim, int prec, int cap,
+hipError_t launch_build_subproblems_from(int64_t M, int nbins, int dim, int prec, int cap, int64_t nsub,
                                          const int32_t* counts, const int32_t* offsets,
                                          const void* scratch, int32_t* sub, hipStream_t st) {
+    if (nsub <= 0 || nbins <= 0) return hipSuccess;
     SortLayout L = layout(M, nbins, dim, prec);
     const int32_t* first = (const int32_t*)((const char*)scratch + L.first);
-    k_build_sub<<<dim3((unsigned)cdiv(nbins, kBlock)), kBlock, 0, st>>>(nbins, cap, counts, offsets,
-                                                                       first, sub);
+    k_build_sub<<<dim3((unsigned)cdiv(nsub, kBlock)), kBlock, 0, st>>>(nbins, nsub, cap, counts, offsets,
+                                                                      first, sub);
     return hipGetLastError();
 }
 

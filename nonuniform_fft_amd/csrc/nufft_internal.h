@@ -322,7 +322,7 @@ hipError_t launch_sort(const SortArgs& a, int32_t* perm, int32_t* counts, int32_
 // Points in the caller's order (GM method): checks and copies the coordinates into xs_out,
 // perm = identity; no binning.
 hipError_t launch_identity_order(const SortArgs& a, int32_t* perm, void* xs_out, int* bad_dev, hipStream_t st);
-hipError_t launch_build_subproblems_from(int64_t M, int nbins, int dim, int prec, int cap,
+hipError_t launch_build_subproblems_from(int64_t M, int nbins, int dim, int prec, int cap, int64_t nsub,
                                          const int32_t* counts, const int32_t* offsets,
                                          const void* scratch, int32_t* sub, hipStream_t st);
 

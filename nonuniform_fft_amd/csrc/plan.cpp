@@ -581,7 +581,7 @@ int setpts_impl(nufft_plan plan, int64_t M, const void* x, const void* y, const 
     } else if ((rc = dev_alloc(plan, plan->sub, sub_bytes, "subproblem list")) != NUFFT_OK) {
         return rc;
     }
-    NUFFT_HIP(nufft::launch_build_subproblems_from(M, (int)plan->nbins, plan->dim, plan->prec, plan->cap,
+    NUFFT_HIP(nufft::launch_build_subproblems_from(M, (int)plan->nbins, plan->dim, plan->prec, plan->cap, host_nsub,
                                                    (const int32_t*)plan->counts.p, (const int32_t*)plan->offsets.p,
                                                    scr, (int32_t*)plan->sub.p, plan->stream));
     record(plan, EV_SORT1);
