@@ -208,21 +208,23 @@ k_spread_sm(GeomArgs g, const cplx<T>* __restrict__ c, cplx<T>* __restrict__ gri
         }
     }
     __syncthreads();
-    // flush the padded bin with periodic wrap (eq. (15)); consecutive lanes take consecutive x
+    // flush the padded bin with periodic wrap (eq. (15)): lane pairs take one cell, the even lane
+    // its real and the odd lane its imaginary part, consecutive pairs consecutive x, so one
+    // atomic instruction covers contiguous grid bytes
     const int P = p1 * p2 * p3;
     auto flush = [&](auto fast) {
         constexpr bool FAST = decltype(fast)::value;
-        CellWalk cw(threadIdx.x, kSpreadBlock, p1, p2);
-        for (int k = threadIdx.x; k < P; k += kSpreadBlock, cw.next()) {
-            const int li = cw.s1 + cw.s2 * pc + cw.s3 * pp;
-            const double re = tre[li], im = tim[li];
-            if (re == 0.0 && im == 0.0) continue;
+        const int comp = threadIdx.x & 1;
+        const double* src = comp ? tim : tre;
+        CellWalk cw(threadIdx.x >> 1, kSpreadBlock / 2, p1, p2);
+        for (int k = threadIdx.x >> 1; k < P; k += kSpreadBlock / 2, cw.next()) {
+            const double v = src[cw.s1 + cw.s2 * pc + cw.s3 * pp];
+            if (v == 0.0) continue;
             const int g1 = wrap_pad<FAST>(origin[0] + cw.s1, g.n[0]);
             const int g2 = wrap_pad<FAST>(origin[1] + cw.s2, g.n[1]);
             const int g3 = (DIM == 3) ? wrap_pad<FAST>(origin[2] + cw.s3, g.n[2]) : 0;
             const size_t gi = grid_index<FAST>(g1, g2, g3, g.n);
-            unsafeAtomicAdd(&grid[gi].re, (T)re);
-            unsafeAtomicAdd(&grid[gi].im, (T)im);
+            unsafeAtomicAdd((T*)grid + 2 * gi + comp, (T)v);
         }
     };
     if (tile_fast(origin, pd, g.n, DIM)) flush(std::true_type{});
@@ -387,24 +389,27 @@ struct ColPt {
 };
 
 // Adds a column kernel's padded bin (z fastest with pitch PZ, z extent pd[2]) to the fine grid
-// with periodic wrap (eq. (15)); consecutive lanes take consecutive x, then y, then z.
+// with periodic wrap (eq. (15)).  Lane pairs take one cell (the even lane its real part, the odd
+// lane its imaginary part), consecutive pairs consecutive x, then y, then z, so one atomic
+// instruction covers contiguous grid bytes: 3D fp32 w = 6, M = 2^24 spread 1.36 -> 1.30 ms
+// against one lane per cell and two atomic instructions.
 template <typename T, int BLOCK, int PZ, typename TT>
 __device__ __forceinline__ void flush_columns(const GeomArgs& g, const TT* tre, const TT* tim,
                                               cplx<T>* grid, const int* origin, const int* pd, int p1, int p2) {
     const int P = p1 * p2 * pd[2];
     auto run = [&](auto fast) {
         constexpr bool FAST = decltype(fast)::value;
-        CellWalk cw(threadIdx.x, BLOCK, p1, p2);
-        for (int k = threadIdx.x; k < P; k += BLOCK, cw.next()) {
-            const int li = (cw.s1 + cw.s2 * p1) * PZ + cw.s3;
-            const TT re = tre[li], im = tim[li];
-            if (re == (TT)0 && im == (TT)0) continue;
+        const int comp = threadIdx.x & 1;
+        const TT* src = comp ? tim : tre;
+        CellWalk cw(threadIdx.x >> 1, BLOCK / 2, p1, p2);
+        for (int k = threadIdx.x >> 1; k < P; k += BLOCK / 2, cw.next()) {
+            const TT v = src[(cw.s1 + cw.s2 * p1) * PZ + cw.s3];
+            if (v == (TT)0) continue;
             const int g1 = wrap_pad<FAST>(origin[0] + cw.s1, g.n[0]);
             const int g2 = wrap_pad<FAST>(origin[1] + cw.s2, g.n[1]);
             const int g3 = wrap_pad<FAST>(origin[2] + cw.s3, g.n[2]);
             const size_t gi = grid_index<FAST>(g1, g2, g3, g.n);
-            unsafeAtomicAdd(&grid[gi].re, (T)re);
-            unsafeAtomicAdd(&grid[gi].im, (T)im);
+            unsafeAtomicAdd((T*)grid + 2 * gi + comp, (T)v);
         }
     };
     if (tile_fast(origin, pd, g.n, 3)) run(std::true_type{});
@@ -963,14 +968,16 @@ __global__ void __launch_bounds__(kSpread1Block) k_spread_sm1(GeomArgs g, const 
         }
     }
     __syncthreads();
+    // lane pairs take one cell: the even lane its real part, the odd lane its imaginary part
     auto flush = [&](auto fast) {
         constexpr bool FAST = decltype(fast)::value;
-        for (int k = threadIdx.x; k < p1; k += kSpread1Block) {
-            const double re = tre[k], im = tim[k];
-            if (re == 0.0 && im == 0.0) continue;
+        const int comp = threadIdx.x & 1;
+        const double* src = comp ? tim : tre;
+        for (int k = threadIdx.x >> 1; k < p1; k += kSpread1Block / 2) {
+            const double v = src[k];
+            if (v == 0.0) continue;
             const int gi = wrap_pad<FAST>(origin + k, g.n[0]);
-            unsafeAtomicAdd(&grid[gi].re, (T)re);
-            unsafeAtomicAdd(&grid[gi].im, (T)im);
+            unsafeAtomicAdd((T*)grid + 2 * (size_t)gi + comp, (T)v);
         }
     };
     if (tile_fast(&origin, &p1, g.n, 1)) flush(std::true_type{});
