@@ -658,7 +658,8 @@ def test_widths_1d_and_gm(nf, orc, dim, prec, eps, method):
 # The 3D column-run spreader at every kernel width it serves
 # ---------------------------------------------------------------------------------------------
 
-COLUMN_CASES = [("f32", 1e-4), ("f32", 1e-6), ("f32", 1e-7)] + \
+# fp32 up to w = 8 runs two 768-lane workgroups per CU, above that one 1024-lane workgroup
+COLUMN_CASES = [("f32", 1e-4), ("f32", 1e-6), ("f32", 1e-7), ("f32", 1e-8), ("f32", 1e-10)] + \
                [("f64", e) for e in (1e-4, 1e-5, 1e-6, 1e-7, 1e-8, 1e-10, 1e-11)]
 
 
